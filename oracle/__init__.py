@@ -1,0 +1,24 @@
+"""fp64 CPU oracle for attention over a resident, shared KV-cache prefix.
+
+TEST INFRASTRUCTURE ONLY. It is the plain, slow definition the HIP path is checked
+against; only ``tests/``, ``__graft_entry__.smoke()`` and the bench's CPU-baseline
+leg may import it. It shares no code with ``kv_cache_prefix_amd`` and imports
+nothing from it; both sides take their inputs from ``synth`` only.
+
+Parity pins (what each function is checked against, besides itself) live in
+``tests/test_oracle_*.py``. Unpinned readings: the LSE base (pinned only through
+merge consistency), the causal alignment for M < S_suf (the plain bottom-right
+reading), and ``top_k`` / ``fa_window`` (not implemented).
+"""
+from .attention import (attend, combine, f64, merge, prefix_query, prefix_query_fused,
+                        resolve_head_map, softmax_scale, suffix_visible)
+from .mlx4g32 import dequantize, quantize, record_bytes, unpack_codes
+from .sparse import (block_means, block_scores, n_blocks, prefix_query_sparse,
+                     prefix_query_sparse_auto, select_blocks)
+
+__all__ = [
+    "attend", "combine", "f64", "merge", "prefix_query", "prefix_query_fused",
+    "resolve_head_map", "softmax_scale", "suffix_visible", "dequantize", "quantize",
+    "record_bytes", "unpack_codes", "block_means", "block_scores", "n_blocks",
+    "prefix_query_sparse", "prefix_query_sparse_auto", "select_blocks",
+]
