@@ -1,0 +1,156 @@
+/*
+ * pion_prefix.h - C ABI for attention over a resident, shared KV-cache prefix on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ATTEND.PREFIX.* family of the "Shared KV Cache Serving" page
+ * (section "Stage 2: ATTEND.PREFIX.* - Pion computes attention on cached K/V", Wire
+ * forms) and of the "ATTEND.* and ATTEND.PREFIX.*" command page (Wire forms and the
+ * externalized-attention command table). Argument order follows those wire forms
+ * (sid, layer, H, N, D, ...); blobs become pointers.
+ *
+ * Conventions for every entry point:
+ *   - Returns PION_OK (0) or a negative PION_ERR_* code; nothing throws across the ABI.
+ *   - Arguments are validated before any GPU work is queued, so on an error no
+ *     output is written.
+ *   - Tensor pointers are DEVICE pointers (hipMalloc or a torch CUDA tensor on the
+ *     same GPU), contiguous, in the layouts stated below. head_map is a HOST pointer.
+ *   - Work is queued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and is asynchronous: inputs must stay valid, and outputs must not be
+ *     read, until `stream` has passed the call.
+ *   - fp16 means IEEE binary16; out and lse are fp32.
+ *   - The softmax scale is 1/sqrt(D); lse is the natural-log log-sum-exp of the
+ *     scaled logits, so two partial results over disjoint key sets merge as
+ *     lse = ln(e^lse1 + e^lse2), out = e^(lse1-lse) out1 + e^(lse2-lse) out2.
+ *   - head_map: int32 per q-head naming its kv-head (GQA); NULL means
+ *     h -> h / (H_q / H_kv), which requires H_kv to divide H_q.
+ *   - Supported head dims: D in {64, 128, 256}; other values -> PION_ERR_UNSUPPORTED.
+ *   - Calls are thread-safe (one library-wide lock guards the slot table).
+ */
+#ifndef PION_PREFIX_H
+#define PION_PREFIX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. The wire's "-ERR session not found" is PION_ERR_NOT_FOUND; +HIT/+MISS
+ * are the 1/0 results of pion_prefix_lookup (ATTEND.* page, ATTEND.PREFIX.LOOKUP row;
+ * "Shared KV Cache Serving", Cold-tier state machine). PION_ERR_COLDMISS is reserved:
+ * this library keeps no cold tier, so it never returns it. */
+enum {
+    PION_OK = 0,
+    PION_ERR_NOT_FOUND = -1,   /* no resident slot for (sid, layer) */
+    PION_ERR_INVALID = -2,     /* bad argument: null pointer, shape mismatch, range */
+    PION_ERR_UNSUPPORTED = -3, /* valid request this build does not implement (D, ...) */
+    PION_ERR_NOMEM = -4,       /* device allocation failed or slot table full */
+    PION_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+    PION_ERR_COLDMISS = -6     /* reserved (cold tier) */
+};
+
+/* Resident formats. FP16 keeps K and V as given. MLX4G32 is the int4 group-32 affine
+ * tier ("Shared KV Cache Serving", Quantized tier - mlx4g32; V-store page, The
+ * mlx4g32 tier), quantized on the device at store time with pion_kv_quantize_mlx4g32. */
+enum { PION_KV_FP16 = 0, PION_KV_MLX4G32 = 1 };
+
+/* ATTEND.PREFIX.STORE <sid> <layer> <H> <N> <D> <K_blob> <V_blob>.
+ * Copies K and V, fp16 [H, N, D] each, into a library-owned slot keyed (sid, layer)
+ * and keeps them resident until pion_prefix_drop or library unload (the command
+ * table: "resident until DROP"). Storing a live key replaces its slot and drops any
+ * cached block means. The library owns the slot memory; K and V may be freed once
+ * `stream` has passed the call. sid is a NUL-terminated string of 1..255 bytes.
+ * Errors: INVALID (null/empty sid, H/N/D <= 0, H > 255, kv_format unknown, D % 32 != 0
+ * for MLX4G32), UNSUPPORTED (D), NOMEM (allocation, or more than PION_MAX_SLOTS slots;
+ * default 4096, env PION_MAX_SLOTS), HIP. */
+int pion_prefix_store(const char *sid, int layer, int H, int N, int D,
+                      const void *K, const void *V, int kv_format, void *stream);
+
+/* ATTEND.PREFIX.LOOKUP <sid> <layer> -> 1 (+HIT) if a slot exists, 0 (+MISS) if not,
+ * PION_ERR_INVALID for a null sid. Host-only. */
+int pion_prefix_lookup(const char *sid, int layer);
+
+/* Frees the slot (sid, layer); layer < 0 frees every layer of sid. Returns the number
+ * of slots freed (0 if none: dropping an absent key is not an error), or INVALID.
+ * Waits for queued work on the device before freeing. */
+int pion_prefix_drop(const char *sid, int layer);
+
+/* Shape of a resident slot: writes H, N, D and kv_format (any pointer may be NULL).
+ * NOT_FOUND if absent. Host-only. */
+int pion_prefix_info(const char *sid, int layer, int *H, int *N, int *D, int *kv_format);
+
+/* ATTEND.PREFIX.QUERY <sid> <layer> <H> <D> <top_k> <Q_blob>, in its M=1 and batched-Q
+ * forms ("Shared KV Cache Serving", Wire-protocol details: Q is (H, M, D), the reply is
+ * H*M*D fp32 followed by an H*M fp32 LSE trailer).
+ *   Q        fp16 [H_q, M, D]; row i of q-head h attends all N resident keys of
+ *            kv-head head_map[h].
+ *   head_map HOST int32 [H_q] or NULL (H_kv is the stored H).
+ *   out      fp32 [H_q, M, D], normalized attention output.
+ *   lse      fp32 [H_q, M] or NULL.
+ * top_k and fa_window are not taken: the pages measure only top_k = N (dense).
+ * Errors: INVALID (pointers, M < 1, H_q < 1 or > 128, D != stored D, head_map entry
+ * outside [0, H_kv), H_kv not dividing H_q without a head_map), NOT_FOUND, HIP. */
+int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M,
+                      const void *Q, const int32_t *head_map,
+                      float *out, float *lse, void *stream);
+
+/* ATTEND.PREFIX.QUERY_FUSED <sid> <layer> <H_q> <D> <S_suf> <H_kv> <Q> <K_suf> <V_suf>
+ * <head_map>: the caller's dense suffix attention merged with the resident prefix in
+ * one call (ATTEND.* page, QUERY_FUSED row; GQA-aware).
+ *   Q            fp16 [H_q, M, D] (the wire derives M from the blob; here it is explicit).
+ *   K_suf, V_suf fp16 [H_kv, S_suf, D]; may be NULL when S_suf == 0.
+ *   Row i of q-head h (g = head_map[h]) attends all N prefix keys of g and the suffix
+ *   keys j <= S_suf - M + i of g: the suffix is causal and aligned bottom-right, so
+ *   M == S_suf is the usual triangular mask and the last row sees the whole suffix.
+ *   out fp32 [H_q, M, D]; lse fp32 [H_q, M] or NULL (the wire sends no trailer).
+ * Errors: as pion_prefix_query, plus INVALID for H_kv != stored H, S_suf < 0,
+ * M > S_suf when S_suf > 0, and null suffix pointers when S_suf > 0. */
+int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M,
+                            int S_suf, int H_kv,
+                            const void *Q, const void *K_suf, const void *V_suf,
+                            const int32_t *head_map, float *out, float *lse,
+                            void *stream);
+
+/* ATTEND.PREFIX.QUERY_SPARSE_AUTO <sid> <layer> <H_q> <D> <B> <K_top> <H_kv> <Q>
+ * <head_map>, and with S_suf > 0 ATTEND.PREFIX.QUERY_SPARSE_AUTO_FUSED (... <S_suf> <Q>
+ * <K_suf> <V_suf> <head_map>): the server picks blocks by block-mean top-K over the
+ * resident K and attends only their tokens ("Shared KV Cache Serving", Stage 2,
+ * sparse-mask paragraph; ATTEND.* page, QUERY_SPARSE_AUTO rows: K_mean cached per slot).
+ *   Q       fp16 [H_q, 1, D] (M = 1).
+ *   Blocks are tokens [b*B, min((b+1)*B, N)), nb = ceil(N/B). K_mean[g, b] is the mean
+ *   of K over block b's tokens; it is computed on first use and cached in the slot per
+ *   B. score[g, b] = sum over q-heads h with head_map[h] == g of q_h . K_mean[g, b].
+ *   Per kv-head, the min(K_top, nb) best blocks by (score desc, block asc) are kept;
+ *   q-head h attends their tokens of kv-head head_map[h], plus all S_suf suffix keys.
+ *   K_suf, V_suf fp16 [H_kv, S_suf, D], NULL when S_suf == 0.
+ *   out        fp32 [H_q, D]; lse fp32 [H_q] or NULL.
+ *   blocks_out int32 [H_kv, K_top] or NULL: chosen blocks ascending, -1 past nb.
+ * Errors: as pion_prefix_query_fused, plus INVALID for B < 1, K_top < 1,
+ * K_top > 1024. */
+int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D,
+                                  int B, int K_top, int H_kv, int S_suf,
+                                  const void *Q, const void *K_suf, const void *V_suf,
+                                  const int32_t *head_map, float *out, float *lse,
+                                  int32_t *blocks_out, void *stream);
+
+/* mlx4g32 encoder ("Shared KV Cache Serving", Quantized tier - mlx4g32; V-store page,
+ * The mlx4g32 tier): int4 codes in groups of 32, affine, fp16 scale and bias per group,
+ * the scale rounded to fp16 before codes are chosen. Per group, in fp32 with IEEE
+ * rounding: mn = min, mx = max, s = fp16((mx - mn) / 15), b = fp16(mn); if s == 0 every
+ * code is 0, else q = clamp(round_half_even((x - b) / s), 0, 15). Element i of a row
+ * goes to word i/8 at bits 4*(i%8); the reader computes x = s*q + b.
+ *   x      fp16 [rows, D], D % 32 == 0.
+ *   codes  uint32 [rows, D/8]; scales, biases fp16 [rows, D/32].
+ * Inputs must be finite. Errors: INVALID (pointers, rows < 0, D <= 0 or D % 32 != 0),
+ * HIP. rows == 0 is a no-op. */
+int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D,
+                             uint32_t *codes, void *scales, void *biases, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *pion_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PION_PREFIX_H */

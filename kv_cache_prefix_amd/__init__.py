@@ -1,0 +1,214 @@
+"""Python binding of libpion_prefix.so: attention over a resident KV-cache prefix on
+MI355X (gfx950).
+
+Thin marshalling only: each function checks tensor device, dtype, contiguity and shape,
+then calls the C entry point of the same name (include/pion_prefix.h) with raw device
+pointers and the current HIP stream. Every step of the computation runs in the
+library's HIP kernels; there is no fallback - if the library is missing, importing a
+function that needs it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PION_OK = 0
+PION_ERR_NOT_FOUND = -1
+PION_ERR_INVALID = -2
+PION_ERR_UNSUPPORTED = -3
+PION_ERR_NOMEM = -4
+PION_ERR_HIP = -5
+PION_ERR_COLDMISS = -6
+PION_KV_FP16 = 0
+PION_KV_MLX4G32 = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpion_prefix.so")
+
+# Every symbol include/pion_prefix.h declares, with its ctypes signature.
+_c_char_p, _int, _vp = ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p
+SIGNATURES = {
+    "pion_prefix_store": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _int, _vp]),
+    "pion_prefix_lookup": (_int, [_c_char_p, _int]),
+    "pion_prefix_drop": (_int, [_c_char_p, _int]),
+    "pion_prefix_info": (_int, [_c_char_p, _int, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query_fused": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query_sparse_auto": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,
+                                             _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pion_kv_quantize_mlx4g32": (_int, [_vp, ctypes.c_int64, _int, _vp, _vp, _vp, _vp]),
+    "pion_status_str": (ctypes.c_char_p, [_int]),
+}
+
+_lib = None
+
+
+class PionError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run kv_cache_prefix_amd/build.py")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().pion_status_str(status).decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise PionError(rc, where)
+    return rc
+
+
+def _sid(sid) -> bytes:
+    return sid.encode() if isinstance(sid, str) else bytes(sid)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t, dtype, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _head_map(head_map, H_q):
+    if head_map is None:
+        return None, None
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(head_map, dtype=np.int32))
+    if arr.shape != (H_q,):
+        raise ValueError("head_map must hold one int32 per q-head")
+    return arr, arr.ctypes.data
+
+
+def pion_prefix_store(sid, layer: int, K, V, kv_format: int = PION_KV_FP16, stream=None) -> int:
+    """ATTEND.PREFIX.STORE: K, V fp16 [H, N, D] device tensors -> resident slot."""
+    import torch
+    if K.dim() != 3 or V.shape != K.shape:
+        raise ValueError("K and V must both be [H, N, D]")
+    H, N, D = K.shape
+    rc = lib().pion_prefix_store(_sid(sid), layer, H, N, D,
+                                 _dev(K, torch.float16, "K"), _dev(V, torch.float16, "V"),
+                                 kv_format, _stream(stream))
+    return _check(rc, "pion_prefix_store")
+
+
+def pion_prefix_lookup(sid, layer: int) -> int:
+    return _check(lib().pion_prefix_lookup(_sid(sid), layer), "pion_prefix_lookup")
+
+
+def pion_prefix_drop(sid, layer: int = -1) -> int:
+    return _check(lib().pion_prefix_drop(_sid(sid), layer), "pion_prefix_drop")
+
+
+def pion_prefix_info(sid, layer: int):
+    vals = [ctypes.c_int() for _ in range(4)]
+    rc = lib().pion_prefix_info(_sid(sid), layer, *[ctypes.byref(v) for v in vals])
+    _check(rc, "pion_prefix_info")
+    return tuple(v.value for v in vals)   # (H, N, D, kv_format)
+
+
+def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=None) -> int:
+    """ATTEND.PREFIX.QUERY (M >= 1): Q fp16 [H_q, M, D] -> out fp32 [H_q, M, D], lse [H_q, M]."""
+    import torch
+    H_q, M, D = Q.shape
+    hm, hm_ptr = _head_map(head_map, H_q)
+    rc = lib().pion_prefix_query(
+        _sid(sid), layer, H_q, D, M, _dev(Q, torch.float16, "Q"), hm_ptr,
+        _dev(out, torch.float32, "out", (H_q, M, D)),
+        None if lse is None else _dev(lse, torch.float32, "lse", (H_q, M)), _stream(stream))
+    return _check(rc, "pion_prefix_query")
+
+
+def pion_prefix_query_fused(sid, layer: int, Q, K_suf, V_suf, out, lse=None, head_map=None,
+                            H_kv: Optional[int] = None, stream=None) -> int:
+    """ATTEND.PREFIX.QUERY_FUSED: Q [H_q, M, D], K_suf/V_suf fp16 [H_kv, S_suf, D]."""
+    import torch
+    H_q, M, D = Q.shape
+    if K_suf is not None:
+        H_kv_s, S_suf, _ = K_suf.shape
+        H_kv = H_kv_s if H_kv is None else H_kv
+        ks = _dev(K_suf, torch.float16, "K_suf", (H_kv, S_suf, D))
+        vs = _dev(V_suf, torch.float16, "V_suf", (H_kv, S_suf, D))
+    else:
+        if H_kv is None:
+            raise ValueError("H_kv is required without a suffix")
+        S_suf, ks, vs = 0, None, None
+    hm, hm_ptr = _head_map(head_map, H_q)
+    rc = lib().pion_prefix_query_fused(
+        _sid(sid), layer, H_q, D, M, S_suf, H_kv, _dev(Q, torch.float16, "Q"), ks, vs, hm_ptr,
+        _dev(out, torch.float32, "out", (H_q, M, D)),
+        None if lse is None else _dev(lse, torch.float32, "lse", (H_q, M)), _stream(stream))
+    return _check(rc, "pion_prefix_query_fused")
+
+
+def pion_prefix_query_sparse_auto(sid, layer: int, Q, B: int, K_top: int, out, lse=None,
+                                  blocks_out=None, K_suf=None, V_suf=None, head_map=None,
+                                  H_kv: Optional[int] = None, stream=None) -> int:
+    """ATTEND.PREFIX.QUERY_SPARSE_AUTO(_FUSED): Q fp16 [H_q, 1, D] -> out fp32 [H_q, D]."""
+    import torch
+    H_q, M, D = Q.shape
+    if M != 1:
+        raise ValueError("sparse-auto takes one query row per head")
+    if K_suf is not None:
+        H_kv_s, S_suf, _ = K_suf.shape
+        H_kv = H_kv_s if H_kv is None else H_kv
+        ks = _dev(K_suf, torch.float16, "K_suf", (H_kv, S_suf, D))
+        vs = _dev(V_suf, torch.float16, "V_suf", (H_kv, S_suf, D))
+    else:
+        if H_kv is None:
+            raise ValueError("H_kv is required without a suffix")
+        S_suf, ks, vs = 0, None, None
+    hm, hm_ptr = _head_map(head_map, H_q)
+    rc = lib().pion_prefix_query_sparse_auto(
+        _sid(sid), layer, H_q, D, B, K_top, H_kv, S_suf, _dev(Q, torch.float16, "Q"), ks, vs,
+        hm_ptr, _dev(out, torch.float32, "out", (H_q, D)),
+        None if lse is None else _dev(lse, torch.float32, "lse", (H_q,)),
+        None if blocks_out is None else _dev(blocks_out, torch.int32, "blocks_out", (H_kv, K_top)),
+        _stream(stream))
+    return _check(rc, "pion_prefix_query_sparse_auto")
+
+
+def pion_kv_quantize_mlx4g32(x, codes, scales, biases, stream=None) -> int:
+    """mlx4g32 encoder: x fp16 [rows, D] -> codes int32 (uint32 bits) [rows, D/8],
+    scales, biases fp16 [rows, D/32]."""
+    import torch
+    rows, D = x.shape
+    rc = lib().pion_kv_quantize_mlx4g32(
+        _dev(x, torch.float16, "x"), rows, D,
+        _dev(codes, torch.int32, "codes", (rows, D // 8)),
+        _dev(scales, torch.float16, "scales", (rows, D // 32)),
+        _dev(biases, torch.float16, "biases", (rows, D // 32)), _stream(stream))
+    return _check(rc, "pion_kv_quantize_mlx4g32")
+
+
+__all__ = [n for n in SIGNATURES if n != "pion_status_str"] + [
+    "lib", "status_str", "PionError", "PION_KV_FP16", "PION_KV_MLX4G32", "LIB_PATH"]

@@ -1,0 +1,634 @@
+// C ABI of the prefix-attention library: argument validation, the resident slot table
+// and the launch plan. Declarations and the contract of every entry point are in
+// include/pion_prefix.h; this file only implements them.
+//
+// Slot table: one entry per (sid, layer) as the ATTEND.PREFIX.STORE wire form keys it
+// ("Shared KV Cache Serving", Stage 2 wire forms). Each entry owns one device
+// allocation holding the resident K/V in the store layout [H, N, D] (fp16), or the
+// mlx4g32 planar arrays (codes [H, N, D/8], scales and biases [H, N, D/32], per side),
+// plus the per-B block-mean cache of the sparse-auto query.
+//
+// Launch plan of an attention call: one split-KV kernel over workgroups (key span,
+// q-head group sharing one kv-head, query index); each writes (acc, m, l) per (row,
+// span) into a per-stream workspace, and the last workgroup of each row group merges
+// them into out and lse. The sparse-auto call runs block_mean (first use per slot and B),
+// block_score and block_topk first, and the split-KV kernel reads the picked block
+// list on the device.
+#include "pion_prefix.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace pion;
+
+constexpr int kMaxSplitsTotal = 1024;
+constexpr int kMaxKTop = 1024;
+
+struct KMean {
+  float *ptr = nullptr;
+  int nb = 0;
+  hipEvent_t ready = nullptr;
+  hipStream_t stream = nullptr;
+  bool done = false;
+};
+
+struct Slot {
+  int H = 0, N = 0, D = 0, fmt = 0;
+  void *mem = nullptr;
+  size_t bytes = 0;
+  KVView view{};
+  hipEvent_t ready = nullptr;
+  hipStream_t stream = nullptr;
+  bool done = false;
+  std::map<int, KMean> kmeans;
+};
+
+struct Workspace {
+  void *ptr = nullptr;
+  size_t cap = 0;
+  int *counters = nullptr;  // ticket counters of the split merge, kMaxCounters ints
+};
+
+constexpr int kMaxCounters = 65536;  // one per workgroup row (grid.y <= 65535)
+
+std::mutex g_mu;
+std::unordered_map<std::string, Slot> g_slots;
+std::unordered_map<hipStream_t, Workspace> g_ws;      // split partials
+std::unordered_map<hipStream_t, Workspace> g_sel_ws;  // sparse-auto scores and picks
+
+std::string key_of(const char *sid, int layer) {
+  std::string k(sid);
+  k.push_back('\0');
+  k.append(std::to_string(layer));
+  return k;
+}
+
+bool sid_ok(const char *sid) {
+  if (!sid) return false;
+  const size_t n = strnlen(sid, 256);
+  return n >= 1 && n <= 255;
+}
+
+bool d_supported(int D) { return D == 64 || D == 128 || D == 256; }
+
+size_t max_slots() {
+  static size_t v = [] {
+    const char *e = getenv("PION_MAX_SLOTS");
+    long x = e ? atol(e) : 4096;
+    return (size_t)(x > 0 ? x : 4096);
+  }();
+  return v;
+}
+
+int split_target() {
+  static int v = [] {
+    const char *e = getenv("PION_SPLIT_TARGET");
+    int x = e ? atoi(e) : 512;
+    return x > 0 ? x : 512;
+  }();
+  return v;
+}
+
+// Memory that a kernel may read or write: device (or managed) allocations only.
+bool on_device(const void *p) {
+  if (!p) return false;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged ||
+         a.type == hipMemoryTypeUnified;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// fp16 tensors are read with 16-byte vector loads; fp32 / int32 with 4-byte accesses.
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+void free_slot(Slot &s) {
+  for (auto &kv : s.kmeans) {
+    if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    if (kv.second.ready) (void)hipEventDestroy(kv.second.ready);
+  }
+  s.kmeans.clear();
+  if (s.mem) (void)hipFree(s.mem);  // hipFree waits for queued device work
+  if (s.ready) (void)hipEventDestroy(s.ready);
+  s.mem = nullptr;
+  s.ready = nullptr;
+}
+
+// Make `st` wait for work recorded on another stream (store or block-mean build).
+hipError_t order_after(hipEvent_t ev, hipStream_t src, bool &done, hipStream_t st) {
+  if (done || !ev) return hipSuccess;
+  hipError_t q = hipEventQuery(ev);
+  if (q == hipSuccess) {
+    done = true;
+    return hipSuccess;
+  }
+  if (q != hipErrorNotReady) return q;
+  if (src == st) return hipSuccess;
+  return hipStreamWaitEvent(st, ev, 0);
+}
+
+// Per-stream scratch for the split partials, plus the zeroed ticket counters (the
+// merging workgroup resets its counter, so they stay zero between calls). Grows by
+// reallocating after the stream has drained; never shrinks.
+hipError_t get_ws(hipStream_t st, size_t bytes, void **out) {
+  Workspace &w = g_ws[st];
+  if (!w.counters) {
+    hipError_t e = hipMalloc(&w.counters, kMaxCounters * sizeof(int));
+    if (e == hipSuccess) e = launch_zero_counters(w.counters, kMaxCounters, st);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      if (w.counters) (void)hipFree(w.counters);
+      w.counters = nullptr;
+      return e;
+    }
+  }
+  if (w.cap < bytes) {
+    if (w.ptr) {
+      hipError_t e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return e;
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.cap = 0;
+    }
+    size_t cap = std::max(bytes, (size_t)1 << 20);
+    cap = align256(cap + cap / 4);
+    hipError_t e = hipMalloc(&w.ptr, cap);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return e;
+    }
+    w.cap = cap;
+  }
+  *out = w.ptr;
+  return hipSuccess;
+}
+
+// head_map (host, may be null) -> vector; returns false when out of range or when the
+// default map is undefined.
+bool resolve_map(const int32_t *head_map, int H_q, int H_kv, std::vector<int> &hm) {
+  hm.resize(H_q);
+  if (!head_map) {
+    if (H_kv < 1 || H_q % H_kv) return false;
+    const int r = H_q / H_kv;
+    for (int h = 0; h < H_q; ++h) hm[h] = h / r;
+    return true;
+  }
+  for (int h = 0; h < H_q; ++h) {
+    if (head_map[h] < 0 || head_map[h] >= H_kv) return false;
+    hm[h] = head_map[h];
+  }
+  return true;
+}
+
+// Group the q-heads of each kv-head into chunks of at most kRowsPerGroup.
+int build_groups(const std::vector<int> &hm, int H_kv, RowGroups &rg) {
+  memset(&rg, 0, sizeof(rg));
+  int maxcnt = 0;
+  for (int g = 0; g < H_kv; ++g) {
+    int cur = -1;
+    for (int h = 0; h < (int)hm.size(); ++h) {
+      if (hm[h] != g) continue;
+      if (cur < 0 || rg.cnt[cur] == kRowsPerGroup) {
+        cur = rg.n++;
+        rg.g[cur] = (uint8_t)g;
+      }
+      rg.heads[cur][rg.cnt[cur]++] = (uint8_t)h;
+      maxcnt = std::max(maxcnt, (int)rg.cnt[cur]);
+    }
+  }
+  int R = 1;
+  while (R < maxcnt) R <<= 1;
+  return R;
+}
+
+int pick_chunk(long long keys, long long y, int granule) {
+  if (keys <= 0) return granule;
+  const long long target = split_target();
+  long long c = (keys * y + target - 1) / target;
+  c = std::max<long long>(c, granule);
+  c = (c + granule - 1) / granule * granule;
+  // keep the span count within the in-kernel merge limit (1024 spans)
+  while ((keys + c - 1) / c > kMaxSplitsTotal / 2) c *= 2;
+  return (int)std::min<long long>(c, 1LL << 30);
+}
+
+struct AttnCall {
+  const uint16_t *Q;
+  int H_q, M, D;
+  const std::vector<int> *hm;
+  int H_kv;
+  const uint16_t *Ksuf, *Vsuf;
+  int S_suf;
+  const int32_t *blocks;  // device [H_kv, K_top] or null
+  int n_sel, K_top, B;
+  float *out, *lse;
+};
+
+int run_attention(const Slot &sl, const AttnCall &c, hipStream_t st) {
+  PartialParams p;
+  memset(&p, 0, sizeof(p));
+  const int R = build_groups(*c.hm, c.H_kv, p.rg);
+  const int Y = p.rg.n * c.M;
+  if (Y > 65535 || Y > kMaxCounters) return PION_ERR_UNSUPPORTED;  // grid.y limit
+  p.Q = c.Q;
+  p.H_q = c.H_q;
+  p.M = c.M;
+  p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
+  p.kv = sl.view;
+  if (c.blocks) {
+    p.blocks = c.blocks;
+    p.K_top = c.K_top;
+    p.B = c.B;
+    p.pre_splits = c.n_sel;
+    p.pre_chunk = c.B;
+  } else {
+    p.pre_chunk = pick_chunk(sl.N, Y, 64);
+    p.pre_splits = (sl.N + p.pre_chunk - 1) / p.pre_chunk;
+  }
+  int suf_splits = 0;
+  if (c.S_suf > 0) {
+    p.Ksuf = c.Ksuf;
+    p.Vsuf = c.Vsuf;
+    p.S_suf = c.S_suf;
+    p.suf_chunk = pick_chunk(c.S_suf, Y, 64);
+    suf_splits = (c.S_suf + p.suf_chunk - 1) / p.suf_chunk;
+  }
+  p.S_total = p.pre_splits + suf_splits;
+  if (p.S_total > kMaxSplitsTotal) return PION_ERR_UNSUPPORTED;
+
+  const size_t rows = (size_t)c.H_q * c.M;
+  const size_t acc_bytes = align256(rows * p.S_total * c.D * sizeof(float));
+  const size_t ml_bytes = align256(rows * p.S_total * sizeof(float));
+  void *ws = nullptr;
+  if (get_ws(st, acc_bytes + 2 * ml_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
+  p.part_acc = (float *)ws;
+  p.part_m = (float *)((char *)ws + acc_bytes);
+  p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
+  p.counters = g_ws[st].counters;
+  p.out = c.out;
+  p.lse = c.lse;
+
+  hipError_t e;
+  if (sl.fmt == PION_KV_MLX4G32) {
+    p.x_begin = 0;
+    e = launch_partial(p, R, Y, p.pre_splits, true, st);
+    if (e == hipSuccess && suf_splits > 0) {
+      p.x_begin = p.pre_splits;
+      e = launch_partial(p, R, Y, suf_splits, false, st);
+    }
+  } else {
+    p.x_begin = 0;
+    e = launch_partial(p, R, Y, p.S_total, false, st);
+  }
+  return e == hipSuccess ? PION_OK : PION_ERR_HIP;
+}
+
+Slot *find_slot(const char *sid, int layer) {
+  auto it = g_slots.find(key_of(sid, layer));
+  return it == g_slots.end() ? nullptr : &it->second;
+}
+
+// Common checks of the query entry points that need no slot. Returns PION_OK or an error.
+int check_query_args(const char *sid, int H_q, int D, int M, const void *Q, const float *out) {
+  if (!sid_ok(sid) || !Q || !out) return PION_ERR_INVALID;
+  if (!aligned(Q, 16) || !aligned(out, 4)) return PION_ERR_INVALID;
+  if (H_q < 1 || H_q > kMaxHeads || M < 1 || D <= 0) return PION_ERR_INVALID;
+  if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
+  return PION_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pion_status_str(int status) {
+  switch (status) {
+    case PION_OK: return "ok";
+    case PION_ERR_NOT_FOUND: return "session not found";
+    case PION_ERR_INVALID: return "invalid argument";
+    case PION_ERR_UNSUPPORTED: return "unsupported";
+    case PION_ERR_NOMEM: return "out of memory";
+    case PION_ERR_HIP: return "HIP error";
+    case PION_ERR_COLDMISS: return "cold miss";
+    default: return "unknown status";
+  }
+}
+
+int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D, uint32_t *codes, void *scales,
+                             void *biases, void *stream) {
+  if (rows < 0 || D <= 0 || D % 32) return PION_ERR_INVALID;
+  if (rows == 0) return PION_OK;
+  if (!x || !codes || !scales || !biases) return PION_ERR_INVALID;
+  if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 2) || !aligned(biases, 2))
+    return PION_ERR_INVALID;
+  if (!on_device(x) || !on_device(codes) || !on_device(scales) || !on_device(biases))
+    return PION_ERR_INVALID;
+  if (launch_quantize_mlx4g32((const uint16_t *)x, rows, D, codes, (uint16_t *)scales,
+                              (uint16_t *)biases, (hipStream_t)stream) != hipSuccess)
+    return PION_ERR_HIP;
+  return PION_OK;
+}
+
+int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const void *K,
+                      const void *V, int kv_format, void *stream) {
+  if (!sid_ok(sid) || H < 1 || H > 255 || N < 1 || D <= 0 || !K || !V) return PION_ERR_INVALID;
+  if (kv_format != PION_KV_FP16 && kv_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
+  if (kv_format == PION_KV_MLX4G32 && D % 32) return PION_ERR_INVALID;
+  if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
+  const size_t elems = (size_t)H * N * D;
+  if ((size_t)N * D > ((size_t)1 << 40)) return PION_ERR_INVALID;
+  if (!aligned(K, 16) || !aligned(V, 16)) return PION_ERR_INVALID;
+  if (!on_device(K) || !on_device(V)) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  const std::string key = key_of(sid, layer);
+  const bool replacing = g_slots.count(key) > 0;
+  if (!replacing && g_slots.size() >= max_slots()) return PION_ERR_NOMEM;
+
+  Slot sl;
+  sl.H = H;
+  sl.N = N;
+  sl.D = D;
+  sl.fmt = kv_format;
+  size_t off[6] = {0};
+  if (kv_format == PION_KV_FP16) {
+    off[0] = 0;
+    off[1] = align256(elems * 2);
+    sl.bytes = off[1] + align256(elems * 2);
+  } else {
+    const size_t cb = align256(elems / 2), sb = align256(elems / 16);
+    off[0] = 0;             // K codes
+    off[1] = cb;            // K scales
+    off[2] = cb + sb;       // K biases
+    off[3] = cb + 2 * sb;   // V codes
+    off[4] = 2 * cb + 2 * sb;
+    off[5] = 2 * cb + 3 * sb;
+    sl.bytes = 2 * cb + 4 * sb;
+  }
+  if (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return PION_ERR_NOMEM;
+  }
+  char *base = (char *)sl.mem;
+  KVView &v = sl.view;
+  v.fmt = kv_format;
+  v.H = H;
+  v.N = N;
+  v.D = D;
+  hipError_t e;
+  if (kv_format == PION_KV_FP16) {
+    v.K = (const uint16_t *)(base + off[0]);
+    v.V = (const uint16_t *)(base + off[1]);
+    e = hipMemcpyAsync(base + off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(base + off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
+  } else {
+    v.Kc = (const uint32_t *)(base + off[0]);
+    v.Ks = (const uint16_t *)(base + off[1]);
+    v.Kb = (const uint16_t *)(base + off[2]);
+    v.Vc = (const uint32_t *)(base + off[3]);
+    v.Vs = (const uint16_t *)(base + off[4]);
+    v.Vb = (const uint16_t *)(base + off[5]);
+    const int64_t rows = (int64_t)H * N;
+    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + off[0]),
+                                (uint16_t *)(base + off[1]), (uint16_t *)(base + off[2]), st);
+    if (e == hipSuccess)
+      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + off[3]),
+                                  (uint16_t *)(base + off[4]), (uint16_t *)(base + off[5]), st);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(sl.ready, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free_slot(sl);
+    return PION_ERR_HIP;
+  }
+  sl.stream = st;
+  if (replacing) free_slot(g_slots[key]);
+  g_slots[key] = sl;
+  return PION_OK;
+}
+
+int pion_prefix_lookup(const char *sid, int layer) {
+  if (!sid_ok(sid)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return find_slot(sid, layer) ? 1 : 0;
+}
+
+int pion_prefix_drop(const char *sid, int layer) {
+  if (!sid_ok(sid)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  int n = 0;
+  if (layer >= 0) {
+    auto it = g_slots.find(key_of(sid, layer));
+    if (it != g_slots.end()) {
+      free_slot(it->second);
+      g_slots.erase(it);
+      n = 1;
+    }
+    return n;
+  }
+  const std::string prefix = std::string(sid) + '\0';
+  for (auto it = g_slots.begin(); it != g_slots.end();) {
+    if (it->first.compare(0, prefix.size(), prefix) == 0) {
+      free_slot(it->second);
+      it = g_slots.erase(it);
+      ++n;
+    } else {
+      ++it;
+    }
+  }
+  return n;
+}
+
+int pion_prefix_info(const char *sid, int layer, int *H, int *N, int *D, int *kv_format) {
+  if (!sid_ok(sid)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  const Slot *s = find_slot(sid, layer);
+  if (!s) return PION_ERR_NOT_FOUND;
+  if (H) *H = s->H;
+  if (N) *N = s->N;
+  if (D) *D = s->D;
+  if (kv_format) *kv_format = s->fmt;
+  return PION_OK;
+}
+
+int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const void *Q,
+                      const int32_t *head_map, float *out, float *lse, void *stream) {
+  int rc = check_query_args(sid, H_q, D, M, Q, out);
+  if (rc != PION_OK) return rc;
+  if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Slot *sl = find_slot(sid, layer);
+  if (!sl) return PION_ERR_NOT_FOUND;
+  if (sl->D != D) return PION_ERR_INVALID;
+  std::vector<int> hm;
+  if (!resolve_map(head_map, H_q, sl->H, hm)) return PION_ERR_INVALID;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+  AttnCall c{};
+  c.Q = (const uint16_t *)Q;
+  c.H_q = H_q;
+  c.M = M;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = sl->H;
+  c.out = out;
+  c.lse = lse;
+  return run_attention(*sl, c, st);
+}
+
+int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, int S_suf,
+                            int H_kv, const void *Q, const void *K_suf, const void *V_suf,
+                            const int32_t *head_map, float *out, float *lse, void *stream) {
+  int rc = check_query_args(sid, H_q, D, M, Q, out);
+  if (rc != PION_OK) return rc;
+  if (S_suf < 0 || H_kv < 1 || H_kv > 255) return PION_ERR_INVALID;
+  if (S_suf > 0 && (M > S_suf || !K_suf || !V_suf)) return PION_ERR_INVALID;
+  if (S_suf > 0 && (!aligned(K_suf, 16) || !aligned(V_suf, 16))) return PION_ERR_INVALID;
+  if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
+  std::vector<int> hm;
+  if (!resolve_map(head_map, H_q, H_kv, hm)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Slot *sl = find_slot(sid, layer);
+  if (!sl) return PION_ERR_NOT_FOUND;
+  if (sl->D != D || sl->H != H_kv) return PION_ERR_INVALID;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
+  if (S_suf > 0 && (!on_device(K_suf) || !on_device(V_suf))) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+  AttnCall c{};
+  c.Q = (const uint16_t *)Q;
+  c.H_q = H_q;
+  c.M = M;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = H_kv;
+  c.Ksuf = (const uint16_t *)K_suf;
+  c.Vsuf = (const uint16_t *)V_suf;
+  c.S_suf = S_suf;
+  c.out = out;
+  c.lse = lse;
+  return run_attention(*sl, c, st);
+}
+
+int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, int B, int K_top,
+                                  int H_kv, int S_suf, const void *Q, const void *K_suf,
+                                  const void *V_suf, const int32_t *head_map, float *out,
+                                  float *lse, int32_t *blocks_out, void *stream) {
+  int rc = check_query_args(sid, H_q, D, 1, Q, out);
+  if (rc != PION_OK) return rc;
+  if (B < 1 || K_top < 1 || K_top > kMaxKTop || S_suf < 0 || H_kv < 1 || H_kv > 255)
+    return PION_ERR_INVALID;
+  if (S_suf > 0 && (!K_suf || !V_suf)) return PION_ERR_INVALID;
+  if (S_suf > 0 && (!aligned(K_suf, 16) || !aligned(V_suf, 16))) return PION_ERR_INVALID;
+  if ((lse && !aligned(lse, 4)) || (blocks_out && !aligned(blocks_out, 4)))
+    return PION_ERR_INVALID;
+  std::vector<int> hm;
+  if (!resolve_map(head_map, H_q, H_kv, hm)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Slot *sl = find_slot(sid, layer);
+  if (!sl) return PION_ERR_NOT_FOUND;
+  if (sl->D != D || sl->H != H_kv) return PION_ERR_INVALID;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
+  if (S_suf > 0 && (!on_device(K_suf) || !on_device(V_suf))) return PION_ERR_INVALID;
+  if (blocks_out && !on_device(blocks_out)) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+
+  const int nb = (sl->N + B - 1) / B;
+  const int n_sel = std::min(K_top, nb);
+  // block means: cached per (slot, B), built on first use
+  auto it = sl->kmeans.find(B);
+  if (it == sl->kmeans.end()) {
+    KMean km;
+    km.nb = nb;
+    if (hipMalloc(&km.ptr, (size_t)H_kv * nb * D * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      return PION_ERR_NOMEM;
+    }
+    hipError_t e = launch_block_mean(sl->view, B, km.ptr, st);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&km.ready, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(km.ready, st);
+    if (e != hipSuccess) {
+      (void)hipFree(km.ptr);
+      if (km.ready) (void)hipEventDestroy(km.ready);
+      return PION_ERR_HIP;
+    }
+    km.stream = st;
+    it = sl->kmeans.emplace(B, km).first;
+  } else if (order_after(it->second.ready, it->second.stream, it->second.done, st) !=
+             hipSuccess) {
+    return PION_ERR_HIP;
+  }
+  // score and block buffers: a per-stream allocation separate from the partials'
+  // workspace (run_attention may grow and move that one)
+  const size_t score_bytes = align256((size_t)H_kv * nb * sizeof(float));
+  const size_t blk_bytes = align256((size_t)H_kv * K_top * sizeof(int32_t));
+  Workspace &w = g_sel_ws[st];
+  if (w.cap < score_bytes + blk_bytes) {
+    if (w.ptr) {
+      if (hipStreamSynchronize(st) != hipSuccess) return PION_ERR_HIP;
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.cap = 0;
+    }
+    const size_t cap = align256(score_bytes + blk_bytes + (1 << 16));
+    if (hipMalloc(&w.ptr, cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return PION_ERR_NOMEM;
+    }
+    w.cap = cap;
+  }
+  float *score = (float *)w.ptr;
+  int32_t *blocks = blocks_out ? blocks_out : (int32_t *)((char *)w.ptr + score_bytes);
+
+  HeadMap hmap;
+  memset(&hmap, 0, sizeof(hmap));
+  hmap.H_q = H_q;
+  for (int h = 0; h < H_q; ++h) hmap.m[h] = (uint8_t)hm[h];
+  if (launch_block_score((const uint16_t *)Q, hmap, it->second.ptr, H_kv, nb, D, score, st) !=
+      hipSuccess)
+    return PION_ERR_HIP;
+  if (launch_block_topk(score, H_kv, nb, K_top, blocks, st) != hipSuccess) return PION_ERR_HIP;
+
+  AttnCall c{};
+  c.Q = (const uint16_t *)Q;
+  c.H_q = H_q;
+  c.M = 1;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = H_kv;
+  c.Ksuf = (const uint16_t *)K_suf;
+  c.Vsuf = (const uint16_t *)V_suf;
+  c.S_suf = S_suf;
+  c.blocks = blocks;
+  c.n_sel = n_sel;
+  c.K_top = K_top;
+  c.B = B;
+  c.out = out;
+  c.lse = lse;
+  return run_attention(*sl, c, st);
+}
+
+}  // extern "C"

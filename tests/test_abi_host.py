@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+function include/pion_prefix.h declares, and rejects bad arguments (and unknown
+sessions) before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_prefix_amd as kp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pion_prefix.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pion_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kp.LIB_PATH):
+        from kv_cache_prefix_amd.build import build
+        build()
+    return kp.lib()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) == 9, names
+    assert set(names) == set(kp.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert kp.status_str(0) == "ok"
+    assert kp.status_str(kp.PION_ERR_NOT_FOUND) == "session not found"
+    assert kp.status_str(12345) == "unknown status"
+
+
+def test_lookup_and_drop_of_absent_session(lib):
+    assert lib.pion_prefix_lookup(b"nope", 0) == 0
+    assert lib.pion_prefix_drop(b"nope", 3) == 0
+    assert lib.pion_prefix_drop(b"nope", -1) == 0
+    assert lib.pion_prefix_lookup(None, 0) == kp.PION_ERR_INVALID
+    assert lib.pion_prefix_lookup(b"", 0) == kp.PION_ERR_INVALID
+    assert lib.pion_prefix_lookup(b"x" * 256, 0) == kp.PION_ERR_INVALID
+    H = ctypes.c_int()
+    assert lib.pion_prefix_info(b"nope", 0, ctypes.byref(H), None, None, None) == kp.PION_ERR_NOT_FOUND
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def test_store_argument_validation(lib):
+    st = lib.pion_prefix_store
+    assert st(None, 0, 2, 8, 64, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 0, 8, 64, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 256, 8, 64, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 2, 0, 64, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 2, 8, 0, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 2, 8, 64, None, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 2, 8, 64, FAKE, FAKE, 7, None) == kp.PION_ERR_INVALID
+    assert st(b"s", 0, 2, 8, 48, FAKE, FAKE, 1, None) == kp.PION_ERR_INVALID    # D % 32
+    assert st(b"s", 0, 2, 8, 96, FAKE, FAKE, 0, None) == kp.PION_ERR_UNSUPPORTED
+    # a host pointer is not device memory
+    buf = np.zeros(2 * 8 * 64, np.float16)
+    hp = ctypes.c_void_p(buf.ctypes.data)
+    assert st(b"s", 0, 2, 8, 64, hp, hp, 0, None) == kp.PION_ERR_INVALID
+    assert lib.pion_prefix_lookup(b"s", 0) == 0
+
+
+def test_query_argument_validation(lib):
+    q = lib.pion_prefix_query
+    assert q(None, 0, 2, 64, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 0, 64, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 129, 64, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 2, 64, 0, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 2, 64, 1, None, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 2, 64, 1, FAKE, None, None, None, None) == kp.PION_ERR_INVALID
+    assert q(b"s", 0, 2, 80, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_UNSUPPORTED
+    assert q(b"s", 0, 2, 64, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_NOT_FOUND
+
+
+def test_fused_argument_validation(lib):
+    f = lib.pion_prefix_query_fused
+    hm_bad = (ctypes.c_int32 * 4)(0, 1, 2, 9)
+    hm_ok = (ctypes.c_int32 * 4)(0, 1, 1, 0)
+    # M > S_suf
+    assert f(b"s", 0, 4, 64, 5, 4, 2, FAKE, FAKE, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    # null suffix with S_suf > 0
+    assert f(b"s", 0, 4, 64, 1, 4, 2, FAKE, None, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    # head_map entry out of range
+    assert f(b"s", 0, 4, 64, 1, 4, 2, FAKE, FAKE, FAKE, hm_bad, FAKE, None, None) == kp.PION_ERR_INVALID
+    # H_kv not dividing H_q without a map
+    assert f(b"s", 0, 4, 64, 1, 4, 3, FAKE, FAKE, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert f(b"s", 0, 4, 64, 1, -1, 2, FAKE, FAKE, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    # everything valid but no such session
+    assert f(b"s", 0, 4, 64, 1, 4, 2, FAKE, FAKE, FAKE, hm_ok, FAKE, None, None) == kp.PION_ERR_NOT_FOUND
+    assert f(b"s", 0, 4, 64, 3, 0, 2, FAKE, None, None, None, FAKE, None, None) == kp.PION_ERR_NOT_FOUND
+
+
+def test_sparse_auto_argument_validation(lib):
+    s = lib.pion_prefix_query_sparse_auto
+    args = lambda B, K, S, H_kv=1: (b"s", 0, 8, 256, B, K, H_kv, S, FAKE, FAKE, FAKE, None, FAKE,
+                                    None, None, None)
+    assert s(*args(0, 8, 0)) == kp.PION_ERR_INVALID
+    assert s(*args(64, 0, 0)) == kp.PION_ERR_INVALID
+    assert s(*args(64, 1025, 0)) == kp.PION_ERR_INVALID
+    assert s(*args(64, 8, -1)) == kp.PION_ERR_INVALID
+    assert s(*args(64, 8, 0, 3)) == kp.PION_ERR_INVALID         # 3 does not divide 8
+    assert s(*args(64, 8, 64)) == kp.PION_ERR_NOT_FOUND
+    assert s(*args(64, 8, 0)) == kp.PION_ERR_NOT_FOUND
+
+
+def test_quantize_argument_validation(lib):
+    qz = lib.pion_kv_quantize_mlx4g32
+    assert qz(FAKE, 4, 48, FAKE, FAKE, FAKE, None) == kp.PION_ERR_INVALID
+    assert qz(FAKE, -1, 64, FAKE, FAKE, FAKE, None) == kp.PION_ERR_INVALID
+    assert qz(None, 4, 64, FAKE, FAKE, FAKE, None) == kp.PION_ERR_INVALID
+    assert qz(None, 0, 64, None, None, None, None) == kp.PION_OK       # empty is a no-op
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    K = torch.zeros(2, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        kp.pion_prefix_store("s", 0, K, K)

@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle on the
+same seeded fp16 inputs. Bit-exact for mlx4g32 codes/scales/biases and for the picked
+block indices; max-abs 2e-3 on fp32 outputs and 1e-4 on LSE."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-3
+LSE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def kp():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_prefix_amd as kp
+    kp.lib()          # raises if the library is not built: no fallback
+    yield kp
+    kp.pion_prefix_drop("t", -1)
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def empty(shape, dtype="float32"):
+    import torch
+    return torch.full(shape, float("nan"), dtype=getattr(torch, dtype), device="cuda") \
+        if dtype == "float32" else torch.zeros(shape, dtype=getattr(torch, dtype), device="cuda")
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check(out, lse, ref_out, ref_lse, rows=None):
+    out = np.asarray(out, np.float64)
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        out, ref_out = out[idx], ref_out[idx]
+        if lse is not None:
+            lse, ref_lse = np.asarray(lse)[idx], ref_lse[idx]
+    assert np.all(np.isfinite(out))
+    err = np.max(np.abs(out - ref_out))
+    assert err <= OUT_TOL, f"out max-abs {err}"
+    if lse is not None:
+        lerr = np.max(np.abs(np.asarray(lse, np.float64) - ref_lse))
+        assert lerr <= LSE_TOL, f"lse max-abs {lerr}"
+
+
+def query(kp, sid, layer, Q, head_map=None, want_lse=True):
+    H_q, M, D = Q.shape
+    out = empty((H_q, M, D))
+    lse = empty((H_q, M)) if want_lse else None
+    kp.pion_prefix_query(sid, layer, dev(Q), out, lse, head_map=head_map)
+    return host(out), (host(lse) if want_lse else None)
+
+
+# ------------------------------------------------------------------ tiny dense case
+def test_tiny_dense_fp16(kp):
+    inp = synth.generate(synth.TINY)
+    kp.pion_prefix_store("t", 0, dev(inp.K), dev(inp.V))
+    assert kp.pion_prefix_lookup("t", 0) == 1
+    assert kp.pion_prefix_info("t", 0) == (2, 128, 64, 0)
+    out, lse = query(kp, "t", 0, inp.Q)
+    ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+    check(out, lse, ref, ref_lse)
+
+
+def _quantize_gpu(kp, x16):
+    import torch
+    rows, D = x16.shape
+    codes = torch.zeros((rows, D // 8), dtype=torch.int32, device="cuda")
+    sc = torch.zeros((rows, D // 32), dtype=torch.float16, device="cuda")
+    bi = torch.zeros((rows, D // 32), dtype=torch.float16, device="cuda")
+    kp.pion_kv_quantize_mlx4g32(dev(x16), codes, sc, bi)
+    return host(codes).view(np.uint32), host(sc), host(bi)
+
+
+def _assert_same_encoding(got, ref):
+    np.testing.assert_array_equal(got[0], ref[0])
+    np.testing.assert_array_equal(got[1].view(np.uint16), ref[1].view(np.uint16))
+    np.testing.assert_array_equal(got[2].view(np.uint16), ref[2].view(np.uint16))
+
+
+def test_tiny_quantize_bit_exact(kp):
+    inp = synth.generate(synth.TINY)
+    for x in (inp.K, inp.V):
+        rows = x.reshape(-1, 64)
+        _assert_same_encoding(_quantize_gpu(kp, rows), oracle.quantize(rows))
+
+
+def test_tiny_mlx4g32_query(kp):
+    inp = synth.generate(synth.TINY)
+    kp.pion_prefix_store("t", 1, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 1, inp.Q)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 64))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 64))).reshape(inp.V.shape)
+    ref, ref_lse = oracle.prefix_query(inp.Q, Kh, Vh)
+    check(out, lse, ref, ref_lse)
+
+
+# ------------------------------------------------------------------ quantizer
+def test_quantize_hand_worked_group_and_edges(kp):
+    from conftest import read_golden
+    g = read_golden("mlx4g32_group.txt")
+    x = np.zeros((7, 64), np.float16)
+    x[0, :32] = np.array([float(v) for v in g["x"]], np.float16)
+    x[0, 32:] = 1.5                                     # constant group
+    x[1, 5] = np.float16(2.0 ** -24)                    # scale underflows fp16
+    x[2] = np.linspace(-65504, 65504, 64).astype(np.float16)   # extreme range
+    x[3] = (np.arange(64) * 2.0 ** -20).astype(np.float16)     # subnormal inputs
+    x[4] = np.linspace(0, 1.1, 64).astype(np.float16)
+    x[5] = -np.abs(np.random.default_rng(3).standard_normal(64)).astype(np.float16)
+    x[6] = np.random.default_rng(4).standard_normal(64).astype(np.float16) * 1000
+    got = _quantize_gpu(kp, x)
+    _assert_same_encoding(got, oracle.quantize(x))
+    assert [int(w) for w in got[0][0, :4]] == [int(w, 16) for w in g["words"]]
+
+
+@pytest.mark.parametrize("rows,D", [(1, 32), (3, 96), (257, 64), (1001, 128), (77, 256)])
+def test_quantize_ragged_shapes(kp, rows, D):
+    rng = np.random.default_rng(rows * D)
+    x = (rng.standard_normal((rows, D)) * rng.lognormal(0, 0.5, (1, D))).astype(np.float16)
+    _assert_same_encoding(_quantize_gpu(kp, x), oracle.quantize(x))
+
+
+def test_quantize_full_mlx4g32_decode_shape(kp):
+    inp = synth.generate(synth.MLX4_DECODE)
+    for x in (inp.K, inp.V):
+        rows = x.reshape(-1, 128)
+        _assert_same_encoding(_quantize_gpu(kp, rows), oracle.quantize(rows))
+
+
+# ------------------------------------------------------------------ M=1 decode, fp16
+def test_decode_shape_all_32_layers(kp):
+    case = synth.DECODE
+    for layer in range(case.layers):
+        inp = synth.generate(case, layer)
+        kp.pion_prefix_store("t", 100 + layer, dev(inp.K), dev(inp.V))
+        out, lse = query(kp, "t", 100 + layer, inp.Q)
+        ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+        check(out, lse, ref, ref_lse)
+    assert kp.pion_prefix_drop("t", 131) == 1
+    assert kp.pion_prefix_lookup("t", 131) == 0
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1000, 4097])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_decode_ragged_lengths(kp, N, D):
+    inp = synth.generate(synth.DECODE, 7, N=N, D=D, H_q=4, H_kv=4)
+    kp.pion_prefix_store("t", 2, dev(inp.K), dev(inp.V))
+    out, lse = query(kp, "t", 2, inp.Q)
+    ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+    check(out, lse, ref, ref_lse)
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(8, 1), (12, 4), (32, 2), (5, 3)])
+def test_decode_gqa_and_arbitrary_maps(kp, H_q, H_kv):
+    inp = synth.generate(synth.DECODE, 9, N=777, H_q=H_q, H_kv=H_kv)
+    hm = synth.random_head_map(H_q, H_kv, 5) if H_q % H_kv else None
+    kp.pion_prefix_store("t", 3, dev(inp.K), dev(inp.V))
+    out, lse = query(kp, "t", 3, inp.Q, head_map=hm)
+    ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V, hm)
+    check(out, lse, ref, ref_lse)
+    hm2 = synth.random_head_map(H_q, H_kv, 11)
+    out, lse = query(kp, "t", 3, inp.Q, head_map=hm2, want_lse=False)
+    ref, _ = oracle.prefix_query(inp.Q, inp.K, inp.V, hm2)
+    check(out, None, ref, None)
+
+
+def test_restore_replaces_and_unknown_session(kp):
+    import kv_cache_prefix_amd as k
+    a = synth.generate(synth.DECODE, 1, N=100, H_q=2, H_kv=2)
+    b = synth.generate(synth.DECODE, 2, N=300, H_q=2, H_kv=2)
+    kp.pion_prefix_store("t", 4, dev(a.K), dev(a.V))
+    kp.pion_prefix_store("t", 4, dev(b.K), dev(b.V))
+    assert kp.pion_prefix_info("t", 4)[1] == 300
+    out, lse = query(kp, "t", 4, b.Q)
+    check(out, lse, *oracle.prefix_query(b.Q, b.K, b.V))
+    with pytest.raises(k.PionError) as e:
+        query(kp, "t", 999, b.Q)
+    assert e.value.status == k.PION_ERR_NOT_FOUND
+
+
+# ------------------------------------------------------------------ batched-Q and fused
+@pytest.mark.parametrize("M,S_suf", [(1, 0), (5, 0), (1, 64), (7, 7), (3, 70), (70, 70)])
+def test_fused_small(kp, M, S_suf):
+    inp = synth.generate(synth.PREFILL, N=300, M=M, S_suf=S_suf, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 5, dev(inp.K), dev(inp.V))
+    out = empty((6, M, 128))
+    lse = empty((6, M))
+    if S_suf:
+        kp.pion_prefix_query_fused("t", 5, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    else:
+        kp.pion_prefix_query_fused("t", 5, dev(inp.Q), None, None, out, lse, H_kv=2)
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+    check(host(out), host(lse), ref, ref_lse)
+
+
+def test_batched_query_matches_m1_rows(kp):
+    inp = synth.generate(synth.PREFILL, N=500, M=9, S_suf=0, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 6, dev(inp.K), dev(inp.V))
+    out, lse = query(kp, "t", 6, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, inp.K, inp.V))
+
+
+def test_fused_prefill_full_size_sampled_rows(kp):
+    case = synth.PREFILL
+    inp = synth.generate(case)
+    kp.pion_prefix_store("t", 7, dev(inp.K), dev(inp.V))
+    out = empty((24, 512, 128))
+    lse = empty((24, 512))
+    kp.pion_prefix_query_fused("t", 7, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    out, lse = host(out), host(lse)
+    rng = np.random.default_rng(0)
+    rows = [(h, i) for h in (0, 1, 2, 12, 23) for i in (0, 1, 255, 510, 511)]
+    rows += [(int(h), int(i)) for h, i in zip(rng.integers(0, 24, 40), rng.integers(0, 512, 40))]
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
+    check(out, lse, ref, ref_lse, rows=rows)
+    assert np.all(np.isfinite(out))
+
+
+# ------------------------------------------------------------------ mlx4g32 decode
+def test_mlx4g32_decode_full_size(kp):
+    case = synth.MLX4_DECODE
+    inp = synth.generate(case)
+    kp.pion_prefix_store("t", 8, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 8, inp.Q, head_map=inp.head_map)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+    ref, ref_lse = oracle.prefix_query(inp.Q, Kh, Vh, inp.head_map)
+    check(out, lse, ref, ref_lse)
+
+
+@pytest.mark.parametrize("N,D,H_q,H_kv", [(1, 64, 2, 2), (99, 128, 6, 2), (1000, 256, 8, 1)])
+def test_mlx4g32_decode_ragged(kp, N, D, H_q, H_kv):
+    inp = synth.generate(synth.MLX4_DECODE, 3, N=N, D=D, H_q=H_q, H_kv=H_kv)
+    kp.pion_prefix_store("t", 9, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 9, inp.Q)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, D))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, D))).reshape(inp.V.shape)
+    check(out, lse, *oracle.prefix_query(inp.Q, Kh, Vh))
+
+
+def test_mlx4g32_fused_suffix(kp):
+    inp = synth.generate(synth.MLX4_DECODE, 4, N=500, H_q=6, H_kv=2, M=3, S_suf=40)
+    kp.pion_prefix_store("t", 10, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = empty((6, 3, 128)), empty((6, 3))
+    kp.pion_prefix_query_fused("t", 10, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, Kh, Vh, inp.K_suf, inp.V_suf))
+
+
+# ------------------------------------------------------------------ sparse-auto
+def sparse_call(kp, sid, layer, inp, B, K_top, H_kv, suffix=True, head_map=None):
+    import torch
+    H_q, _, D = inp.Q.shape
+    out, lse = empty((H_q, D)), empty((H_q,))
+    blocks = torch.full((H_kv, K_top), -7, dtype=torch.int32, device="cuda")
+    ks = dev(inp.K_suf) if (suffix and inp.K_suf is not None) else None
+    vs = dev(inp.V_suf) if (suffix and inp.V_suf is not None) else None
+    kp.pion_prefix_query_sparse_auto(sid, layer, dev(inp.Q), B, K_top, out, lse, blocks,
+                                     ks, vs, head_map=head_map, H_kv=H_kv)
+    return host(out), host(lse), host(blocks)
+
+
+def test_sparse_auto_full_size(kp):
+    case = synth.SPARSE
+    inp = synth.generate(case)
+    kp.pion_prefix_store("t", 11, dev(inp.K), dev(inp.V))
+    for fused in (True, False):
+        out, lse, blocks = sparse_call(kp, "t", 11, inp, case.B, case.K_top, 1, suffix=fused)
+        ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(
+            inp.Q, inp.K, inp.V, case.B, case.K_top, inp.head_map,
+            inp.K_suf if fused else None, inp.V_suf if fused else None)
+        np.testing.assert_array_equal(blocks, ref_blocks)
+        np.testing.assert_array_equal(blocks[0], inp.needles[0])
+        check(out, lse, ref, ref_lse)
+
+
+@pytest.mark.parametrize("N,B,K_top", [(1000, 64, 3), (640, 64, 10), (650, 64, 40), (257, 16, 5)])
+def test_sparse_auto_edges(kp, N, B, K_top):
+    inp = synth.generate(synth.SPARSE, 2, N=N, H_q=4, H_kv=2, D=64, S_suf=12, n_needles=2)
+    kp.pion_prefix_store("t", 12, dev(inp.K), dev(inp.V))
+    out, lse, blocks = sparse_call(kp, "t", 12, inp, B, K_top, 2)
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(
+        inp.Q, inp.K, inp.V, B, K_top, inp.head_map, inp.K_suf, inp.V_suf)
+    np.testing.assert_array_equal(blocks, ref_blocks)
+    check(out, lse, ref, ref_lse)
+
+
+def test_sparse_auto_tie_goes_to_lower_block(kp):
+    inp = synth.generate(synth.SPARSE, 3, N=64 * 20, H_q=2, H_kv=1, D=128, S_suf=0, n_needles=0)
+    K = inp.K.copy()
+    K[0, 13 * 64:14 * 64] = K[0, 4 * 64:5 * 64]            # block 13 duplicates block 4
+    km = oracle.block_means(K, 64)
+    Q = inp.Q.copy()
+    Q[:, 0, :] = (km[0, 4] * 4).astype(np.float16)            # point both heads at block 4
+    inp.Q, inp.K = Q, K
+    kp.pion_prefix_store("t", 13, dev(K), dev(inp.V))
+    out, lse, blocks = sparse_call(kp, "t", 13, inp, 64, 1, 1, suffix=False)
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(Q, K, inp.V, 64, 1)
+    assert ref_blocks[0, 0] == 4 and blocks[0, 0] == 4
+    check(out, lse, ref, ref_lse)
+
+
+def test_sparse_auto_mlx4g32_slot(kp):
+    inp = synth.generate(synth.SPARSE, 4, N=64 * 30, H_q=4, H_kv=1, D=128, S_suf=8, n_needles=3)
+    kp.pion_prefix_store("t", 14, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse, blocks = sparse_call(kp, "t", 14, inp, 64, 3, 1)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(inp.Q, Kh, Vh, 64, 3, None,
+                                                               inp.K_suf, inp.V_suf)
+    np.testing.assert_array_equal(blocks, ref_blocks)
+    np.testing.assert_array_equal(blocks[0], inp.needles[0])
+    check(out, lse, ref, ref_lse)
+
+
+# ------------------------------------------------------------------ streams
+def test_store_on_one_stream_query_on_another(kp):
+    import torch
+    inp = synth.generate(synth.DECODE, 5, N=3000, H_q=8, H_kv=8)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    K, V, Q = dev(inp.K), dev(inp.V), dev(inp.Q)
+    torch.cuda.synchronize()
+    out, lse = empty((8, 1, 128)), empty((8, 1))
+    kp.pion_prefix_store("t", 15, K, V, stream=s1)
+    kp.pion_prefix_query("t", 15, Q, out, lse, stream=s2)
+    torch.cuda.synchronize()
+    check(host(out), host(lse), *oracle.prefix_query(inp.Q, inp.K, inp.V))
