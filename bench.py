@@ -7,14 +7,15 @@ out + LSE per layer - the shape the pages quote their M=1 latency on. Inputs are
 seeded synthetic generators (K with per-channel lognormal(0, 0.5) scales, Q and V
 N(0, 1)); all of it is resident in HBM before the timed region starts.
 
-Timed region: K steps, each the 32 pion_prefix_query calls issued through the C ABI on
-one HIP stream. The 32 calls of a step are captured once into a HIP graph (after an
-eager warm-up) and the graph is replayed per step, so the device runs the kernels
-back-to-back without host launch gaps (--eager issues them from the host instead).
-Per-launch duration: after the timed region, the same calls are issued eagerly with a
-HIP event pair around each one on the launch stream; the roofline figure uses the
-algorithmic K/V bytes of one launch (8 heads x 2048 tokens x 2 x 128 x 2 B =
-8,388,608 B) over the mean of those durations.
+Timed region: K steps on one HIP stream. Default (--mode layers): a step is one
+pion_prefix_query_layers call covering the 32 layers (one kernel launch). --mode calls:
+a step is 32 pion_prefix_query calls. The step's calls are captured once into a HIP
+graph (after an eager warm-up) and the graph is replayed per step (--eager issues them
+from the host instead). Per-launch duration: after the timed region, the same calls
+are issued eagerly with a HIP event pair around each one on the launch stream; the
+roofline figure uses the algorithmic K/V bytes of one launch (per layer: 8 heads x
+2048 tokens x (K + V) x 128 x 2 B = 8,388,608 B; 268,435,456 B for the 32-layer launch)
+over the mean of those durations.
 
 cpu_baseline: the fp64 numpy oracle as it stands, one thread, on whole 32-layer passes
 of the same inputs, repeated for about 10 s.
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue calls from the host, no graph")
+    ap.add_argument("--mode", choices=["layers", "calls"], default="layers",
+                    help="layers: one pion_prefix_query_layers launch per step; "
+                         "calls: 32 pion_prefix_query calls per step")
     return ap.parse_args()
 
 
@@ -97,8 +101,19 @@ def main():
     sidb = sid.encode()
     stream = torch.cuda.Stream(device=dev)
     # raw arguments, marshalled once
-    calls = [(sidb, l, case.H_q, case.D, 1, Qs[l].data_ptr(), None, outs[l].data_ptr(),
-              lses[l].data_ptr()) for l in range(case.layers)]
+    Qall = torch.stack(Qs).contiguous()
+    out_all = torch.empty((case.layers, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
+    lse_all = torch.empty((case.layers, case.H_q, 1), dtype=torch.float32, device=dev)
+    if args.mode == "layers":
+        fn = lib.pion_prefix_query_layers
+        calls = [(sidb, 0, case.layers, case.H_q, case.D, 1, Qall.data_ptr(), None,
+                  out_all.data_ptr(), lse_all.data_ptr())]
+        outs = list(out_all)
+        lses = list(lse_all)
+    else:
+        fn = lib.pion_prefix_query
+        calls = [(sidb, l, case.H_q, case.D, 1, Qs[l].data_ptr(), None, outs[l].data_ptr(),
+                  lses[l].data_ptr()) for l in range(case.layers)]
     starts = [torch.cuda.Event(enable_timing=True) for _ in calls]
     ends = [torch.cuda.Event(enable_timing=True) for _ in calls]
 
@@ -107,9 +122,9 @@ def main():
         for i, c in enumerate(calls):
             if timed_events:
                 starts[i].record()
-            rc = lib.pion_prefix_query(*c, h)
+            rc = fn(*c, h)
             if rc != 0:
-                raise kp.PionError(rc, "pion_prefix_query")
+                raise kp.PionError(rc, fn.__name__)
             if timed_events:
                 ends[i].record()
 
@@ -150,8 +165,9 @@ def main():
             launch_ms += [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
     avg_launch_us = 1e3 * float(np.mean(launch_ms))
-    bytes_per_launch = case.H_kv * case.N * case.D * 2 * 2
-    bytes_per_step = bytes_per_launch * case.layers
+    bytes_per_layer = case.H_kv * case.N * case.D * 2 * 2
+    bytes_per_step = bytes_per_layer * case.layers
+    bytes_per_launch = bytes_per_step // len(calls)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
 
@@ -182,12 +198,15 @@ def main():
         "data": "synthetic (seeded numpy: K N(0,1) x lognormal(0,0.5) per channel, Q/V N(0,1))",
         "config": {"workload": "M=1 prefix attention, decode shape H_q=H_kv=8 N=2048 D=128, "
                                "32 resident layers queried back-to-back per step",
+                   "entry": fn.__name__,
+                   "launches_per_step": len(calls),
                    "launch": "eager" if graph is None else "hip-graph replay",
                    "bytes_per_step": bytes_per_step},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None,
-                     "kernel": "partial_fp16_kernel<128,1,4> (split-KV decode + in-kernel merge)",
+                     "kernel": "attn_split_kernel<128,1,4,0> (split-KV decode + in-kernel merge)",
+                     "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": round(avg_launch_us, 3)},
         "cpu_baseline": cpu,
     }

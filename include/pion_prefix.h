@@ -94,6 +94,19 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M,
                       const void *Q, const int32_t *head_map,
                       float *out, float *lse, void *stream);
 
+/* Batched form of pion_prefix_query over the layers layer0 .. layer0 + n_layers - 1 of
+ * one session, computed in a single launch. Not a wire form of the pages: it issues the
+ * per-layer ATTEND.PREFIX.QUERY calls of independent layers together, so the device
+ * streams every layer's K/V in one pass instead of paying launch and merge latency
+ * per layer. Each layer's result is exactly that of pion_prefix_query.
+ *   Q    fp16 [n_layers, H_q, M, D]; out fp32 [n_layers, H_q, M, D];
+ *   lse  fp32 [n_layers, H_q, M] or NULL.
+ * All slots must exist (else NOT_FOUND) and share H, D and kv_format (else INVALID);
+ * N may differ per layer. 1 <= n_layers <= 64. Other errors as pion_prefix_query. */
+int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q, int D, int M,
+                             const void *Q, const int32_t *head_map, float *out, float *lse,
+                             void *stream);
+
 /* ATTEND.PREFIX.QUERY_FUSED <sid> <layer> <H_q> <D> <S_suf> <H_kv> <Q> <K_suf> <V_suf>
  * <head_map>: the caller's dense suffix attention merged with the resident prefix in
  * one call (ATTEND.* page, QUERY_FUSED row; GQA-aware).

@@ -33,6 +33,8 @@ SIGNATURES = {
     "pion_prefix_drop": (_int, [_c_char_p, _int]),
     "pion_prefix_info": (_int, [_c_char_p, _int, _vp, _vp, _vp, _vp]),
     "pion_prefix_query": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query_layers": (_int, [_c_char_p, _int, _int, _int, _int, _int, _vp, _vp, _vp,
+                                        _vp, _vp]),
     "pion_prefix_query_fused": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pion_prefix_query_sparse_auto": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,
@@ -146,6 +148,20 @@ def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=N
         _dev(out, torch.float32, "out", (H_q, M, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (H_q, M)), _stream(stream))
     return _check(rc, "pion_prefix_query")
+
+
+def pion_prefix_query_layers(sid, layer0: int, Q, out, lse=None, head_map=None,
+                             stream=None) -> int:
+    """Layers layer0 .. layer0 + n - 1 in one launch: Q fp16 [n, H_q, M, D] ->
+    out fp32 [n, H_q, M, D], lse fp32 [n, H_q, M]."""
+    import torch
+    n, H_q, M, D = Q.shape
+    hm, hm_ptr = _head_map(head_map, H_q)
+    rc = lib().pion_prefix_query_layers(
+        _sid(sid), layer0, n, H_q, D, M, _dev(Q, torch.float16, "Q"), hm_ptr,
+        _dev(out, torch.float32, "out", (n, H_q, M, D)),
+        None if lse is None else _dev(lse, torch.float32, "lse", (n, H_q, M)), _stream(stream))
+    return _check(rc, "pion_prefix_query_layers")
 
 
 def pion_prefix_query_fused(sid, layer: int, Q, K_suf, V_suf, out, lse=None, head_map=None,

@@ -20,6 +20,41 @@ struct RowGroups {
   uint8_t heads[kMaxHeads][kRowsPerGroup];
 };
 
+constexpr int kMaxBatch = 64;     // problems (layers) per launch
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte offsets of the arrays inside one slot allocation; host (store) and device
+// (query) both derive pointers from this. fp16: K, V [H, N, D]. mlx4g32: K codes
+// [H, N, D/8] u32, K scales, K biases [H, N, D/32] fp16, then the same three for V.
+struct SlotLayout {
+  size_t off[6];
+  size_t bytes;
+};
+
+__host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int N, int D) {
+  SlotLayout L;
+  const size_t elems = (size_t)H * N * D;
+  if (fmt == 0) {
+    const size_t b = (elems * 2 + 255) & ~(size_t)255;
+    L.off[0] = 0;
+    L.off[1] = b;
+    L.off[2] = L.off[3] = L.off[4] = L.off[5] = 0;
+    L.bytes = 2 * b;
+  } else {
+    const size_t cb = (elems / 2 + 255) & ~(size_t)255;
+    const size_t sb = (elems / 16 + 255) & ~(size_t)255;
+    L.off[0] = 0;
+    L.off[1] = cb;
+    L.off[2] = cb + sb;
+    L.off[3] = cb + 2 * sb;
+    L.off[4] = 2 * cb + 2 * sb;
+    L.off[5] = 2 * cb + 3 * sb;
+    L.bytes = 2 * cb + 4 * sb;
+  }
+  return L;
+}
+
 // One resident prefix as the kernels see it.
 struct KVView {
   int fmt;              // 0 fp16, 1 mlx4g32
@@ -29,29 +64,64 @@ struct KVView {
   const uint16_t *Ks, *Kb, *Vs, *Vb;     // mlx4g32 scales / biases [H, N, D/32]
 };
 
-// Split-over-keys attention. Workgroup (x, y): y = head group * M + query index,
-// x = key span. Spans [0, pre_splits) cover the prefix (dense chunks of pre_chunk
-// tokens, or with `blocks` one selected block each); spans [pre_splits, S_total) cover
-// the fp16 suffix in chunks of suf_chunk tokens, clipped to the causal limit.
-// Partials (acc unnormalized against m, m and l in log2 units) go to
-// part_acc [H_q*M][S_total][D], part_m / part_l [H_q*M][S_total]; the last workgroup
-// of each y (ticket on counters[y], which must start at zero and is left at zero)
-// merges them into out [H_q*M][D] and lse [H_q*M].
+__host__ __device__ inline KVView make_view(const void *base, int fmt, int H, int N, int D) {
+  const SlotLayout L = slot_layout(fmt, H, N, D);
+  const char *b = (const char *)base;
+  KVView v;
+  v.fmt = fmt;
+  v.H = H;
+  v.N = N;
+  v.D = D;
+  v.K = v.V = nullptr;
+  v.Kc = v.Vc = nullptr;
+  v.Ks = v.Kb = v.Vs = v.Vb = nullptr;
+  if (fmt == 0) {
+    v.K = (const uint16_t *)(b + L.off[0]);
+    v.V = (const uint16_t *)(b + L.off[1]);
+  } else {
+    v.Kc = (const uint32_t *)(b + L.off[0]);
+    v.Ks = (const uint16_t *)(b + L.off[1]);
+    v.Kb = (const uint16_t *)(b + L.off[2]);
+    v.Vc = (const uint32_t *)(b + L.off[3]);
+    v.Vs = (const uint16_t *)(b + L.off[4]);
+    v.Vb = (const uint16_t *)(b + L.off[5]);
+  }
+  return v;
+}
+
+// Split-over-keys attention for up to kMaxBatch independent problems (resident slots
+// of identical H, D and format, e.g. the layers of one session) in one launch.
+// Workgroup (x, y, z): z = problem, y = head group * M + query index, x = key span.
+// Spans [0, pre_splits) cover the prefix (dense chunks of pre_chunk tokens, or with
+// `blocks` one selected block each); spans [pre_splits, pre_splits + suf_splits)
+// cover the fp16 suffix in chunks of suf_chunk tokens, clipped to the causal limit.
+// Partials (acc unnormalized against m; m and l in log2 units) of problem z go to
+// part_acc + z*part_stride as [H_q*M][S_max][D] and part_m / part_l + z*ml_stride as
+// [H_q*M][S_max]; the last workgroup of each (z, y) (ticket on counters[z*y_groups+y],
+// which start at zero and are left at zero) merges them into out and lse.
 struct PartialParams {
-  const uint16_t *Q;    // fp16 [H_q, M, D]
-  int H_q, M;
-  float qscale;         // log2(e) / sqrt(D)
-  KVView kv;
-  int pre_splits, pre_chunk;
-  const int32_t *blocks;  // [H_kv, K_top] or null
-  int K_top, B;
-  const uint16_t *Ksuf, *Vsuf;  // fp16 [H_kv, S_suf, D]
-  int S_suf, suf_chunk;
-  int S_total;
+  int H_q, M, D, H_kv, fmt;
+  float qscale;           // log2(e) / sqrt(D)
+  int n_prob;
+  const void *kv_base[kMaxBatch];
+  int N[kMaxBatch];
+  const uint16_t *Q;      // fp16 [n_prob][H_q, M, D]
+  size_t q_stride;
+  float *out;             // [n_prob][H_q, M, D]
+  size_t out_stride;
+  float *lse;             // [n_prob][H_q, M] or null
+  size_t lse_stride;
+  int pre_chunk;
+  const int32_t *blocks;  // [H_kv, K_top] or null (single problem only)
+  int K_top, B, n_sel;
+  const uint16_t *Ksuf, *Vsuf;  // fp16 [H_kv, S_suf, D] (single problem only)
+  int S_suf, suf_chunk, suf_splits;
+  int S_max;              // span stride of the partial layout
   int x_begin;            // span index of this launch's blockIdx.x == 0
   float *part_acc, *part_m, *part_l;
-  int *counters;          // [y_groups], zero between calls
-  float *out, *lse;       // lse may be null
+  size_t part_stride, ml_stride;
+  int *counters;
+  int y_groups;
   RowGroups rg;
 };
 
@@ -61,11 +131,11 @@ struct HeadMap {
   uint8_t m[kMaxHeads];
 };
 
-
-// Launches spans [x_begin, x_begin + x_count). mlx4_prefix selects the kernel that reads
-// an mlx4g32 prefix (those spans must all be prefix spans); otherwise the fp16 kernel.
-hipError_t launch_partial(const PartialParams &p, int rows_per_group, int y_groups,
-                          int x_count, bool mlx4_prefix, hipStream_t s);
+// Launches spans [x_begin, x_begin + x_count) of every problem. mlx4_prefix selects the
+// kernel that reads an mlx4g32 prefix (it skips suffix spans); otherwise the fp16 kernel
+// (it skips prefix spans of an mlx4g32 slot).
+hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_count,
+                          bool mlx4_prefix, hipStream_t s);
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);
 

@@ -34,7 +34,7 @@ namespace {
 
 using namespace pion;
 
-constexpr int kMaxSplitsTotal = 1024;
+constexpr int kMaxSplitsTotal = 1024;  // spans per row: the in-kernel merge limit
 constexpr int kMaxKTop = 1024;
 
 struct KMean {
@@ -113,8 +113,6 @@ bool on_device(const void *p) {
   return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged ||
          a.type == hipMemoryTypeUnified;
 }
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // fp16 tensors are read with 16-byte vector loads; fp32 / int32 with 4-byte accesses.
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -219,10 +217,10 @@ int build_groups(const std::vector<int> &hm, int H_kv, RowGroups &rg) {
   return R;
 }
 
-int pick_chunk(long long keys, long long y, int granule) {
+int pick_chunk(long long keys, long long work_rows, int granule) {
   if (keys <= 0) return granule;
   const long long target = split_target();
-  long long c = (keys * y + target - 1) / target;
+  long long c = (keys * work_rows + target - 1) / target;
   c = std::max<long long>(c, granule);
   c = (c + granule - 1) / granule * granule;
   // keep the span count within the in-kernel merge limit (1024 spans)
@@ -232,6 +230,7 @@ int pick_chunk(long long keys, long long y, int granule) {
 
 struct AttnCall {
   const uint16_t *Q;
+  size_t q_stride;        // elements between problems
   int H_q, M, D;
   const std::vector<int> *hm;
   int H_kv;
@@ -240,63 +239,84 @@ struct AttnCall {
   const int32_t *blocks;  // device [H_kv, K_top] or null
   int n_sel, K_top, B;
   float *out, *lse;
+  size_t out_stride, lse_stride;
 };
 
-int run_attention(const Slot &sl, const AttnCall &c, hipStream_t st) {
-  PartialParams p;
+// One launch (two for an mlx4g32 prefix with an fp16 suffix) over `slots`, which share
+// H, D and format.
+int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hipStream_t st) {
+  static PartialParams p;  // large; the library lock serializes callers
   memset(&p, 0, sizeof(p));
+  const int n_prob = (int)slots.size();
+  const Slot &s0 = *slots[0];
   const int R = build_groups(*c.hm, c.H_kv, p.rg);
   const int Y = p.rg.n * c.M;
-  if (Y > 65535 || Y > kMaxCounters) return PION_ERR_UNSUPPORTED;  // grid.y limit
-  p.Q = c.Q;
+  if (Y > 65535 || (long long)Y * n_prob > kMaxCounters) return PION_ERR_UNSUPPORTED;
   p.H_q = c.H_q;
   p.M = c.M;
+  p.D = c.D;
+  p.H_kv = s0.H;
+  p.fmt = s0.fmt;
   p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
-  p.kv = sl.view;
+  p.n_prob = n_prob;
+  int N_max = 0;
+  for (int z = 0; z < n_prob; ++z) {
+    p.kv_base[z] = slots[z]->mem;
+    p.N[z] = slots[z]->N;
+    N_max = std::max(N_max, slots[z]->N);
+  }
+  p.Q = c.Q;
+  p.q_stride = c.q_stride;
+  p.out = c.out;
+  p.out_stride = c.out_stride;
+  p.lse = c.lse;
+  p.lse_stride = c.lse_stride;
+  int pre_max;
   if (c.blocks) {
     p.blocks = c.blocks;
     p.K_top = c.K_top;
     p.B = c.B;
-    p.pre_splits = c.n_sel;
+    p.n_sel = c.n_sel;
     p.pre_chunk = c.B;
+    pre_max = c.n_sel;
   } else {
-    p.pre_chunk = pick_chunk(sl.N, Y, 64);
-    p.pre_splits = (sl.N + p.pre_chunk - 1) / p.pre_chunk;
+    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64);
+    pre_max = (N_max + p.pre_chunk - 1) / p.pre_chunk;
   }
-  int suf_splits = 0;
   if (c.S_suf > 0) {
     p.Ksuf = c.Ksuf;
     p.Vsuf = c.Vsuf;
     p.S_suf = c.S_suf;
     p.suf_chunk = pick_chunk(c.S_suf, Y, 64);
-    suf_splits = (c.S_suf + p.suf_chunk - 1) / p.suf_chunk;
+    p.suf_splits = (c.S_suf + p.suf_chunk - 1) / p.suf_chunk;
   }
-  p.S_total = p.pre_splits + suf_splits;
-  if (p.S_total > kMaxSplitsTotal) return PION_ERR_UNSUPPORTED;
+  p.S_max = pre_max + p.suf_splits;
+  if (p.S_max > kMaxSplitsTotal) return PION_ERR_UNSUPPORTED;
+  p.y_groups = Y;
 
   const size_t rows = (size_t)c.H_q * c.M;
-  const size_t acc_bytes = align256(rows * p.S_total * c.D * sizeof(float));
-  const size_t ml_bytes = align256(rows * p.S_total * sizeof(float));
+  p.part_stride = rows * p.S_max * c.D;
+  p.ml_stride = rows * p.S_max;
+  const size_t acc_bytes = align256(n_prob * p.part_stride * sizeof(float));
+  const size_t ml_bytes = align256(n_prob * p.ml_stride * sizeof(float));
   void *ws = nullptr;
   if (get_ws(st, acc_bytes + 2 * ml_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
   p.part_acc = (float *)ws;
   p.part_m = (float *)((char *)ws + acc_bytes);
   p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
   p.counters = g_ws[st].counters;
-  p.out = c.out;
-  p.lse = c.lse;
 
   hipError_t e;
-  if (sl.fmt == PION_KV_MLX4G32) {
+  if (p.fmt == PION_KV_MLX4G32) {
     p.x_begin = 0;
-    e = launch_partial(p, R, Y, p.pre_splits, true, st);
-    if (e == hipSuccess && suf_splits > 0) {
-      p.x_begin = p.pre_splits;
-      e = launch_partial(p, R, Y, suf_splits, false, st);
+    e = launch_partial(p, R, pre_max, true, st);
+    if (e == hipSuccess && p.suf_splits > 0) {
+      p.x_begin = pre_max;  // single problem: its prefix spans are exactly pre_max
+      e = launch_partial(p, R, p.suf_splits, false, st);
     }
   } else {
     p.x_begin = 0;
-    e = launch_partial(p, R, Y, p.S_total, false, st);
+    e = launch_partial(p, R, p.S_max, false, st);
   }
   return e == hipSuccess ? PION_OK : PION_ERR_HIP;
 }
@@ -369,51 +389,26 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
   sl.N = N;
   sl.D = D;
   sl.fmt = kv_format;
-  size_t off[6] = {0};
-  if (kv_format == PION_KV_FP16) {
-    off[0] = 0;
-    off[1] = align256(elems * 2);
-    sl.bytes = off[1] + align256(elems * 2);
-  } else {
-    const size_t cb = align256(elems / 2), sb = align256(elems / 16);
-    off[0] = 0;             // K codes
-    off[1] = cb;            // K scales
-    off[2] = cb + sb;       // K biases
-    off[3] = cb + 2 * sb;   // V codes
-    off[4] = 2 * cb + 2 * sb;
-    off[5] = 2 * cb + 3 * sb;
-    sl.bytes = 2 * cb + 4 * sb;
-  }
+  const SlotLayout L = slot_layout(kv_format, H, N, D);
+  sl.bytes = L.bytes;
   if (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
     (void)hipGetLastError();
     return PION_ERR_NOMEM;
   }
   char *base = (char *)sl.mem;
-  KVView &v = sl.view;
-  v.fmt = kv_format;
-  v.H = H;
-  v.N = N;
-  v.D = D;
+  sl.view = make_view(sl.mem, kv_format, H, N, D);
   hipError_t e;
   if (kv_format == PION_KV_FP16) {
-    v.K = (const uint16_t *)(base + off[0]);
-    v.V = (const uint16_t *)(base + off[1]);
-    e = hipMemcpyAsync(base + off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
+    e = hipMemcpyAsync(base + L.off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(base + off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
+      e = hipMemcpyAsync(base + L.off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
   } else {
-    v.Kc = (const uint32_t *)(base + off[0]);
-    v.Ks = (const uint16_t *)(base + off[1]);
-    v.Kb = (const uint16_t *)(base + off[2]);
-    v.Vc = (const uint32_t *)(base + off[3]);
-    v.Vs = (const uint16_t *)(base + off[4]);
-    v.Vb = (const uint16_t *)(base + off[5]);
     const int64_t rows = (int64_t)H * N;
-    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + off[0]),
-                                (uint16_t *)(base + off[1]), (uint16_t *)(base + off[2]), st);
+    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + L.off[0]),
+                                (uint16_t *)(base + L.off[1]), (uint16_t *)(base + L.off[2]), st);
     if (e == hipSuccess)
-      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + off[3]),
-                                  (uint16_t *)(base + off[4]), (uint16_t *)(base + off[5]), st);
+      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[3]),
+                                  (uint16_t *)(base + L.off[4]), (uint16_t *)(base + L.off[5]), st);
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(sl.ready, st);
@@ -495,7 +490,47 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const v
   c.H_kv = sl->H;
   c.out = out;
   c.lse = lse;
-  return run_attention(*sl, c, st);
+  return run_attention({sl}, c, st);
+}
+
+int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q, int D, int M,
+                             const void *Q, const int32_t *head_map, float *out, float *lse,
+                             void *stream) {
+  int rc = check_query_args(sid, H_q, D, M, Q, out);
+  if (rc != PION_OK) return rc;
+  if (n_layers < 1 || n_layers > kMaxBatch) return PION_ERR_INVALID;
+  if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  std::vector<const Slot *> slots(n_layers);
+  for (int i = 0; i < n_layers; ++i) {
+    Slot *sl = find_slot(sid, layer0 + i);
+    if (!sl) return PION_ERR_NOT_FOUND;
+    slots[i] = sl;
+  }
+  const Slot &s0 = *slots[0];
+  for (const Slot *sl : slots)
+    if (sl->D != D || sl->H != s0.H || sl->fmt != s0.fmt) return PION_ERR_INVALID;
+  std::vector<int> hm;
+  if (!resolve_map(head_map, H_q, s0.H, hm)) return PION_ERR_INVALID;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  for (int i = 0; i < n_layers; ++i) {
+    Slot *sl = find_slot(sid, layer0 + i);
+    if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+  }
+  AttnCall c{};
+  c.Q = (const uint16_t *)Q;
+  c.q_stride = (size_t)H_q * M * D;
+  c.H_q = H_q;
+  c.M = M;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = s0.H;
+  c.out = out;
+  c.out_stride = (size_t)H_q * M * D;
+  c.lse = lse;
+  c.lse_stride = (size_t)H_q * M;
+  return run_attention(slots, c, st);
 }
 
 int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, int S_suf,
@@ -529,7 +564,7 @@ int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, i
   c.S_suf = S_suf;
   c.out = out;
   c.lse = lse;
-  return run_attention(*sl, c, st);
+  return run_attention({sl}, c, st);
 }
 
 int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, int B, int K_top,
@@ -628,7 +663,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   c.B = B;
   c.out = out;
   c.lse = lse;
-  return run_attention(*sl, c, st);
+  return run_attention({sl}, c, st);
 }
 
 }  // extern "C"

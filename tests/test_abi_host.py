@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -83,6 +83,14 @@ def test_query_argument_validation(lib):
     assert q(b"s", 0, 2, 64, 1, FAKE, None, None, None, None) == kp.PION_ERR_INVALID
     assert q(b"s", 0, 2, 80, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_UNSUPPORTED
     assert q(b"s", 0, 2, 64, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_NOT_FOUND
+
+
+def test_layers_argument_validation(lib):
+    ql = lib.pion_prefix_query_layers
+    assert ql(b"s", 0, 0, 8, 128, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert ql(b"s", 0, 65, 8, 128, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_INVALID
+    assert ql(b"s", 0, 32, 8, 100, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_UNSUPPORTED
+    assert ql(b"s", 0, 32, 8, 128, 1, FAKE, None, FAKE, None, None) == kp.PION_ERR_NOT_FOUND
 
 
 def test_fused_argument_validation(lib):

@@ -338,3 +338,67 @@ def test_store_on_one_stream_query_on_another(kp):
     kp.pion_prefix_query("t", 15, Q, out, lse, stream=s2)
     torch.cuda.synchronize()
     check(host(out), host(lse), *oracle.prefix_query(inp.Q, inp.K, inp.V))
+
+
+# ------------------------------------------------------------------ batched layers
+def test_query_layers_decode_shape(kp):
+    import torch
+    case = synth.DECODE
+    inputs = [synth.generate(case, l) for l in range(case.layers)]
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store("t", 200 + l, dev(inp.K), dev(inp.V))
+    Q = dev(np.stack([inp.Q for inp in inputs]))
+    out, lse = empty((32, 8, 1, 128)), empty((32, 8, 1))
+    kp.pion_prefix_query_layers("t", 200, Q, out, lse)
+    out, lse = host(out), host(lse)
+    for l, inp in enumerate(inputs):
+        check(out[l], lse[l], *oracle.prefix_query(inp.Q, inp.K, inp.V))
+    # the same numbers as the per-layer call
+    o1, l1 = query(kp, "t", 213, inputs[13].Q)
+    np.testing.assert_allclose(out[13], o1, atol=1e-6)
+
+
+def test_query_layers_ragged_lengths_and_gqa(kp):
+    Ns = [1, 65, 300, 2049, 77]
+    inputs = [synth.generate(synth.MLX4_DECODE, l, N=N, H_q=6, H_kv=2, D=64, M=3)
+              for l, N in enumerate(Ns)]
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store("t", 300 + l, dev(inp.K), dev(inp.V))
+    hm = np.array([1, 0, 1, 1, 0, 0], np.int32)
+    Q = dev(np.stack([inp.Q for inp in inputs]))
+    out, lse = empty((5, 6, 3, 64)), empty((5, 6, 3))
+    kp.pion_prefix_query_layers("t", 300, Q, out, lse, head_map=hm)
+    out, lse = host(out), host(lse)
+    for l, inp in enumerate(inputs):
+        check(out[l], lse[l], *oracle.prefix_query(inp.Q, inp.K, inp.V, hm))
+
+
+def test_query_layers_mlx4g32(kp):
+    inputs = [synth.generate(synth.MLX4_DECODE, l, N=1000 + 100 * l, H_q=24, H_kv=8)
+              for l in range(3)]
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store("t", 400 + l, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    Q = dev(np.stack([inp.Q for inp in inputs]))
+    out, lse = empty((3, 24, 1, 128)), empty((3, 24, 1))
+    kp.pion_prefix_query_layers("t", 400, Q, out, lse)
+    out, lse = host(out), host(lse)
+    for l, inp in enumerate(inputs):
+        Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+        Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+        check(out[l], lse[l], *oracle.prefix_query(inp.Q, Kh, Vh))
+
+
+def test_query_layers_rejects_mixed_slots(kp):
+    import kv_cache_prefix_amd as k
+    a = synth.generate(synth.DECODE, 1, N=100, H_q=2, H_kv=2)
+    kp.pion_prefix_store("t", 500, dev(a.K), dev(a.V))
+    kp.pion_prefix_store("t", 501, dev(a.K), dev(a.V), kp.PION_KV_MLX4G32)
+    Q = dev(np.stack([a.Q, a.Q]))
+    out = empty((2, 2, 1, 128))
+    with pytest.raises(k.PionError) as e:
+        kp.pion_prefix_query_layers("t", 500, Q, out)
+    assert e.value.status == k.PION_ERR_INVALID
+    with pytest.raises(k.PionError) as e:
+        kp.pion_prefix_query_layers("t", 501, Q, out)   # layer 502 absent
+    assert e.value.status == k.PION_ERR_NOT_FOUND
+    assert np.all(np.isnan(host(out)))                  # nothing written on error
