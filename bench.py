@@ -1,24 +1,29 @@
 #!/usr/bin/env python3
-"""Throughput of M=1 attention over a resident KV-cache prefix on one MI355X.
+"""Throughput of attention over a resident KV-cache prefix on one MI355X.
 
-Workload (one "step"): the decode shape H_q = H_kv = 8, N = 2048, D = 128, M = 1,
-fp16 K/V resident in 32 independent (sid, layer) slots, queried back-to-back, fp32
-out + LSE per layer - the shape the pages quote their M=1 latency on. Inputs are the
+Default workload (--config 2, one "step"): the decode shape H_q = H_kv = 8, N = 2048,
+D = 128, M = 1, fp16 K/V resident in 32 independent (sid, layer) slots, fp32 out + LSE
+per layer - the shape the pages quote their M=1 latency on. Inputs come from the
 seeded synthetic generators (K with per-channel lognormal(0, 0.5) scales, Q and V
 N(0, 1)); all of it is resident in HBM before the timed region starts.
+  --mode layers (default): a step is one pion_prefix_query_layers call covering the 32
+      layers (one kernel launch), issued eagerly.
+  --mode calls: a step is 32 pion_prefix_query calls, captured once into a HIP graph
+      (after an eager warm-up) and replayed per step (--eager: issued from the host).
 
-Timed region: K steps on one HIP stream. Default (--mode layers): a step is one
-pion_prefix_query_layers call covering the 32 layers (one kernel launch). --mode calls:
-a step is 32 pion_prefix_query calls. The step's calls are captured once into a HIP
-graph (after an eager warm-up) and the graph is replayed per step (--eager issues them
-from the host instead). Per-launch duration: after the timed region, the same calls
-are issued eagerly with a HIP event pair around each one on the launch stream; the
-roofline figure uses the algorithmic K/V bytes of one launch (per layer: 8 heads x
-2048 tokens x (K + V) x 128 x 2 B = 8,388,608 B; 268,435,456 B for the 32-layer launch)
-over the mean of those durations.
+Other workloads, one call per step (for the design notes; the default run is the one
+above): --config 1 tiny dense query; --config 3 fused batched-Q prefill (TFLOP/s);
+--config 4 mlx4g32 decode (GB/s of resident codes/scales/biases); --config 5 sparse-auto
+fused query (us/query).
 
-cpu_baseline: the fp64 numpy oracle as it stands, one thread, on whole 32-layer passes
-of the same inputs, repeated for about 10 s.
+Timing: wall clock over K steps between device synchronizations; a HIP event pair on
+the launch stream brackets the same timed region, and its elapsed time over the number
+of launches is the mean launch duration (back-to-back launches, so inter-kernel gaps
+count against the kernel). The roofline figure is the algorithmic bytes (or flops) of
+one launch over that duration.
+
+cpu_baseline: the fp64 numpy oracle as it stands, one thread, on a bounded sample of the
+same workload (about 10 s), scaled to the metric's unit.
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "prefix-attn K/V GB/s (M=1) & TFLOP/s (batched-Q), % of MI355X roofline"
 
 
 def parse():
@@ -39,34 +46,302 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="issue calls from the host, no graph")
+    ap.add_argument("--eager", action="store_true", help="calls mode: no graph")
     ap.add_argument("--mode", choices=["layers", "calls"], default="layers",
-                    help="layers: one pion_prefix_query_layers launch per step; "
-                         "calls: 32 pion_prefix_query calls per step")
+                    help="config 2: one pion_prefix_query_layers launch per step, "
+                         "or 32 pion_prefix_query calls per step")
     return ap.parse_args()
 
 
-def cpu_baseline(case, inputs, seconds):
-    import numpy as np
-    import oracle
+class Timed:
+    """Times `step` (a host function issuing ABI calls on the current stream)."""
+
+    def __init__(self, torch, stream, step, launches_per_step, use_graph):
+        self.torch, self.stream, self.step = torch, stream, step
+        self.lps = launches_per_step
+        self.graph = None
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                step()
+        torch.cuda.synchronize()
+        if use_graph:
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph, stream=stream):
+                step()
+            torch.cuda.synchronize()
+
+    def _run(self, n):
+        with self.torch.cuda.stream(self.stream):
+            for _ in range(n):
+                if self.graph is not None:
+                    self.graph.replay()
+                else:
+                    self.step()
+
+    def measure(self, steps, warmup):
+        torch = self.torch
+        self._run(warmup)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(self.stream)
+        self._run(steps)
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / steps
+        launch_us = ev0.elapsed_time(ev1) * 1e3 / (steps * self.lps)
+        return ms_per_step, launch_us
+
+
+def cpu_time(fn, seconds):
+    """Repeat fn() (one sample unit) for about `seconds` on one thread."""
     from threadpoolctl import threadpool_limits
-    passes = 0
+    n = 0
     t0 = time.perf_counter()
     with threadpool_limits(1):
         while True:
-            for inp in inputs:
-                oracle.prefix_query(inp.Q, inp.K, inp.V)
-            passes += 1
+            fn()
+            n += 1
             el = time.perf_counter() - t0
             if el >= seconds:
-                break
-    bytes_per_pass = case.layers * case.H_kv * case.N * case.D * 2 * 2
-    return {"value": round(bytes_per_pass * passes / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{passes} whole 32-layer passes of the decode workload "
-                      f"({el:.1f} s, fp64 numpy, 1 thread)"}
+                return n, el
+
+
+def check_close(got, ref, tol, what):
+    import numpy as np
+    err = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+    if not err <= tol:
+        raise SystemExit(f"bench {what} disagrees with the oracle: max-abs {err}")
+
+
+# ----------------------------------------------------------------------------- configs
+def run_decode(args, torch, kp, synth, dev, stream):
+    import numpy as np
+    import oracle
+    case = synth.DECODE
+    inputs = [synth.generate(case, l) for l in range(case.layers)]
+    sid = "bench-decode"
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store(sid, l, torch.from_numpy(inp.K).to(dev),
+                             torch.from_numpy(inp.V).to(dev))
+    Qall = torch.from_numpy(np.stack([i.Q for i in inputs])).to(dev)
+    out = torch.empty((case.layers, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((case.layers, case.H_q, 1), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    lib, sidb = kp.lib(), sid.encode()
+    if args.mode == "layers":
+        fn = lib.pion_prefix_query_layers
+        calls = [(sidb, 0, case.layers, case.H_q, case.D, 1, Qall.data_ptr(), None,
+                  out.data_ptr(), lse.data_ptr())]
+    else:
+        fn = lib.pion_prefix_query
+        calls = [(sidb, l, case.H_q, case.D, 1, Qall[l].data_ptr(), None, out[l].data_ptr(),
+                  lse[l].data_ptr()) for l in range(case.layers)]
+
+    def step():
+        h = torch.cuda.current_stream().cuda_stream
+        for c in calls:
+            rc = fn(*c, h)
+            if rc != 0:
+                raise kp.PionError(rc, fn.__name__)
+
+    graph = args.mode == "calls" and not args.eager
+    t = Timed(torch, stream, step, len(calls), graph)
+    ms, launch_us = t.measure(args.steps, args.warmup)
+    for l in (0, case.layers - 1):
+        ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
+        check_close(out[l].cpu().numpy(), ref, 2e-3, "out")
+        check_close(lse[l].cpu().numpy(), ref_lse, 1e-4, "lse")
+    bytes_layer = case.H_kv * case.N * case.D * 2 * 2
+    bytes_step = bytes_layer * case.layers
+    bytes_launch = bytes_step // len(calls)
+    cpu = None
+    if not args.no_cpu_baseline:
+        def one_pass():
+            for inp in inputs:
+                oracle.prefix_query(inp.Q, inp.K, inp.V)
+        n, el = cpu_time(one_pass, args.cpu_seconds)
+        cpu = {"value": round(bytes_step * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} whole 32-layer passes of this workload "
+                         f"({el:.1f} s, fp64 numpy, 1 thread)"}
+    kp.pion_prefix_drop(sid, -1)
+    return {
+        "value": bytes_step / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
+        "dtype": "fp16 K/V, fp32 accumulate",
+        "config": {"workload": "M=1 prefix attention, decode shape H_q=H_kv=8 N=2048 D=128, "
+                               "32 resident layers queried per step",
+                   "entry": fn.__name__, "launches_per_step": len(calls),
+                   "launch": "hip-graph replay" if graph else "eager",
+                   "bytes_per_step": bytes_step},
+        "roofline": {"bound": "hbm", "achieved": bytes_launch / (launch_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "kernel": "attn_split_kernel<128,1,4,0>",
+                     "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_prefill(args, torch, kp, synth, dev, stream):
+    import oracle
+    case = synth.PREFILL
+    inp = synth.generate(case)
+    sid = "bench-prefill"
+    kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
+                         torch.from_numpy(inp.V).to(dev))
+    Q, Ks, Vs = (torch.from_numpy(a).to(dev) for a in (inp.Q, inp.K_suf, inp.V_suf))
+    out = torch.empty((case.H_q, case.M, case.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((case.H_q, case.M), dtype=torch.float32, device=dev)
+    lib, sidb = kp.lib(), sid.encode()
+    a = (sidb, 0, case.H_q, case.D, case.M, case.S_suf, case.H_kv, Q.data_ptr(),
+         Ks.data_ptr(), Vs.data_ptr(), None, out.data_ptr(), lse.data_ptr())
+
+    def step():
+        rc = lib.pion_prefix_query_fused(*a, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise kp.PionError(rc, "pion_prefix_query_fused")
+
+    t = Timed(torch, stream, step, 1, False)
+    ms, launch_us = t.measure(args.steps, args.warmup)
+    rows = [(0, 0), (5, 511), (23, 300), (12, 100)]
+    ref, _ = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
+    o = out.cpu().numpy()
+    for h, i in rows:
+        check_close(o[h, i], ref[h, i], 2e-3, "out")
+    flops = 4 * case.H_q * case.D * (case.M * case.N + case.M * (case.M + 1) // 2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows_all = [(h, i) for h in range(case.H_q) for i in range(0, case.M, 64)]
+        k = [0]
+
+        def one_row():
+            h, i = rows_all[k[0] % len(rows_all)]
+            k[0] += 1
+            oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=[(h, i)])
+        n, el = cpu_time(one_row, args.cpu_seconds)
+        per_row = 4 * case.D * (case.N + case.S_suf / 2)
+        cpu = {"value": round(per_row * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+               "kind": "oracle", "sample": f"{n} query rows of this workload ({el:.1f} s)"}
+    kp.pion_prefix_drop(sid, -1)
+    return {
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
+        "dtype": "fp16 in, fp32 accumulate",
+        "config": {"workload": "fused batched-Q prefill H_q=24 H_kv=8 (h//3) D=128 N=4096 "
+                               "M=S_suf=512 causal suffix", "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": flops / (launch_us * 1e-6) / 1e12,
+                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None,
+                     "avg_launch_us": launch_us},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_mlx4(args, torch, kp, synth, dev, stream):
+    import oracle
+    case = synth.MLX4_DECODE
+    inp = synth.generate(case)
+    sid = "bench-mlx4"
+    kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
+                         torch.from_numpy(inp.V).to(dev), kp.PION_KV_MLX4G32)
+    Q = torch.from_numpy(inp.Q).to(dev)
+    out = torch.empty((case.H_q, 1, case.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((case.H_q, 1), dtype=torch.float32, device=dev)
+    lib, sidb = kp.lib(), sid.encode()
+    a = (sidb, 0, case.H_q, case.D, 1, Q.data_ptr(), None, out.data_ptr(), lse.data_ptr())
+
+    def step():
+        rc = lib.pion_prefix_query(*a, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise kp.PionError(rc, "pion_prefix_query")
+
+    t = Timed(torch, stream, step, 1, False)
+    ms, launch_us = t.measure(args.steps, args.warmup)
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+    ref, _ = oracle.prefix_query(inp.Q, Kh, Vh)
+    check_close(out.cpu().numpy(), ref, 2e-3, "out")
+    nbytes = case.H_kv * case.N * 160
+    kp.pion_prefix_drop(sid, -1)
+    return {
+        "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
+        "dtype": "int4 codes + fp16 scale/bias, fp32 accumulate",
+        "config": {"workload": "mlx4g32 decode H_q=24 H_kv=8 (h//3) D=128 N=32768 M=1",
+                   "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "avg_launch_us": launch_us},
+        "cpu_baseline": None,
+    }
+
+
+def run_sparse(args, torch, kp, synth, dev, stream):
+    import oracle
+    case = synth.SPARSE
+    inp = synth.generate(case)
+    sid = "bench-sparse"
+    kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
+                         torch.from_numpy(inp.V).to(dev))
+    Q, Ks, Vs = (torch.from_numpy(a).to(dev) for a in (inp.Q, inp.K_suf, inp.V_suf))
+    out = torch.empty((case.H_q, case.D), dtype=torch.float32, device=dev)
+    blocks = torch.empty((case.H_kv, case.K_top), dtype=torch.int32, device=dev)
+    lib, sidb = kp.lib(), sid.encode()
+    a = (sidb, 0, case.H_q, case.D, case.B, case.K_top, case.H_kv, case.S_suf, Q.data_ptr(),
+         Ks.data_ptr(), Vs.data_ptr(), None, out.data_ptr(), None, blocks.data_ptr())
+
+    def step():
+        rc = lib.pion_prefix_query_sparse_auto(*a, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise kp.PionError(rc, "pion_prefix_query_sparse_auto")
+
+    t = Timed(torch, stream, step, 3, False)   # block_score, block_topk, split kernel
+    ms, _ = t.measure(args.steps, args.warmup)
+    ref, _, ref_blocks = oracle.prefix_query_sparse_auto(inp.Q, inp.K, inp.V, case.B,
+                                                         case.K_top, None, inp.K_suf, inp.V_suf)
+    check_close(out.cpu().numpy(), ref, 2e-3, "out")
+    if not (blocks.cpu().numpy() == ref_blocks).all():
+        raise SystemExit("bench sparse blocks disagree with the oracle")
+    nb = case.N // case.B
+    nbytes = (case.H_kv * nb * case.D * 4 + case.K_top * case.B * case.D * 4
+              + case.S_suf * case.D * 4 + case.H_q * case.D * 6)
+    kp.pion_prefix_drop(sid, -1)
+    return {
+        "value": ms * 1e3, "unit": "us/query", "ms_per_step": ms,
+        "dtype": "fp16 K/V, fp32 accumulate",
+        "config": {"workload": "sparse-auto fused H_q=8 H_kv=1 D=256 N=65536 B=64 K_top=8 "
+                               "S_suf=64 M=1 (block means cached)", "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
+def run_tiny(args, torch, kp, synth, dev, stream):
+    import oracle
+    case = synth.TINY
+    inp = synth.generate(case)
+    kp.pion_prefix_store("bench-tiny", 0, torch.from_numpy(inp.K).to(dev),
+                         torch.from_numpy(inp.V).to(dev))
+    Q = torch.from_numpy(inp.Q).to(dev)
+    out = torch.empty((2, 1, 64), dtype=torch.float32, device=dev)
+    lib = kp.lib()
+    a = (b"bench-tiny", 0, 2, 64, 1, Q.data_ptr(), None, out.data_ptr(), None)
+
+    def step():
+        rc = lib.pion_prefix_query(*a, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise kp.PionError(rc, "pion_prefix_query")
+
+    t = Timed(torch, stream, step, 1, False)
+    ms, _ = t.measure(args.steps, args.warmup)
+    check_close(out.cpu().numpy(), oracle.prefix_query(inp.Q, inp.K, inp.V)[0], 2e-3, "out")
+    kp.pion_prefix_drop("bench-tiny", -1)
+    return {"value": ms * 1e3, "unit": "us/query", "ms_per_step": ms, "dtype": "fp16",
+            "config": {"workload": "tiny dense query H=2 N=128 D=64 M=1"},
+            "roofline": None, "cpu_baseline": None}
 
 
 def main():
@@ -75,140 +350,37 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-
-    import numpy as np
     import torch
-
     import kv_cache_prefix_amd as kp
     import synth
 
-    case = synth.DECODE
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inputs = [synth.generate(case, l) for l in range(case.layers)]
-    sid = "bench-decode"
-    Qs, outs, lses = [], [], []
-    for l, inp in enumerate(inputs):
-        K = torch.from_numpy(inp.K).to(dev)
-        V = torch.from_numpy(inp.V).to(dev)
-        kp.pion_prefix_store(sid, l, K, V)
-        Qs.append(torch.from_numpy(inp.Q).to(dev))
-        outs.append(torch.empty((case.H_q, 1, case.D), dtype=torch.float32, device=dev))
-        lses.append(torch.empty((case.H_q, 1), dtype=torch.float32, device=dev))
-    torch.cuda.synchronize()
-
-    lib = kp.lib()
-    sidb = sid.encode()
     stream = torch.cuda.Stream(device=dev)
-    # raw arguments, marshalled once
-    Qall = torch.stack(Qs).contiguous()
-    out_all = torch.empty((case.layers, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
-    lse_all = torch.empty((case.layers, case.H_q, 1), dtype=torch.float32, device=dev)
-    if args.mode == "layers":
-        fn = lib.pion_prefix_query_layers
-        calls = [(sidb, 0, case.layers, case.H_q, case.D, 1, Qall.data_ptr(), None,
-                  out_all.data_ptr(), lse_all.data_ptr())]
-        outs = list(out_all)
-        lses = list(lse_all)
-    else:
-        fn = lib.pion_prefix_query
-        calls = [(sidb, l, case.H_q, case.D, 1, Qs[l].data_ptr(), None, outs[l].data_ptr(),
-                  lses[l].data_ptr()) for l in range(case.layers)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in calls]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in calls]
-
-    def step(timed_events: bool):
-        h = torch.cuda.current_stream().cuda_stream
-        for i, c in enumerate(calls):
-            if timed_events:
-                starts[i].record()
-            rc = fn(*c, h)
-            if rc != 0:
-                raise kp.PionError(rc, fn.__name__)
-            if timed_events:
-                ends[i].record()
-
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            step(False)
-    torch.cuda.synchronize()
-
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step(False)
-        torch.cuda.synchronize()
-
-    def run(n):
-        with torch.cuda.stream(stream):
-            for _ in range(n):
-                if graph is not None:
-                    graph.replay()
-                else:
-                    step(False)
-
-    run(args.warmup)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(args.steps)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per-launch duration: the same calls issued eagerly with a HIP event pair around
-    # each one on the launch stream (the kernel runs alone between its events)
-    launch_ms = []
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, min(args.steps, 50))):
-            step(True)
-            torch.cuda.synchronize()
-            launch_ms += [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = wall * 1e3 / args.steps
-    avg_launch_us = 1e3 * float(np.mean(launch_ms))
-    bytes_per_layer = case.H_kv * case.N * case.D * 2 * 2
-    bytes_per_step = bytes_per_layer * case.layers
-    bytes_per_launch = bytes_per_step // len(calls)
-    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
-
-    # parity spot check of the last step's outputs (layer 0 and 31) against the oracle
-    import oracle
-    for l in (0, case.layers - 1):
-        ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
-        err = float(np.max(np.abs(outs[l].cpu().numpy() - ref)))
-        lerr = float(np.max(np.abs(lses[l].cpu().numpy() - ref_lse)))
-        if not (err <= 2e-3 and lerr <= 1e-4):
-            raise SystemExit(f"bench outputs disagree with the oracle: {err} {lerr}")
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline(case, inputs, args.cpu_seconds)
-    kp.pion_prefix_drop(sid, -1)
-
+    runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse}[args.config]
+    r = runner(args, torch, kp, synth, dev, stream)
+    roof = r["roofline"]
+    if roof is not None:
+        roof["achieved"] = round(roof["achieved"], 2)
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        if "avg_launch_us" in roof:
+            roof["avg_launch_us"] = round(roof["avg_launch_us"], 3)
     line = {
-        "metric": "prefix-attn K/V GB/s (M=1) & TFLOP/s (batched-Q), % of MI355X roofline",
-        "value": round(value, 2),
-        "unit": "GB/s",
+        "metric": METRIC,
+        "value": round(r["value"], 3),
+        "unit": r["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": r["unit"] != "us/query",
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 K/V, fp32 accumulate",
-        "data": "synthetic (seeded numpy: K N(0,1) x lognormal(0,0.5) per channel, Q/V N(0,1))",
-        "config": {"workload": "M=1 prefix attention, decode shape H_q=H_kv=8 N=2048 D=128, "
-                               "32 resident layers queried back-to-back per step",
-                   "entry": fn.__name__,
-                   "launches_per_step": len(calls),
-                   "launch": "eager" if graph is None else "hip-graph replay",
-                   "bytes_per_step": bytes_per_step},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "attn_split_kernel<128,1,4,0> (split-KV decode + in-kernel merge)",
-                     "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": round(avg_launch_us, 3)},
-        "cpu_baseline": cpu,
+        "dtype": r["dtype"],
+        "data": "synthetic (seeded numpy generators; see synth/)",
+        "config": r["config"],
+        "roofline": roof,
+        "cpu_baseline": r["cpu_baseline"],
     }
     print(json.dumps(line), flush=True)
 

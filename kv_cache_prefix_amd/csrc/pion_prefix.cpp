@@ -93,11 +93,14 @@ size_t max_slots() {
   return v;
 }
 
+// Workgroups a launch aims for when it splits keys: one per CU of the MI355X (256 CUs).
+// More, shorter spans add merge work without adding bandwidth (measured on the 32-layer
+// decode launch). Env PION_SPLIT_TARGET overrides it for tuning.
 int split_target() {
   static int v = [] {
     const char *e = getenv("PION_SPLIT_TARGET");
-    int x = e ? atoi(e) : 512;
-    return x > 0 ? x : 512;
+    int x = e ? atoi(e) : 256;
+    return x > 0 ? x : 256;
   }();
   return v;
 }
