@@ -136,6 +136,27 @@ struct HeadMap {
 // (it skips prefix spans of an mlx4g32 slot).
 hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_count,
                           bool mlx4_prefix, hipStream_t s);
+// Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
+// causal suffix (bottom-right aligned). Workgroup (x, y): x = (q-head, block of 128
+// query rows), y = key split of split_keys tokens over the concatenated key index
+// [0, N + S_suf). With n_splits > 1 the splits' partials (same layout as PartialParams,
+// S_max = n_splits) merge in the last-arriving workgroup of each x (counters[x]).
+struct PrefillParams {
+  const uint16_t *Q;              // fp16 [H_q, M, D]
+  const uint16_t *K, *V;          // fp16 [H_kv, N, D]
+  const uint16_t *Ksuf, *Vsuf;    // fp16 [H_kv, S_suf, D] or null
+  int H_q, M, D, H_kv, N, S_suf;
+  float qscale;                   // log2(e) / sqrt(D)
+  int n_iblk;                     // ceil(M / 128)
+  int n_splits, split_keys;       // split_keys a multiple of 64
+  float *out, *lse;
+  float *part_acc, *part_m, *part_l;
+  int *counters;
+  HeadMap hm;
+};
+
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
+
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);
 

@@ -105,6 +105,11 @@ int split_target() {
   return v;
 }
 
+bool getenv_flag(const char *name) {
+  const char *e = getenv(name);
+  return e && e[0] && e[0] != '0';
+}
+
 // Memory that a kernel may read or write: device (or managed) allocations only.
 bool on_device(const void *p) {
   if (!p) return false;
@@ -245,9 +250,61 @@ struct AttnCall {
   size_t out_stride, lse_stride;
 };
 
+// Query rows at or above which an fp16 query runs on the MFMA kernel.
+constexpr int kMfmaMinRows = 32;
+
+// Batched-Q on the MFMA kernel: one fp16 slot, no block list. Splits the key range so
+// that row blocks x splits gives about two workgroups per CU.
+int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
+  PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.Q = c.Q;
+  p.K = sl.view.K;
+  p.V = sl.view.V;
+  p.Ksuf = c.S_suf > 0 ? c.Ksuf : nullptr;
+  p.Vsuf = c.S_suf > 0 ? c.Vsuf : nullptr;
+  p.H_q = c.H_q;
+  p.M = c.M;
+  p.D = c.D;
+  p.H_kv = sl.H;
+  p.N = sl.N;
+  p.S_suf = c.S_suf;
+  p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
+  p.n_iblk = (c.M + 127) / 128;
+  const long long tiles = (long long)c.H_q * p.n_iblk;
+  if (tiles > kMaxCounters) return PION_ERR_UNSUPPORTED;
+  const long long total = (long long)sl.N + c.S_suf;
+  long long ns = std::max<long long>(1, (2LL * 256 + tiles / 2) / tiles);
+  ns = std::min<long long>(ns, std::min<long long>(16, (total + 63) / 64));
+  long long sk = (total + ns - 1) / ns;
+  sk = (sk + 63) / 64 * 64;
+  if (sk > (1LL << 30)) return PION_ERR_UNSUPPORTED;
+  p.split_keys = (int)sk;
+  p.n_splits = (int)((total + sk - 1) / sk);
+  p.out = c.out;
+  p.lse = c.lse;
+  p.hm.H_q = c.H_q;
+  for (int h = 0; h < c.H_q; ++h) p.hm.m[h] = (uint8_t)(*c.hm)[h];
+  if (p.n_splits > 1) {
+    const size_t rows = (size_t)c.H_q * c.M;
+    const size_t acc_bytes = align256(rows * p.n_splits * c.D * sizeof(float));
+    const size_t ml_bytes = align256(rows * p.n_splits * sizeof(float));
+    void *ws = nullptr;
+    if (get_ws(st, acc_bytes + 2 * ml_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
+    p.part_acc = (float *)ws;
+    p.part_m = (float *)((char *)ws + acc_bytes);
+    p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
+    p.counters = g_ws[st].counters;
+  }
+  return launch_prefill(p, st) == hipSuccess ? PION_OK : PION_ERR_HIP;
+}
+
 // One launch (two for an mlx4g32 prefix with an fp16 suffix) over `slots`, which share
 // H, D and format.
 int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hipStream_t st) {
+  if (slots.size() == 1 && slots[0]->fmt == PION_KV_FP16 && !c.blocks && c.M >= kMfmaMinRows &&
+      !getenv_flag("PION_NO_MFMA"))
+    return run_prefill(*slots[0], c, st);
   static PartialParams p;  // large; the library lock serializes callers
   memset(&p, 0, sizeof(p));
   const int n_prob = (int)slots.size();

@@ -402,3 +402,48 @@ def test_query_layers_rejects_mixed_slots(kp):
         kp.pion_prefix_query_layers("t", 501, Q, out)   # layer 502 absent
     assert e.value.status == k.PION_ERR_NOT_FOUND
     assert np.all(np.isnan(host(out)))                  # nothing written on error
+
+
+# ------------------------------------------------------------------ MFMA batched-Q path
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("N,M,S_suf", [(300, 40, 40), (1000, 130, 200), (64, 32, 0), (777, 257, 0)])
+def test_mfma_prefill_shapes(kp, D, N, M, S_suf):
+    inp = synth.generate(synth.PREFILL, 11, N=N, M=M, S_suf=S_suf, H_q=6, H_kv=2, D=D)
+    kp.pion_prefix_store("t", 600, dev(inp.K), dev(inp.V))
+    out, lse = empty((6, M, D)), empty((6, M))
+    if S_suf:
+        kp.pion_prefix_query_fused("t", 600, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    else:
+        kp.pion_prefix_query("t", 600, dev(inp.Q), out, lse)
+    out, lse = host(out), host(lse)
+    rng = np.random.default_rng(N + M)
+    rows = [(h, i) for h in range(6) for i in (0, M - 1)] + \
+        [(int(h), int(i)) for h, i in zip(rng.integers(0, 6, 30), rng.integers(0, M, 30))]
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
+    check(out, lse, ref, ref_lse, rows=rows)
+    assert np.all(np.isfinite(out))
+
+
+def test_mfma_prefill_arbitrary_head_map_all_rows(kp):
+    inp = synth.generate(synth.PREFILL, 12, N=200, M=48, S_suf=50, H_q=5, H_kv=3)
+    hm = synth.random_head_map(5, 3, 7)
+    kp.pion_prefix_store("t", 601, dev(inp.K), dev(inp.V))
+    out, lse = empty((5, 48, 128)), empty((5, 48))
+    kp.pion_prefix_query_fused("t", 601, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse,
+                               head_map=hm)
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf,
+                                                           inp.V_suf, hm))
+
+
+def test_mfma_and_valu_paths_agree(kp, monkeypatch):
+    inp = synth.generate(synth.PREFILL, 13, N=500, M=64, S_suf=64, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 602, dev(inp.K), dev(inp.V))
+    outs = []
+    for flag in ("0", "1"):
+        monkeypatch.setenv("PION_NO_MFMA", flag)
+        out, lse = empty((6, 64, 128)), empty((6, 64))
+        kp.pion_prefix_query_fused("t", 602, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+        outs.append((host(out), host(lse)))
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+    for o, l in outs:
+        check(o, l, ref, ref_lse)
