@@ -274,7 +274,10 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   const long long tiles = (long long)c.H_q * p.n_iblk;
   if (tiles > kMaxCounters) return PION_ERR_UNSUPPORTED;
   const long long total = (long long)sl.N + c.S_suf;
-  long long ns = std::max<long long>(1, (2LL * 256 + tiles / 2) / tiles);
+  // splits: as many as fit one workgroup per CU next to the other row blocks (each
+  // split adds a partial round trip and merge work); env PION_PREFILL_SPLITS overrides
+  long long ns = std::max<long long>(1, 256 / tiles);
+  if (const char *e = getenv("PION_PREFILL_SPLITS")) ns = std::max(1, atoi(e));
   ns = std::min<long long>(ns, std::min<long long>(16, (total + 63) / 64));
   long long sk = (total + ns - 1) / ns;
   sk = (sk + 63) / 64 * 64;

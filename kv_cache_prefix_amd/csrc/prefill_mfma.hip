@@ -9,7 +9,9 @@
 //                 (LDS, row-major), B = Q^T (registers, loaded once); the result lane l
 //                 holds 16 keys x 1 query (query l % 32).
 //   online softmax in fp32 (log2 units, scale folded into the exponent; the row sum
-//                 uses the fp32 weights, the PV product their fp16 roundings); a lane's p
+//                 uses the fp32 weights, the PV product their fp16 roundings; the
+//                 accumulators are rescaled only when a row max grows by more than
+//                 2^8, and only boundary tiles are masked); a lane's p
 //                 values are already the B operand of the next product: result element
 //                 (i, j) of the S^T block is key 8i + 4(l/32) + j, and a 16-key k-step of
 //                 the PV product takes elements i = 2s, 2s+1 as its eight k slots.
@@ -28,6 +30,11 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Note: the result of __builtin_amdgcn_raw_buffer_load_b128 is reinterpreted as a whole
+// vector (bit_cast to f32x4); bit-casting its elements one by one makes this compiler
+// narrow the load to a single dword.
 
 constexpr float kNegBig = -1.0e30f;
 constexpr int BQ = 128;   // query rows per workgroup
@@ -36,21 +43,41 @@ constexpr int kMaxPrefillSplits = 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ void st_agent(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int D>
 struct PrefillSmem {
   static constexpr int KST = D + 8;   // K tile row stride (halves)
   static constexpr int VST = BK + 4;  // V^T row stride (halves)
-  _Float16 k[BK * KST];
-  _Float16 vt[D * VST];
+  union {
+    struct {
+      alignas(16) _Float16 k[BK * KST];
+      alignas(16) _Float16 vt[D * VST];
+    };
+    struct {                      // split merge: per (row, split) m then weight, and l
+      float w[BQ * 16];
+      float l[BQ * 16];
+      float inv[BQ];
+    } mg;
+  };
   int last;
 };
+
+// A row max may grow by this much (log2 units, a factor 2^8) before the accumulators
+// are rescaled: weights up to 2^8 stay exact enough in fp16 and the fp32 sums cannot
+// overflow, and after the first tiles a rescale is rare.
+constexpr float kRescaleSlack = 8.0f;
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zero, which
+// masks the tails of the prefix and suffix without branches. 0x00020000 is the raw
+// 32-bit data format of the descriptor's last word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
@@ -60,6 +87,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   constexpr int CH = D / 8;                   // 16-byte chunks per key row
   constexpr int KITEMS = BK * CH / 256;       // K chunks per thread per tile
   constexpr int VITEMS = (BK / 2) * CH / 256; // V (key-pair, chunk) items per thread
+  constexpr uint32_t ROWB = D * 2;            // bytes per key row
   __shared__ PrefillSmem<D> sm;
 
   const int tile = blockIdx.x, split = blockIdx.y;
@@ -77,10 +105,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   const int k_stop = min(k_end, lim_wg);
   const int lim_row = p.S_suf > 0 ? p.N + p.S_suf - p.M + qi_c + 1 : p.N;
   const int row_end = min(k_end, lim_row);
+  // 32-key sub-tiles ending at or below this need no mask for any row of the workgroup
+  const int lim_first = p.S_suf > 0 ? p.N + p.S_suf - p.M + i0 + 1 : p.N;
+  const int full_end = min(k_end, lim_first);
 
-  const uint16_t *Kp = p.K + (size_t)g * p.N * D, *Vp = p.V + (size_t)g * p.N * D;
-  const uint16_t *Ksp = p.Ksuf ? p.Ksuf + (size_t)g * p.S_suf * D : nullptr;
-  const uint16_t *Vsp = p.Vsuf ? p.Vsuf + (size_t)g * p.S_suf * D : nullptr;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.K + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.V + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
+  const bool has_suf = p.S_suf > 0;  // a null suffix gets an empty range
+  const __amdgpu_buffer_rsrc_t rKs =
+      make_rsrc(has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : p.K, (uint32_t)p.S_suf * ROWB);
+  const __amdgpu_buffer_rsrc_t rVs =
+      make_rsrc(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWB);
 
   half8 qb[NDS];
   {
@@ -96,23 +131,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   float m_run = kNegBig, l_run = 0.f;
 
   uint4 kreg[KITEMS], vreg[VITEMS][2];
-  auto row_ptr = [&](const uint16_t *pre, const uint16_t *suf, int k) -> const uint16_t * {
-    return k < p.N ? pre + (size_t)k * D : suf + (size_t)(k - p.N) * D;
-  };
-  auto gload = [&](int t0) {
+  // Tiles never straddle the prefix / suffix boundary: the split's prefix part
+  // [k_begin, pre_end) is tiled from k_begin, its suffix part [suf_beg, k_stop) from
+  // suf_beg. Tile j < n_pre is prefix, the rest suffix.
+  const int pre_end = min(k_stop, p.N);
+  const int suf_beg = max(k_begin, p.N);
+  const int n_pre = k_begin < pre_end ? (pre_end - k_begin + BK - 1) / BK : 0;
+  const int n_suf = suf_beg < k_stop ? (k_stop - suf_beg + BK - 1) / BK : 0;
+  auto gload = [&](int j) {
+    const bool suf = j >= n_pre;  // workgroup-uniform
+    const int r0 = suf ? suf_beg - p.N + (j - n_pre) * BK : k_begin + j * BK;  // source row
+    const __amdgpu_buffer_rsrc_t rk = suf ? rKs : rK, rv = suf ? rVs : rV;
 #pragma unroll
     for (int it = 0; it < KITEMS; ++it) {
       const int item = tid + 256 * it, key = item / CH, ch = item - key * CH;
-      const int k = t0 + key;
-      kreg[it] = k < total ? *(const uint4 *)(row_ptr(Kp, Ksp, k) + ch * 8) : make_uint4(0, 0, 0, 0);
+      kreg[it] = bload(rk, (uint32_t)(r0 + key) * ROWB + ch * 16);
     }
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
       const int item = tid + 256 * it, kp = item & 31, ch = item >> 5;
-      const int k = t0 + 2 * kp;
-      vreg[it][0] = k < total ? *(const uint4 *)(row_ptr(Vp, Vsp, k) + ch * 8) : make_uint4(0, 0, 0, 0);
-      vreg[it][1] = k + 1 < total ? *(const uint4 *)(row_ptr(Vp, Vsp, k + 1) + ch * 8)
-                                  : make_uint4(0, 0, 0, 0);
+      vreg[it][0] = bload(rv, (uint32_t)(r0 + 2 * kp) * ROWB + ch * 16);
+      vreg[it][1] = bload(rv, (uint32_t)(r0 + 2 * kp + 1) * ROWB + ch * 16);
     }
   };
   auto swrite = [&]() {
@@ -136,64 +175,72 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  int t0 = k_begin;
-  if (t0 < k_stop) gload(t0);
-  for (; t0 < k_stop; t0 += BK) {
+  const int n_tiles = n_pre + n_suf;
+  if (n_tiles > 0) gload(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    const bool suf = j >= n_pre;
+    const int t0 = suf ? suf_beg + (j - n_pre) * BK : k_begin + j * BK;  // concatenated index
+    const int seg_end = suf ? k_stop : pre_end;   // keys at or past this are not in the tile
+    const int lane_end = suf ? row_end : pre_end; // this row's limit inside the tile
+    const int clean_end = suf ? min(k_stop, full_end) : pre_end;  // no mask below this
     __syncthreads();  // the previous tile's operand reads are done
     swrite();
     __syncthreads();
-    if (t0 + BK < k_stop) gload(t0 + BK);
+    if (j + 1 < n_tiles) gload(j + 1);
 
-    f16v s[2];
+    // two 32-key sub-tiles: S^T, softmax, PV
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const int kt = t0 + 32 * kb;
+      if (kt >= seg_end) break;  // workgroup-uniform
+      f16v s;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const half8 a = *(const half8 *)&sm.k[(32 * kb + col) * KST + 16 * ds + 8 * hl];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[ds], s[kb], 0, 0, 0);
+        const uint4 araw = *(const uint4 *)&sm.k[(32 * kb + col) * KST + 16 * ds + 8 * hl];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, araw), qb[ds], s,
+                                                   0, 0, 0);
       }
-    }
-    float mt = kNegBig;
+      if (kt + 32 > clean_end) {  // boundary sub-tile: mask keys past this row's limit
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int jj = 0; jj < 4; ++jj)
+            if (kt + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
+      }
+      float mt = -INFINITY;  // raw-score max; the scale is positive
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = t0 + 32 * kb + 8 * i + 4 * hl + j;
-          const float v = key < row_end ? s[kb][4 * i + j] * p.qscale : -INFINITY;
-          s[kb][4 * i + j] = v;
-          mt = fmaxf(mt, v);
-        }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.qscale;
+      const bool grow = mt > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rare after the first tiles
+        const float m_new = grow ? mt : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      }
       half8 pb[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pf = fast_exp2(s[kb][e] - m_new);  // masked: 0
-        l_run += pf;                                    // row sum from the fp32 weights
-        pb[e >> 3][e & 7] = (_Float16)pf;
+        const float pf = fast_exp2(__builtin_fmaf(s[e], p.qscale, -m_run));  // masked: 0
+        l_run += pf;                       // row sum from the fp32 weights
+        pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const _Float16 *vrow = &sm.vt[(32 * db + col) * VST + 32 * kb + 16 * s2 + 4 * hl];
-          const half4 lo = *(const half4 *)vrow;
-          const half4 hi = *(const half4 *)(vrow + 8);
-          const half8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[s2], o[db], 0, 0, 0);
+          const uint2 lo = *(const uint2 *)vrow;
+          const uint2 hi = *(const uint2 *)(vrow + 8);
+          const uint4 araw = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, araw), pb[s2],
+                                                         o[db], 0, 0, 0);
         }
       }
     }
@@ -218,19 +265,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     return;
   }
 
-  // split partial: acc unnormalized against m_run, in the split-KV layout
-  if (row_ok) {
-    const size_t o_idx = row * p.n_splits + split;
+  // Split partial (acc unnormalized against m_run; m and l in log2 units) in the
+  // split-KV layout [row][split][D], written with agent-coherent (sc1) 16-byte stores
+  // through a buffer range that covers only this block's valid rows.
+  const int S = p.n_splits;
+  const int rows_valid = min(BQ, p.M - i0);
+  const size_t row0 = (size_t)h * p.M + i0;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(p.part_acc + row0 * S * D, (uint32_t)(rows_valid * S * D * 4));
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
+  constexpr int SC1 = 16;  // cache policy: system coherent
+  {
+    const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          st_agent(p.part_acc + o_idx * D + 32 * db + 8 * i + 4 * hl + j, o[db][4 * i + j]);
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, v), rA,
+            (int)(((r * S + split) * D + 32 * db + 8 * i + 4 * hl) * 4), 0, SC1);
+      }
     if (hl == 0) {
-      st_agent(p.part_m + o_idx, l_run > 0.f ? m_run : -INFINITY);
-      st_agent(p.part_l + o_idx, l_run);
+      const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM,
+                                            (r * S + split) * 4, 0, SC1);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL,
+                                            (r * S + split) * 4, 0, SC1);
     }
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -238,36 +300,63 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   if (tid == 0) {
     const int t = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = (t == p.n_splits - 1);
+    sm.last = (t == S - 1);
   }
   __syncthreads();
   if (!sm.last) return;
-  // merge: thread t handles dim t % D of rows t / D, t / D + 256 / D, ...
-  constexpr int RPP = 256 / D;  // rows per pass
-  const int d = tid % D;
-  for (int r = tid / D; r < BQ; r += RPP) {
-    const int i = i0 + r;
-    if (i >= p.M) break;
-    const size_t rw = (size_t)h * p.M + i;
-    float mc[kMaxPrefillSplits], lc[kMaxPrefillSplits], ac[kMaxPrefillSplits];
-    float M = kNegBig;
-#pragma unroll
-    for (int c = 0; c < kMaxPrefillSplits; ++c) {
-      const bool in = c < p.n_splits;
-      mc[c] = in ? ld_agent(p.part_m + rw * p.n_splits + c) : -INFINITY;
-      lc[c] = in ? ld_agent(p.part_l + rw * p.n_splits + c) : 0.f;
-      ac[c] = in ? ld_agent(p.part_acc + (rw * p.n_splits + c) * D + d) : 0.f;
-      M = fmaxf(M, mc[c]);
+
+  // Merge, in three phases with every load of a phase in flight together:
+  // (1) m and l of all (row, split) into LDS; (2) per row the weights 2^(m_c - m*) and
+  // 1 / sum_c w_c l_c, and lse; (3) out = sum_c w_c acc_c / L in 16-byte pieces.
+  for (int x = tid; x < rows_valid * S; x += 256) {
+    sm.mg.w[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, x * 4, 0, SC1));
+    sm.mg.l[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, x * 4, 0, SC1));
+  }
+  __syncthreads();
+  if (tid < rows_valid) {
+    float M = -INFINITY;
+    for (int c = 0; c < S; ++c) M = fmaxf(M, sm.mg.w[tid * S + c]);
+    float L = 0.f;
+    for (int c = 0; c < S; ++c) {
+      const float w = fast_exp2(sm.mg.w[tid * S + c] - M);  // -inf -> 0
+      sm.mg.w[tid * S + c] = w;
+      L = __builtin_fmaf(w, sm.mg.l[tid * S + c], L);
     }
-    float L = 0.f, A = 0.f;
+    sm.mg.inv[tid] = 1.f / L;
+    if (p.lse) p.lse[row0 + tid] = (M + __log2f(L)) * 0.69314718055994530942f;
+  }
+  __syncthreads();
+  constexpr int Q4 = D / 4;                  // 16-byte pieces per row
+  constexpr int ITER = BQ * Q4 / 256;        // pieces per thread
+  float4 acc[ITER];
 #pragma unroll
-    for (int c = 0; c < kMaxPrefillSplits; ++c) {
-      const float w = fast_exp2(mc[c] - M);
-      L = __builtin_fmaf(w, lc[c], L);
-      A = __builtin_fmaf(w, ac[c], A);
+  for (int it = 0; it < ITER; ++it) acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < S; ++c) {
+    f32x4 v[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
+      v[it] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, ((r * S + c) * D + 4 * d4) * 4, 0, SC1));
     }
-    p.out[rw * D + d] = A / L;
-    if (d == 0 && p.lse) p.lse[rw] = (M + __log2f(L)) * 0.69314718055994530942f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int q = tid + 256 * it, r = q / Q4;
+      const float w = r < rows_valid ? sm.mg.w[r * S + c] : 0.f;
+      acc[it].x = __builtin_fmaf(w, v[it].x, acc[it].x);
+      acc[it].y = __builtin_fmaf(w, v[it].y, acc[it].y);
+      acc[it].z = __builtin_fmaf(w, v[it].z, acc[it].z);
+      acc[it].w = __builtin_fmaf(w, v[it].w, acc[it].w);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
+    if (r < rows_valid) {
+      const float inv = sm.mg.inv[r];
+      *(float4 *)(p.out + (row0 + r) * D + 4 * d4) =
+          make_float4(acc[it].x * inv, acc[it].y * inv, acc[it].z * inv, acc[it].w * inv);
+    }
   }
   if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
