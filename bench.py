@@ -37,6 +37,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the decode kernel in --mode layers, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE counter passes scaled by the same counters on a plain 256 MiB copy
+# (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
+# taken on (sha256 of attn_partial.hip + kernels.h); any other source reports null.
+DECODE_TRAFFIC = {"sources_sha256": "d72be12ad2ee26be5621fb37f1f5a4032775b90c56299bc79dc2ca22c4b5a5cc",
+                  "bytes_per_launch": 269102239}
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_partial.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "kv_cache_prefix_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "prefix-attn K/V GB/s (M=1) & TFLOP/s (batched-Q), % of MI355X roofline"
 
@@ -50,6 +66,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="calls mode: no graph")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (a known-size "
+                         "reference for the HBM byte counters) and exit")
     ap.add_argument("--mode", choices=["layers", "calls"], default="layers",
                     help="config 2: one pion_prefix_query_layers launch per step, "
                          "or 32 pion_prefix_query calls per step")
@@ -180,7 +199,11 @@ def run_decode(args, torch, kp, synth, dev, stream):
                    "launch": "hip-graph replay" if graph else "eager",
                    "bytes_per_step": bytes_step},
         "roofline": {"bound": "hbm", "achieved": bytes_launch / (launch_us * 1e-6) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "traffic": (DECODE_TRAFFIC["bytes_per_launch"]
+                                 if args.mode == "layers"
+                                 and kernel_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]
+                                 else None),
                      "kernel": "attn_split_kernel<128,1,4,0>",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
         "cpu_baseline": cpu,
@@ -351,6 +374,14 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_bytes > 0:
+        x = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "copies": 5}), flush=True)
+        return
     import kv_cache_prefix_amd as kp
     import synth
 
