@@ -204,7 +204,7 @@ def run_decode(args, torch, kp, synth, dev, stream):
                                  if args.mode == "layers"
                                  and kernel_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]
                                  else None),
-                     "kernel": "attn_split_kernel<128,1,4,0>",
+                     "kernel": "attn_split_kernel<128,1,4>",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
         "cpu_baseline": cpu,
     }

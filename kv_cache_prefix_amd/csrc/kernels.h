@@ -26,9 +26,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Byte offsets of the arrays inside one slot allocation; host (store) and device
 // (query) both derive pointers from this. fp16: K, V [H, N, D]. mlx4g32: K codes
-// [H, N, D/8] u32, K scales, K biases [H, N, D/32] fp16, then the same three for V.
+// [H, N, D/8] u32, K scale/bias pairs [H, N, D/32] u32 (fp16 scale in the low half,
+// fp16 bias in the high half), then the same two for V. A lane that owns one group of
+// one token reads its 16 code bytes and its 4-byte pair with two loads.
 struct SlotLayout {
-  size_t off[6];
+  size_t off[4];
   size_t bytes;
 };
 
@@ -39,18 +41,16 @@ __host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int N, int D) 
     const size_t b = (elems * 2 + 255) & ~(size_t)255;
     L.off[0] = 0;
     L.off[1] = b;
-    L.off[2] = L.off[3] = L.off[4] = L.off[5] = 0;
+    L.off[2] = L.off[3] = 0;
     L.bytes = 2 * b;
   } else {
-    const size_t cb = (elems / 2 + 255) & ~(size_t)255;
-    const size_t sb = (elems / 16 + 255) & ~(size_t)255;
+    const size_t cb = (elems / 2 + 255) & ~(size_t)255;   // codes: 4 bits per element
+    const size_t sb = (elems / 8 + 255) & ~(size_t)255;   // pairs: 4 bytes per 32 elements
     L.off[0] = 0;
     L.off[1] = cb;
     L.off[2] = cb + sb;
-    L.off[3] = cb + 2 * sb;
-    L.off[4] = 2 * cb + 2 * sb;
-    L.off[5] = 2 * cb + 3 * sb;
-    L.bytes = 2 * cb + 4 * sb;
+    L.off[3] = 2 * cb + sb;
+    L.bytes = 2 * cb + 2 * sb;
   }
   return L;
 }
@@ -61,7 +61,7 @@ struct KVView {
   int H, N, D;
   const uint16_t *K, *V;                 // fp16 [H, N, D]
   const uint32_t *Kc, *Vc;               // mlx4g32 codes [H, N, D/8]
-  const uint16_t *Ks, *Kb, *Vs, *Vb;     // mlx4g32 scales / biases [H, N, D/32]
+  const uint32_t *Ksb, *Vsb;             // mlx4g32 (scale | bias << 16) [H, N, D/32]
 };
 
 __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, int N, int D) {
@@ -74,17 +74,15 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
   v.D = D;
   v.K = v.V = nullptr;
   v.Kc = v.Vc = nullptr;
-  v.Ks = v.Kb = v.Vs = v.Vb = nullptr;
+  v.Ksb = v.Vsb = nullptr;
   if (fmt == 0) {
     v.K = (const uint16_t *)(b + L.off[0]);
     v.V = (const uint16_t *)(b + L.off[1]);
   } else {
     v.Kc = (const uint32_t *)(b + L.off[0]);
-    v.Ks = (const uint16_t *)(b + L.off[1]);
-    v.Kb = (const uint16_t *)(b + L.off[2]);
-    v.Vc = (const uint32_t *)(b + L.off[3]);
-    v.Vs = (const uint16_t *)(b + L.off[4]);
-    v.Vb = (const uint16_t *)(b + L.off[5]);
+    v.Ksb = (const uint32_t *)(b + L.off[1]);
+    v.Vc = (const uint32_t *)(b + L.off[2]);
+    v.Vsb = (const uint32_t *)(b + L.off[3]);
   }
   return v;
 }
@@ -96,9 +94,11 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
 // `blocks` one selected block each); spans [pre_splits, pre_splits + suf_splits)
 // cover the fp16 suffix in chunks of suf_chunk tokens, clipped to the causal limit.
 // Partials (acc unnormalized against m; m and l in log2 units) of problem z go to
-// part_acc + z*part_stride as [H_q*M][S_max][D] and part_m / part_l + z*ml_stride as
-// [H_q*M][S_max]; the last workgroup of each (z, y) (ticket on counters[z*y_groups+y],
-// which start at zero and are left at zero) merges them into out and lse.
+// part_acc + z*part_stride as [M][H_q][S_max][D] and part_m / part_l + z*ml_stride as
+// [M][H_q][S_max] (query index outermost, so the rows of one query index lie within
+// H_q*S_max*D*4 bytes); the last workgroup of each (z, y) (ticket on
+// counters[z*y_groups+y], which start at zero and are left at zero) merges them into
+// out and lse.
 struct PartialParams {
   int H_q, M, D, H_kv, fmt;
   float qscale;           // log2(e) / sqrt(D)
@@ -131,11 +131,14 @@ struct HeadMap {
   uint8_t m[kMaxHeads];
 };
 
-// Launches spans [x_begin, x_begin + x_count) of every problem. mlx4_prefix selects the
-// kernel that reads an mlx4g32 prefix (it skips suffix spans); otherwise the fp16 kernel
-// (it skips prefix spans of an mlx4g32 slot).
-hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_count,
-                          bool mlx4_prefix, hipStream_t s);
+// Launch spans [x_begin, x_begin + x_count) of every problem. launch_partial runs the
+// fp16 kernel (prefix spans of an fp16 slot, suffix spans; it skips prefix spans of an
+// mlx4g32 slot); launch_partial_mlx4 the mlx4g32-prefix kernel (it skips suffix spans,
+// and takes rows_per_group <= kMlx4Rows).
+constexpr int kMlx4Rows = 4;
+hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_count, hipStream_t s);
+hipError_t launch_partial_mlx4(const PartialParams &p, int rows_per_group, int x_count,
+                               hipStream_t s);
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
 // causal suffix (bottom-right aligned). Workgroup (x, y): x = (q-head, block of 128
 // query rows), y = key split of split_keys tokens over the concatenated key index
@@ -160,8 +163,12 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);
 
+// Encode rows x [rows, D] (fp16) as mlx4g32: codes [rows, D/8] u32; the scale and bias
+// of group i go to scales[i * sb_stride] and biases[i * sb_stride] (sb_stride 1 for
+// separate arrays, 2 for interleaved (scale, bias) pairs).
 hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint32_t *codes,
-                                   uint16_t *scales, uint16_t *biases, hipStream_t s);
+                                   uint16_t *scales, uint16_t *biases, int sb_stride,
+                                   hipStream_t s);
 
 // Block means of K (fp32 [H, nb, D]) for blocks of B tokens.
 hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t s);

@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
                                                                int64_t nwords,
                                                                uint32_t *__restrict__ codes,
                                                                uint16_t *__restrict__ scales,
-                                                               uint16_t *__restrict__ biases) {
+                                                               uint16_t *__restrict__ biases,
+                                                               int sb_stride) {
 #pragma clang fp contract(off)
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool valid = t < nwords;
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
   if (valid) {
     codes[t] = word;
     if ((t & 3) == 0) {
-      scales[t >> 2] = __builtin_bit_cast(uint16_t, s16);
-      biases[t >> 2] = __builtin_bit_cast(uint16_t, b16);
+      scales[(t >> 2) * sb_stride] = __builtin_bit_cast(uint16_t, s16);
+      biases[(t >> 2) * sb_stride] = __builtin_bit_cast(uint16_t, b16);
     }
   }
 }
@@ -76,13 +77,15 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
 }  // namespace
 
 hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint32_t *codes,
-                                   uint16_t *scales, uint16_t *biases, hipStream_t s) {
+                                   uint16_t *scales, uint16_t *biases, int sb_stride,
+                                   hipStream_t s) {
   const int64_t nwords = rows * (D / 8);
   if (nwords <= 0) return hipSuccess;
+  if (sb_stride != 1 && sb_stride != 2) return hipErrorInvalidValue;
   const int64_t blocks = (nwords + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quantize_mlx4g32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x,
-                     nwords, codes, scales, biases);
+                     nwords, codes, scales, biases, sb_stride);
   return hipGetLastError();
 }
 

@@ -5,11 +5,12 @@
 // Slot table: one entry per (sid, layer) as the ATTEND.PREFIX.STORE wire form keys it
 // ("Shared KV Cache Serving", Stage 2 wire forms). Each entry owns one device
 // allocation holding the resident K/V in the store layout [H, N, D] (fp16), or the
-// mlx4g32 planar arrays (codes [H, N, D/8], scales and biases [H, N, D/32], per side),
+// mlx4g32 arrays (codes [H, N, D/8] and (scale, bias) pairs [H, N, D/32], per side),
 // plus the per-B block-mean cache of the sparse-auto query.
 //
-// Launch plan of an attention call: one split-KV kernel over workgroups (key span,
-// q-head group sharing one kv-head, query index); each writes (acc, m, l) per (row,
+// Launch plan of an attention call: one split-KV kernel (fp16 or mlx4g32 prefix; an
+// mlx4g32 prefix with an fp16 suffix takes one launch of each) over workgroups (key
+// span, q-head group sharing one kv-head, query index); each writes (acc, m, l) per (row,
 // span) into a per-stream workspace, and the last workgroup of each row group merges
 // them into out and lse. The sparse-auto call runs block_mean (first use per slot and B),
 // block_score and block_topk first, and the split-KV kernel reads the picked block
@@ -204,15 +205,16 @@ bool resolve_map(const int32_t *head_map, int H_q, int H_kv, std::vector<int> &h
   return true;
 }
 
-// Group the q-heads of each kv-head into chunks of at most kRowsPerGroup.
-int build_groups(const std::vector<int> &hm, int H_kv, RowGroups &rg) {
+// Group the q-heads of each kv-head into chunks of at most `cap` (<= kRowsPerGroup)
+// rows; returns the largest group size.
+int build_groups(const std::vector<int> &hm, int H_kv, int cap, RowGroups &rg) {
   memset(&rg, 0, sizeof(rg));
   int maxcnt = 0;
   for (int g = 0; g < H_kv; ++g) {
     int cur = -1;
     for (int h = 0; h < (int)hm.size(); ++h) {
       if (hm[h] != g) continue;
-      if (cur < 0 || rg.cnt[cur] == kRowsPerGroup) {
+      if (cur < 0 || rg.cnt[cur] == cap) {
         cur = rg.n++;
         rg.g[cur] = (uint8_t)g;
       }
@@ -220,8 +222,12 @@ int build_groups(const std::vector<int> &hm, int H_kv, RowGroups &rg) {
       maxcnt = std::max(maxcnt, (int)rg.cnt[cur]);
     }
   }
+  return maxcnt;
+}
+
+int pow2_at_least(int n) {
   int R = 1;
-  while (R < maxcnt) R <<= 1;
+  while (R < n) R <<= 1;
   return R;
 }
 
@@ -312,7 +318,10 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   memset(&p, 0, sizeof(p));
   const int n_prob = (int)slots.size();
   const Slot &s0 = *slots[0];
-  const int R = build_groups(*c.hm, c.H_kv, p.rg);
+  const bool mlx4 = s0.fmt == PION_KV_MLX4G32;
+  // the mlx4g32 kernel holds up to kMlx4Rows rows; both launches of a call share groups
+  const int grp_rows = build_groups(*c.hm, c.H_kv, mlx4 ? kMlx4Rows : kRowsPerGroup, p.rg);
+  const int R = pow2_at_least(grp_rows);
   const int Y = p.rg.n * c.M;
   if (Y > 65535 || (long long)Y * n_prob > kMaxCounters) return PION_ERR_UNSUPPORTED;
   p.H_q = c.H_q;
@@ -370,16 +379,16 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   p.counters = g_ws[st].counters;
 
   hipError_t e;
-  if (p.fmt == PION_KV_MLX4G32) {
+  if (mlx4) {
     p.x_begin = 0;
-    e = launch_partial(p, R, pre_max, true, st);
+    e = launch_partial_mlx4(p, grp_rows, pre_max, st);
     if (e == hipSuccess && p.suf_splits > 0) {
       p.x_begin = pre_max;  // single problem: its prefix spans are exactly pre_max
-      e = launch_partial(p, R, p.suf_splits, false, st);
+      e = launch_partial(p, R, p.suf_splits, st);
     }
   } else {
     p.x_begin = 0;
-    e = launch_partial(p, R, p.S_max, false, st);
+    e = launch_partial(p, R, p.S_max, st);
   }
   return e == hipSuccess ? PION_OK : PION_ERR_HIP;
 }
@@ -425,7 +434,7 @@ int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D, uint32_t *codes
   if (!on_device(x) || !on_device(codes) || !on_device(scales) || !on_device(biases))
     return PION_ERR_INVALID;
   if (launch_quantize_mlx4g32((const uint16_t *)x, rows, D, codes, (uint16_t *)scales,
-                              (uint16_t *)biases, (hipStream_t)stream) != hipSuccess)
+                              (uint16_t *)biases, 1, (hipStream_t)stream) != hipSuccess)
     return PION_ERR_HIP;
   return PION_OK;
 }
@@ -467,11 +476,13 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
       e = hipMemcpyAsync(base + L.off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
   } else {
     const int64_t rows = (int64_t)H * N;
-    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + L.off[0]),
-                                (uint16_t *)(base + L.off[1]), (uint16_t *)(base + L.off[2]), st);
+    // scale and bias interleaved as (scale | bias << 16) words
+    uint16_t *ksb = (uint16_t *)(base + L.off[1]), *vsb = (uint16_t *)(base + L.off[3]);
+    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + L.off[0]), ksb,
+                                ksb + 1, 2, st);
     if (e == hipSuccess)
-      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[3]),
-                                  (uint16_t *)(base + L.off[4]), (uint16_t *)(base + L.off[5]), st);
+      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[2]),
+                                  vsb, vsb + 1, 2, st);
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(sl.ready, st);

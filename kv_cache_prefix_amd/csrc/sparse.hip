@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int n
       } else {
         const uint32_t w = kv.Kc[tok * (D / 8) + d / 8];
         const float c = (float)((w >> (4 * (d % 8))) & 0xFu);
-        x = __builtin_fmaf(h2f(kv.Ks[tok * (D / 32) + d / 32]), c,
-                           h2f(kv.Kb[tok * (D / 32) + d / 32]));
+        const uint32_t sb = kv.Ksb[tok * (D / 32) + d / 32];
+        x = __builtin_fmaf(h2f((uint16_t)(sb & 0xffffu)), c, h2f((uint16_t)(sb >> 16)));
       }
       sum += x;
     }

@@ -260,6 +260,68 @@ def test_mlx4g32_fused_suffix(kp):
     check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, Kh, Vh, inp.K_suf, inp.V_suf))
 
 
+def mlx4_ref(inp_K, inp_V):
+    D = inp_K.shape[-1]
+    Kh = oracle.dequantize(*oracle.quantize(inp_K.reshape(-1, D))).reshape(inp_K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp_V.reshape(-1, D))).reshape(inp_V.shape)
+    return Kh, Vh
+
+
+# q-heads per kv-head 1..4 fill one row group; 5 and 6 split into 4 + 1 and 4 + 2
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("H_q,H_kv", [(2, 2), (4, 2), (6, 2), (8, 2), (5, 1), (12, 2)])
+def test_mlx4g32_every_row_count(kp, D, H_q, H_kv):
+    inp = synth.generate(synth.MLX4_DECODE, 5, N=777, D=D, H_q=H_q, H_kv=H_kv)
+    kp.pion_prefix_store("t", 11, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 11, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V)))
+
+
+def test_mlx4g32_uneven_head_map(kp):
+    # kv-head 0 gets 5 q-heads (groups of 4 and 1), kv-head 1 gets 2, kv-head 2 gets 1
+    inp = synth.generate(synth.MLX4_DECODE, 6, N=300, H_q=8, H_kv=3)
+    hm = np.array([0, 1, 0, 0, 2, 0, 1, 0], np.int32)
+    kp.pion_prefix_store("t", 12, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 12, inp.Q, head_map=hm)
+    check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V), hm))
+
+
+def test_mlx4g32_large_values_stay_finite(kp):
+    # values near the fp16 limit: group scales up to ~8.7e3, where a fp16 weight p * s
+    # with p > 7.5 would overflow; the result must stay finite and close in relative terms
+    inp = synth.generate(synth.MLX4_DECODE, 7, N=1000, H_q=6, H_kv=2)
+    V = (inp.V.astype(np.float32) * 2.0e4).clip(-65504, 65504).astype(np.float16)
+    kp.pion_prefix_store("t", 13, dev(inp.K), dev(V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 13, inp.Q)
+    ref, ref_lse = oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, V))
+    assert np.all(np.isfinite(out))
+    scale = float(np.max(np.abs(V.astype(np.float64))))
+    assert np.max(np.abs(out - ref)) <= 1e-3 * scale
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_TOL
+
+
+def test_mlx4g32_rising_logits_rescale(kp):
+    # logits rise along the sequence, so every key slot's running max keeps moving
+    inp = synth.generate(synth.MLX4_DECODE, 8, N=4096, H_q=3, H_kv=1)
+    ramp = np.linspace(0.0, 4.0, 4096, dtype=np.float32)[None, :, None]
+    qdir = inp.Q[0, 0].astype(np.float32)
+    K = (inp.K.astype(np.float32) * 0.5 + ramp * qdir / np.linalg.norm(qdir)).astype(np.float16)
+    kp.pion_prefix_store("t", 14, dev(K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 14, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(K, inp.V)))
+
+
+def test_mlx4g32_dominant_key(kp):
+    # one key aligned with every query: its weight is ~1 and the rest ~0
+    inp = synth.generate(synth.MLX4_DECODE, 9, N=2048, H_q=4, H_kv=1)
+    K = inp.K.copy()
+    qsum = inp.Q[:, 0].astype(np.float32).sum(0)
+    K[0, 1234] = (40.0 * qsum / np.linalg.norm(qsum)).astype(np.float16)
+    kp.pion_prefix_store("t", 15, dev(K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 15, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(K, inp.V)))
+
+
 # ------------------------------------------------------------------ sparse-auto
 def sparse_call(kp, sid, layer, inp, B, K_top, H_kv, suffix=True, head_map=None):
     import torch
