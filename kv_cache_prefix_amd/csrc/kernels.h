@@ -140,10 +140,12 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
 hipError_t launch_partial_mlx4(const PartialParams &p, int rows_per_group, int x_count,
                                hipStream_t s);
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
-// causal suffix (bottom-right aligned). Workgroup (x, y): x = (q-head, block of 128
-// query rows), y = key split of split_keys tokens over the concatenated key index
-// [0, N + S_suf). With n_splits > 1 the splits' partials (same layout as PartialParams,
-// S_max = n_splits) merge in the last-arriving workgroup of each x (counters[x]).
+// causal suffix (bottom-right aligned). A workgroup serves (tile, split): tile = (q-head,
+// block of 128 query rows), split = a range of split_keys tokens of the concatenated key
+// index [0, N + S_suf). With n_splits > 1 the splits' partials ([H_q*M][n_splits][D] and
+// [H_q*M][n_splits]) merge in the last-arriving workgroup of each tile (counters[tile]).
+// The 1-D grid is ordered so that the workgroups of one kv-head share an XCD:
+// order[] lists the q-heads grouped by kv-head.
 struct PrefillParams {
   const uint16_t *Q;              // fp16 [H_q, M, D]
   const uint16_t *K, *V;          // fp16 [H_kv, N, D]
@@ -156,6 +158,7 @@ struct PrefillParams {
   float *part_acc, *part_m, *part_l;
   int *counters;
   HeadMap hm;
+  uint8_t order[kMaxHeads];       // q-heads sorted by kv-head
 };
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);

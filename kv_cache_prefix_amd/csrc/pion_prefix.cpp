@@ -280,9 +280,11 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   const long long tiles = (long long)c.H_q * p.n_iblk;
   if (tiles > kMaxCounters) return PION_ERR_UNSUPPORTED;
   const long long total = (long long)sl.N + c.S_suf;
-  // splits: as many as fit one workgroup per CU next to the other row blocks (each
-  // split adds a partial round trip and merge work); env PION_PREFILL_SPLITS overrides
-  long long ns = std::max<long long>(1, 256 / tiles);
+  // splits: up to about 1.5 workgroups per CU over the row blocks (two fit on a CU for
+  // D <= 128, one for D = 256); each split adds a partial round trip and merge work.
+  // env PION_PREFILL_SPLITS overrides
+  const long long slots = c.D <= 128 ? 384 : 256;
+  long long ns = std::max<long long>(1, (slots + tiles / 2) / tiles);
   if (const char *e = getenv("PION_PREFILL_SPLITS")) ns = std::max(1, atoi(e));
   ns = std::min<long long>(ns, std::min<long long>(16, (total + 63) / 64));
   long long sk = (total + ns - 1) / ns;
@@ -294,6 +296,12 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   p.lse = c.lse;
   p.hm.H_q = c.H_q;
   for (int h = 0; h < c.H_q; ++h) p.hm.m[h] = (uint8_t)(*c.hm)[h];
+  {
+    int n = 0;
+    for (int g = 0; g < c.H_kv; ++g)
+      for (int h = 0; h < c.H_q; ++h)
+        if ((*c.hm)[h] == g) p.order[n++] = (uint8_t)h;
+  }
   if (p.n_splits > 1) {
     const size_t rows = (size_t)c.H_q * c.M;
     const size_t acc_bytes = align256(rows * p.n_splits * c.D * sizeof(float));
@@ -311,7 +319,10 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
 // One launch (two for an mlx4g32 prefix with an fp16 suffix) over `slots`, which share
 // H, D and format.
 int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hipStream_t st) {
+  // (the MFMA kernel addresses a kv-head's K, V and suffix through 32-bit buffer ranges)
+  const long long row_bytes = 2LL * c.D;
   if (slots.size() == 1 && slots[0]->fmt == PION_KV_FP16 && !c.blocks && c.M >= kMfmaMinRows &&
+      slots[0]->N * row_bytes < (1LL << 31) && c.S_suf * row_bytes < (1LL << 31) &&
       !getenv_flag("PION_NO_MFMA"))
     return run_prefill(*slots[0], c, st);
   static PartialParams p;  // large; the library lock serializes callers

@@ -17,12 +17,24 @@
 //                 the PV product takes elements i = 2s, 2s+1 as its eight k slots.
 //   O^T += V^T P^T  A = V^T (LDS, stored transposed at staging so each lane reads two
 //                 runs of 4 keys), with the k slots in that same key order.
-// K and V of the next tile are fetched into registers while the current tile is
-// consumed, then written to LDS (K as rows padded by 16 bytes, V transposed with rows
-// padded by 8 bytes; both conflict-free for the operand reads).
+// Staging: K and V tiles go from HBM straight into LDS with buffer loads that write LDS
+// (no register staging), NSTAGE tiles deep: the loads of tile j + NSTAGE - 1 are issued
+// when tile j starts. Both tiles are stored row-major with the 16-byte chunks of a row
+// XOR-swizzled by a function of the row (swz), which makes the K operand reads and the
+// transposed V reads bank-conflict free. V^T operands come from row-major V through the
+// LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i receives
+// element i % 4 of the 8-byte pieces addressed by lanes 4j + i/4 (j = 0..3), so lanes
+// addressing (row kbase + q/4, dims dbase + 4(q%4)) receive 4 consecutive keys of dim
+// dbase + i.
+// The compiler cannot tell which LDS bytes an asynchronous LDS load writes, so it
+// would wait for every outstanding one before any LDS read; the loads are issued
+// through inline assembly instead and the kernel waits for them itself (s_waitcnt
+// vmcnt, then a barrier) before a stage is read.
 // Splits of the key range run in different workgroups; the last one of a row block
 // merges their (acc, m, l) partials with the LSE rule, as in the split-KV decode kernel.
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace pion {
 namespace {
@@ -44,16 +56,14 @@ constexpr int kMaxPrefillSplits = 16;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
+constexpr int NSTAGE = 2;  // LDS tile stages (loads run NSTAGE - 1 tiles ahead)
+
 template <int D>
 struct PrefillSmem {
-  static constexpr int KST = D + 8;   // K tile row stride (halves)
-  static constexpr int VST = BK + 4;  // V^T row stride (halves)
+  static constexpr int TB = BK * 2 * D;  // bytes of one K or V tile
   union {
-    struct {
-      alignas(16) _Float16 k[BK * KST];
-      alignas(16) _Float16 vt[D * VST];
-    };
-    struct {                      // split merge: per (row, split) m then weight, and l
+    alignas(16) char kv[NSTAGE][2][TB];  // [stage][0: K, 1: V]
+    struct {                             // split merge: per (row, split) m then weight, and l
       float w[BQ * 16];
       float l[BQ * 16];
       float inv[BQ];
@@ -61,6 +71,33 @@ struct PrefillSmem {
   };
   int last;
 };
+
+// Physical 16-byte chunk of logical chunk c in tile row r is c ^ swz(r) (found by an
+// exhaustive search for conflict-free K reads and transposed V reads, 64 banks).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) return ((r & 3) << 1) ^ ((r >> 1) & 7);
+  else return ((r & 3) << 2) ^ ((r >> 2) & 3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));  // builtin type
+#define LDS_PTR(T, x) ((__attribute__((address_space(3))) T *)(x))
+
+// Raw buffer descriptor words (as make_rsrc) for the LDS-writing loads.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
+}
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (lds uniform);
+// past the buffer's end the bytes are zero. One wait state separates the M0 write from
+// the load that reads it.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(lds), "s"(rsrc)
+                   : "memory", "m0");
+}
 
 // A row max may grow by this much (log2 units, a factor 2^8) before the accumulators
 // are rescaled: weights up to 2^8 stay exact enough in fp16 and the fp32 sums cannot
@@ -74,24 +111,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(PrefillParams p) {
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
   constexpr int NDS = D / 16;                 // 16-dim k-steps of S^T
-  constexpr int KST = PrefillSmem<D>::KST, VST = PrefillSmem<D>::VST;
   constexpr int CH = D / 8;                   // 16-byte chunks per key row
-  constexpr int KITEMS = BK * CH / 256;       // K chunks per thread per tile
-  constexpr int VITEMS = (BK / 2) * CH / 256; // V (key-pair, chunk) items per thread
   constexpr uint32_t ROWB = D * 2;            // bytes per key row
+  constexpr int TB = PrefillSmem<D>::TB;
+  constexpr int NLD = TB / 1024 / 4;          // 1 KB LDS loads per wave, tile and side
   __shared__ PrefillSmem<D> sm;
 
-  const int tile = blockIdx.x, split = blockIdx.y;
-  const int h = tile / p.n_iblk, i0 = (tile - h * p.n_iblk) * BQ;
+  // Workgroups are dispatched to the 8 XCDs round-robin by block index; block b runs
+  // logical workgroup xcd * C + b / 8 (C = blocks per XCD), and logical workgroups are
+  // ordered by (q-head in kv-head order, row block, split). The workgroups that read one
+  // kv-head's K and V then share an XCD and its L2. Blocks past the end exit.
+  const int W = p.H_q * p.n_iblk * p.n_splits, C = (W + 7) >> 3;
+  const int L = (blockIdx.x & 7) * C + (blockIdx.x >> 3);
+  if (L >= W) return;
+  const int split = L % p.n_splits, ts = L / p.n_splits;
+  const int hs = ts / p.n_iblk, ib = ts - hs * p.n_iblk;
+  const int h = p.order[hs], i0 = ib * BQ;
+  const int tile = h * p.n_iblk + ib;
   const int g = p.hm.m[h];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
@@ -109,28 +150,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   const int lim_first = p.S_suf > 0 ? p.N + p.S_suf - p.M + i0 + 1 : p.N;
   const int full_end = min(k_end, lim_first);
 
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.K + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.V + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
+  const i32x4 rK = rsrc_words(p.K + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
+  const i32x4 rV = rsrc_words(p.V + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
   const bool has_suf = p.S_suf > 0;  // a null suffix gets an empty range
-  const __amdgpu_buffer_rsrc_t rKs =
-      make_rsrc(has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : p.K, (uint32_t)p.S_suf * ROWB);
-  const __amdgpu_buffer_rsrc_t rVs =
-      make_rsrc(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWB);
+  const i32x4 rKs =
+      rsrc_words(has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : p.K, (uint32_t)p.S_suf * ROWB);
+  const i32x4 rVs =
+      rsrc_words(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWB);
 
-  half8 qb[NDS];
-  {
-    const uint16_t *qrow = p.Q + ((size_t)h * p.M + qi_c) * D;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qb[ds] = *(const half8 *)(qrow + 16 * ds + 8 * hl);
-  }
-  f16v o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
-
-  uint4 kreg[KITEMS], vreg[VITEMS][2];
   // Tiles never straddle the prefix / suffix boundary: the split's prefix part
   // [k_begin, pre_end) is tiled from k_begin, its suffix part [suf_beg, k_stop) from
   // suf_beg. Tile j < n_pre is prefix, the rest suffix.
@@ -138,76 +165,136 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   const int suf_beg = max(k_begin, p.N);
   const int n_pre = k_begin < pre_end ? (pre_end - k_begin + BK - 1) / BK : 0;
   const int n_suf = suf_beg < k_stop ? (k_stop - suf_beg + BK - 1) / BK : 0;
-  auto gload = [&](int j) {
+  const int n_tiles = n_pre + n_suf;
+
+  // LDS loads of a tile: wave w's load t fills tile bytes [1 KB (NLD w + t), +1 KB),
+  // lane l the 16 bytes at 16 l there: tile row r, physical chunk l % CH, which holds
+  // logical chunk (l % CH) ^ swz(r) of source row r0 + r.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, &sm.kv[0][0][0]);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t voff[NLD];
+#pragma unroll
+  for (int t = 0; t < NLD; ++t) {
+    const int r = (1024 * (NLD * wave_u + t) + 16 * lane) / (int)ROWB;
+    const int pc = lane % CH;
+    voff[t] = (uint32_t)r * ROWB + (uint32_t)((pc ^ swz<D>(r)) * 16);
+  }
+  auto issue = [&](int j) {
     const bool suf = j >= n_pre;  // workgroup-uniform
     const int r0 = suf ? suf_beg - p.N + (j - n_pre) * BK : k_begin + j * BK;  // source row
-    const __amdgpu_buffer_rsrc_t rk = suf ? rKs : rK, rv = suf ? rVs : rV;
+    const i32x4 rk = suf ? rKs : rK, rv = suf ? rVs : rV;
+    const uint32_t st = lds0 + (uint32_t)((j % NSTAGE) * 2 * TB + 1024 * NLD * wave_u);
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int item = tid + 256 * it, key = item / CH, ch = item - key * CH;
-      kreg[it] = bload(rk, (uint32_t)(r0 + key) * ROWB + ch * 16);
-    }
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int item = tid + 256 * it, kp = item & 31, ch = item >> 5;
-      vreg[it][0] = bload(rv, (uint32_t)(r0 + 2 * kp) * ROWB + ch * 16);
-      vreg[it][1] = bload(rv, (uint32_t)(r0 + 2 * kp + 1) * ROWB + ch * 16);
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int item = tid + 256 * it, key = item / CH, ch = item - key * CH;
-      *(uint4 *)&sm.k[key * KST + ch * 8] = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int item = tid + 256 * it, kp = item & 31, ch = item >> 5;
-      const uint32_t a[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
-      const uint32_t b[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t lo = (a[c] & 0xffffu) | (b[c] << 16);          // dim 2c of both keys
-        const uint32_t hi = (a[c] >> 16) | (b[c] & 0xffff0000u);     // dim 2c + 1
-        *(uint32_t *)&sm.vt[(ch * 8 + 2 * c) * VST + 2 * kp] = lo;
-        *(uint32_t *)&sm.vt[(ch * 8 + 2 * c + 1) * VST + 2 * kp] = hi;
-      }
+    for (int t = 0; t < NLD; ++t) {
+      load_lds16(rk, (uint32_t)r0 * ROWB + voff[t], st + 1024 * t);
+      load_lds16(rv, (uint32_t)r0 * ROWB + voff[t], st + TB + 1024 * t);
     }
   };
 
-  const int n_tiles = n_pre + n_suf;
-  if (n_tiles > 0) gload(0);
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = 0; j < NSTAGE - 1 && j < n_tiles; ++j) issue(j);
+  half8 qb[NDS];
+  {
+    const uint16_t *qrow = p.Q + ((size_t)h * p.M + qi_c) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qb[ds] = *(const half8 *)(qrow + 16 * ds + 8 * hl);
+  }
+  // Q (and the first tiles) have arrived: the compiler then knows no load of its own is
+  // outstanding in the loop, where any vmcnt wait it added would also drain the loads
+  // of the next tiles
+  __builtin_amdgcn_s_waitcnt(0);
+  f16v o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+
+  // Operand addresses inside a stage, as loop-invariant lane offsets (the stage and
+  // sub-tile parts are immediates): K row 32 kb + col at logical chunk 2 ds + hl; V^T
+  // via transposed reads: lane (group gq, index q) addresses row kbase + q/4 at dims
+  // 32 db + 16 gq + 4 (q%4), for kbase = 32 kb + 16 s2 + 4 hl + 8 c (c = 0, 1: the two
+  // runs of 4 keys of a 16-key k-step); the swizzle of those rows depends on q, hl, c.
+  const char *smb = &sm.kv[0][0][0];
+  uint32_t koff[NDS];
+  {
+    const int swk = swz<D>(col);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      koff[ds] = (uint32_t)col * ROWB + (uint32_t)(((2 * ds + hl) ^ swk) << 4);
+  }
+  uint32_t voffs[2][NDB];
+  {
+    const int q16 = lane & 15, gq = (lane >> 4) & 1;
+    const int vch = 2 * gq + ((q16 & 3) >> 1);  // logical chunk minus 4 db
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = 4 * hl + 8 * c + (q16 >> 2);  // row modulo 16
+      const int vsw = swz<D>(r);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        voffs[c][db] = (uint32_t)r * ROWB + (uint32_t)(q16 & 1) * 8 +
+                       (uint32_t)(((4 * db + vch) ^ vsw) << 4);
+    }
+  }
+  auto kfrag = [&](int base, int ds) {  // base: byte offset of the 32-key sub-tile in LDS
+    return __builtin_bit_cast(half8, *(const uint4 *)(smb + base + koff[ds]));
+  };
+  auto vfrag = [&](int base, int db) {  // base: byte offset of the 16-key k-step in LDS
+    half4 part[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      part[c] = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                              LDS_PTR(fp16x4_t, smb + base + voffs[c][db])));
+    return half8{part[0][0], part[0][1], part[0][2], part[0][3],
+                 part[1][0], part[1][1], part[1][2], part[1][3]};
+  };
+  constexpr int KR = NDS < 4 ? NDS : 4;  // K fragments in flight ahead of their product
+
+  // One 64-key tile from LDS stage STG (a compile-time constant, so every operand
+  // address is a lane offset plus an immediate).
+  auto run_tile = [&](auto stg, int j) {
+    constexpr int STG = decltype(stg)::value;
     const bool suf = j >= n_pre;
     const int t0 = suf ? suf_beg + (j - n_pre) * BK : k_begin + j * BK;  // concatenated index
     const int seg_end = suf ? k_stop : pre_end;   // keys at or past this are not in the tile
     const int lane_end = suf ? row_end : pre_end; // this row's limit inside the tile
     const int clean_end = suf ? min(k_stop, full_end) : pre_end;  // no mask below this
-    __syncthreads();  // the previous tile's operand reads are done
-    swrite();
+    // this wave's loads of tile j are done (later tiles' loads may stay in flight) ...
+    if (NSTAGE > 2 && j + 1 < n_tiles)
+      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD * (NSTAGE > 2 ? NSTAGE - 2 : 0)) : "memory");
+    else
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // ... and every wave's; every wave is also done reading the stage loaded next
     __syncthreads();
-    if (j + 1 < n_tiles) gload(j + 1);
+    if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
+    constexpr int KB = STG * 2 * TB, VB = KB + TB;  // stage offsets of K and V
 
     // two 32-key sub-tiles: S^T, softmax, PV
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int kt = t0 + 32 * kb;
-      if (kt >= seg_end) break;  // workgroup-uniform
+      const int kt0 = t0 + 32 * kb;
+      if (kt0 >= seg_end) break;  // workgroup-uniform
       f16v s;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      half8 kf[KR];
+#pragma unroll
+      for (int ds = 0; ds < KR; ++ds) kf[ds] = kfrag(KB + 32 * kb * (int)ROWB, ds);
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const uint4 araw = *(const uint4 *)&sm.k[(32 * kb + col) * KST + 16 * ds + 8 * hl];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, araw), qb[ds], s,
-                                                   0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds % KR], qb[ds], s, 0, 0, 0);
+        if (ds + KR < NDS) kf[ds % KR] = kfrag(KB + 32 * kb * (int)ROWB, ds + KR);
       }
-      if (kt + 32 > clean_end) {  // boundary sub-tile: mask keys past this row's limit
+      // the first k-step's V^T fragments load while the softmax runs
+      half8 vf[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf[db] = vfrag(VB + 32 * kb * (int)ROWB, db);
+      if (kt0 + 32 > clean_end) {  // boundary sub-tile: mask keys past this row's limit
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            if (kt + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
+            if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
       }
       float mt = -INFINITY;  // raw-score max; the scale is positive
 #pragma unroll
@@ -232,18 +319,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
       }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const _Float16 *vrow = &sm.vt[(32 * db + col) * VST + 32 * kb + 16 * s2 + 4 * hl];
-          const uint2 lo = *(const uint2 *)vrow;
-          const uint2 hi = *(const uint2 *)(vrow + 8);
-          const uint4 araw = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, araw), pb[s2],
-                                                         o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pb[0], o[db], 0, 0, 0);
+        vf[db] = vfrag(VB + (32 * kb + 16) * (int)ROWB, db);
       }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pb[1], o[db], 0, 0, 0);
     }
+  };
+
+  for (int j = 0; j < n_tiles; j += NSTAGE) {
+    run_tile(std::integral_constant<int, 0>(), j);
+    if (j + 1 < n_tiles) run_tile(std::integral_constant<int, 1>(), j + 1);
+    if constexpr (NSTAGE > 2)
+      if (j + 2 < n_tiles) run_tile(std::integral_constant<int, 2>(), j + 2);
   }
   l_run += __shfl_xor(l_run, 32);
 
@@ -305,12 +395,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   __syncthreads();
   if (!sm.last) return;
 
-  // Merge, in three phases with every load of a phase in flight together:
+  // Merge, in three phases with the loads of a phase issued together:
   // (1) m and l of all (row, split) into LDS; (2) per row the weights 2^(m_c - m*) and
-  // 1 / sum_c w_c l_c, and lse; (3) out = sum_c w_c acc_c / L in 16-byte pieces.
-  for (int x = tid; x < rows_valid * S; x += 256) {
-    sm.mg.w[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, x * 4, 0, SC1));
-    sm.mg.l[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, x * 4, 0, SC1));
+  // 1 / sum_c w_c l_c, and lse; (3) out = sum_c w_c acc_c / L in 16-byte pieces, CB
+  // splits per round (up to 16 pieces in flight per thread).
+  for (int x0 = 0; x0 < rows_valid * S; x0 += 4 * 256) {
+    constexpr int ML = 4;
+    float mv[ML], lv[ML];
+#pragma unroll
+    for (int k = 0; k < ML; ++k) {
+      const int x = x0 + tid + 256 * k;
+      const bool in = x < rows_valid * S;
+      mv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, x * 4, 0, SC1)) : 0.f;
+      lv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, x * 4, 0, SC1)) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < ML; ++k) {
+      const int x = x0 + tid + 256 * k;
+      if (x < rows_valid * S) {
+        sm.mg.w[x] = mv[k];
+        sm.mg.l[x] = lv[k];
+      }
+    }
   }
   __syncthreads();
   if (tid < rows_valid) {
@@ -328,25 +434,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   __syncthreads();
   constexpr int Q4 = D / 4;                  // 16-byte pieces per row
   constexpr int ITER = BQ * Q4 / 256;        // pieces per thread
+  constexpr int CB = ITER >= 16 ? 1 : 16 / ITER;  // splits per round
   float4 acc[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < S; ++c) {
-    f32x4 v[ITER];
+  for (int c0 = 0; c0 < S; c0 += CB) {
+    f32x4 v[CB][ITER];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
-      v[it] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, ((r * S + c) * D + 4 * d4) * 4, 0, SC1));
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = c0 + cb < S ? c0 + cb : c0;  // a past-the-end split repeats c0, weight 0
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
+        v[cb][it] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, ((r * S + c) * D + 4 * d4) * 4, 0, SC1));
+      }
     }
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int q = tid + 256 * it, r = q / Q4;
-      const float w = r < rows_valid ? sm.mg.w[r * S + c] : 0.f;
-      acc[it].x = __builtin_fmaf(w, v[it].x, acc[it].x);
-      acc[it].y = __builtin_fmaf(w, v[it].y, acc[it].y);
-      acc[it].z = __builtin_fmaf(w, v[it].z, acc[it].z);
-      acc[it].w = __builtin_fmaf(w, v[it].w, acc[it].w);
+    for (int cb = 0; cb < CB; ++cb) {
+      if (c0 + cb >= S) break;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int q = tid + 256 * it, r = q / Q4;
+        const float w = r < rows_valid ? sm.mg.w[r * S + c0 + cb] : 0.f;
+        acc[it].x = __builtin_fmaf(w, v[cb][it].x, acc[it].x);
+        acc[it].y = __builtin_fmaf(w, v[cb][it].y, acc[it].y);
+        acc[it].z = __builtin_fmaf(w, v[cb][it].z, acc[it].z);
+        acc[it].w = __builtin_fmaf(w, v[cb][it].w, acc[it].w);
+      }
     }
   }
 #pragma unroll
@@ -365,7 +480,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s) {
   if (p.n_splits < 1 || p.n_splits > kMaxPrefillSplits || p.split_keys % BK) return hipErrorInvalidValue;
-  dim3 grid(p.H_q * p.n_iblk, p.n_splits);
+  const int W = p.H_q * p.n_iblk * p.n_splits;
+  dim3 grid(8 * ((W + 7) / 8));
   switch (p.D) {
     case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, p); break;
     case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, p); break;
