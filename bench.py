@@ -22,6 +22,13 @@ of launches is the mean launch duration (back-to-back launches, so inter-kernel 
 count against the kernel). The roofline figure is the algorithmic bytes (or flops) of
 one launch over that duration.
 
+Cold memory-side cache: MI355X keeps up to 256 MB of recently used lines in its
+memory-side (infinity) cache. The M=1 workloads therefore rotate over copies of their
+resident data whose total is well above that (config 2: two 32-layer sets, 537 MB;
+config 4: 16 slots, 671 MB; config 5: 4 slots), so each step reads data the previous
+steps have evicted; `value` is that cold figure. `warm` repeats one set every step and
+is reported beside it, labelled.
+
 cpu_baseline: the fp64 numpy oracle as it stands, one thread, on a bounded sample of the
 same workload (about 10 s), scaled to the metric's unit.
 """
@@ -41,15 +48,16 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the decode kernel in --mode layers, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counter passes scaled by the same counters on a plain 256 MiB copy
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
-# taken on (sha256 of attn_partial.hip + kernels.h); any other source reports null.
-DECODE_TRAFFIC = {"sources_sha256": "d72be12ad2ee26be5621fb37f1f5a4032775b90c56299bc79dc2ca22c4b5a5cc",
-                  "bytes_per_launch": 269102239}
+# taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
+# reports null.
+DECODE_TRAFFIC = {"sources_sha256": "760e53c9ab08f23d62bd41fa554d6b25ab09df9e2a60ea062de75765ba7ba12f",
+                  "bytes_per_launch": 269461387}
 
 
 def kernel_sources_sha256():
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn_partial.hip", "kernels.h"):
+    for f in ("attn_partial.hip", "split_common.h", "kernels.h"):
         with open(os.path.join(ROOT, "kv_cache_prefix_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -76,29 +84,37 @@ def parse():
 
 
 class Timed:
-    """Times `step` (a host function issuing ABI calls on the current stream)."""
+    """Times steps: `steps` is a list of host functions issuing ABI calls on the current
+    stream; step i of the timed run is steps[i % len(steps)] (one graph each in graph
+    mode)."""
 
-    def __init__(self, torch, stream, step, launches_per_step, use_graph):
-        self.torch, self.stream, self.step = torch, stream, step
+    def __init__(self, torch, stream, steps, launches_per_step, use_graph):
+        self.torch, self.stream = torch, stream
+        self.steps = steps if isinstance(steps, list) else [steps]
         self.lps = launches_per_step
-        self.graph = None
+        self.graphs = None
         with torch.cuda.stream(stream):
             for _ in range(3):
-                step()
+                for st in self.steps:
+                    st()
         torch.cuda.synchronize()
         if use_graph:
-            self.graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(self.graph, stream=stream):
-                step()
+            self.graphs = []
+            for st in self.steps:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    st()
+                self.graphs.append(g)
             torch.cuda.synchronize()
 
     def _run(self, n):
+        k = len(self.steps)
         with self.torch.cuda.stream(self.stream):
-            for _ in range(n):
-                if self.graph is not None:
-                    self.graph.replay()
+            for i in range(n):
+                if self.graphs is not None:
+                    self.graphs[i % k].replay()
                 else:
-                    self.step()
+                    self.steps[i % k]()
 
     def measure(self, steps, warmup):
         torch = self.torch
@@ -115,6 +131,14 @@ class Timed:
         ms_per_step = wall * 1e3 / steps
         launch_us = ev0.elapsed_time(ev1) * 1e3 / (steps * self.lps)
         return ms_per_step, launch_us
+
+
+def warm_cold(torch, stream, steps, lps, graph, args):
+    """Cold figure (rotating over all step functions) and warm figure (the first one
+    repeated)."""
+    cold = Timed(torch, stream, steps, lps, graph).measure(args.steps, args.warmup)
+    warm = Timed(torch, stream, steps[:1], lps, graph).measure(args.steps, args.warmup)
+    return cold, warm
 
 
 def cpu_time(fn, seconds):
@@ -145,9 +169,11 @@ def run_decode(args, torch, kp, synth, dev, stream):
     case = synth.DECODE
     inputs = [synth.generate(case, l) for l in range(case.layers)]
     sid = "bench-decode"
-    for l, inp in enumerate(inputs):
-        kp.pion_prefix_store(sid, l, torch.from_numpy(inp.K).to(dev),
-                             torch.from_numpy(inp.V).to(dev))
+    NSET = 2   # layers [32 k, 32 k + 32) hold set k (the same data)
+    for k in range(NSET):
+        for l, inp in enumerate(inputs):
+            kp.pion_prefix_store(sid, case.layers * k + l, torch.from_numpy(inp.K).to(dev),
+                                 torch.from_numpy(inp.V).to(dev))
     Qall = torch.from_numpy(np.stack([i.Q for i in inputs])).to(dev)
     out = torch.empty((case.layers, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
     lse = torch.empty((case.layers, case.H_q, 1), dtype=torch.float32, device=dev)
@@ -155,30 +181,34 @@ def run_decode(args, torch, kp, synth, dev, stream):
     lib, sidb = kp.lib(), sid.encode()
     if args.mode == "layers":
         fn = lib.pion_prefix_query_layers
-        calls = [(sidb, 0, case.layers, case.H_q, case.D, 1, Qall.data_ptr(), None,
-                  out.data_ptr(), lse.data_ptr())]
+        calls = [[(sidb, case.layers * k, case.layers, case.H_q, case.D, 1, Qall.data_ptr(), None,
+                   out.data_ptr(), lse.data_ptr())] for k in range(NSET)]
     else:
         fn = lib.pion_prefix_query
-        calls = [(sidb, l, case.H_q, case.D, 1, Qall[l].data_ptr(), None, out[l].data_ptr(),
-                  lse[l].data_ptr()) for l in range(case.layers)]
+        calls = [[(sidb, case.layers * k + l, case.H_q, case.D, 1, Qall[l].data_ptr(), None,
+                   out[l].data_ptr(), lse[l].data_ptr()) for l in range(case.layers)]
+                 for k in range(NSET)]
 
-    def step():
-        h = torch.cuda.current_stream().cuda_stream
-        for c in calls:
-            rc = fn(*c, h)
-            if rc != 0:
-                raise kp.PionError(rc, fn.__name__)
+    def make_step(cs):
+        def step():
+            h = torch.cuda.current_stream().cuda_stream
+            for c in cs:
+                rc = fn(*c, h)
+                if rc != 0:
+                    raise kp.PionError(rc, fn.__name__)
+        return step
 
     graph = args.mode == "calls" and not args.eager
-    t = Timed(torch, stream, step, len(calls), graph)
-    ms, launch_us = t.measure(args.steps, args.warmup)
+    lps = len(calls[0])
+    (ms, launch_us), (wms, wlaunch_us) = warm_cold(torch, stream, [make_step(c) for c in calls],
+                                                   lps, graph, args)
     for l in (0, case.layers - 1):
         ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
         check_close(out[l].cpu().numpy(), ref, 2e-3, "out")
         check_close(lse[l].cpu().numpy(), ref_lse, 1e-4, "lse")
     bytes_layer = case.H_kv * case.N * case.D * 2 * 2
     bytes_step = bytes_layer * case.layers
-    bytes_launch = bytes_step // len(calls)
+    bytes_launch = bytes_step // lps
     cpu = None
     if not args.no_cpu_baseline:
         def one_pass():
@@ -195,9 +225,11 @@ def run_decode(args, torch, kp, synth, dev, stream):
         "dtype": "fp16 K/V, fp32 accumulate",
         "config": {"workload": "M=1 prefix attention, decode shape H_q=H_kv=8 N=2048 D=128, "
                                "32 resident layers queried per step",
-                   "entry": fn.__name__, "launches_per_step": len(calls),
+                   "entry": fn.__name__, "launches_per_step": lps,
                    "launch": "hip-graph replay" if graph else "eager",
-                   "bytes_per_step": bytes_step},
+                   "bytes_per_step": bytes_step,
+                   "memory_side_cache": f"cold: steps alternate over {NSET} copies of the 32 "
+                                        f"layers ({NSET * bytes_step / 1e6:.0f} MB)"},
         "roofline": {"bound": "hbm", "achieved": bytes_launch / (launch_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "traffic": (DECODE_TRAFFIC["bytes_per_launch"]
@@ -206,6 +238,9 @@ def run_decode(args, torch, kp, synth, dev, stream):
                                  else None),
                      "kernel": "attn_split_kernel<128,1,4>",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
+        "warm": {"value": round(bytes_step / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
+                 "avg_launch_us": round(wlaunch_us, 3),
+                 "note": "the same 32 layers every step (memory-side cache warm)"},
         "cpu_baseline": cpu,
     }
 
@@ -268,21 +303,27 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
     case = synth.MLX4_DECODE
     inp = synth.generate(case)
     sid = "bench-mlx4"
-    kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
-                         torch.from_numpy(inp.V).to(dev), kp.PION_KV_MLX4G32)
+    NSLOT = 16   # the same quantized prefix in 16 slots (671 MB)
+    K16, V16 = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
+    for k in range(NSLOT):
+        kp.pion_prefix_store(sid, k, K16, V16, kp.PION_KV_MLX4G32)
+    del K16, V16
     Q = torch.from_numpy(inp.Q).to(dev)
     out = torch.empty((case.H_q, 1, case.D), dtype=torch.float32, device=dev)
     lse = torch.empty((case.H_q, 1), dtype=torch.float32, device=dev)
     lib, sidb = kp.lib(), sid.encode()
-    a = (sidb, 0, case.H_q, case.D, 1, Q.data_ptr(), None, out.data_ptr(), lse.data_ptr())
 
-    def step():
-        rc = lib.pion_prefix_query(*a, torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
-            raise kp.PionError(rc, "pion_prefix_query")
+    def make_step(k):
+        a = (sidb, k, case.H_q, case.D, 1, Q.data_ptr(), None, out.data_ptr(), lse.data_ptr())
 
-    t = Timed(torch, stream, step, 1, False)
-    ms, launch_us = t.measure(args.steps, args.warmup)
+        def step():
+            rc = lib.pion_prefix_query(*a, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_prefix_query")
+        return step
+
+    (ms, launch_us), (wms, wlaunch_us) = warm_cold(
+        torch, stream, [make_step(k) for k in range(NSLOT)], 1, False, args)
     Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
     Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
     ref, _ = oracle.prefix_query(inp.Q, Kh, Vh)
@@ -293,10 +334,16 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
         "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
         "dtype": "int4 codes + fp16 scale/bias, fp32 accumulate",
         "config": {"workload": "mlx4g32 decode H_q=24 H_kv=8 (h//3) D=128 N=32768 M=1",
-                   "bytes_per_step": nbytes},
+                   "bytes_per_step": nbytes,
+                   "memory_side_cache": f"cold: steps rotate over {NSLOT} slots "
+                                        f"({NSLOT * nbytes / 1e6:.0f} MB)"},
         "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "kernel": "mlx4_split_kernel<128,3,2,8>",
                      "avg_launch_us": launch_us},
+        "warm": {"value": round(nbytes / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
+                 "avg_launch_us": round(wlaunch_us, 3),
+                 "note": "one slot every step (memory-side cache warm)"},
         "cpu_baseline": None,
     }
 
@@ -306,22 +353,30 @@ def run_sparse(args, torch, kp, synth, dev, stream):
     case = synth.SPARSE
     inp = synth.generate(case)
     sid = "bench-sparse"
-    kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
-                         torch.from_numpy(inp.V).to(dev))
+    NSLOT = 4   # the same prefix in 4 slots (268 MB)
+    K16, V16 = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
+    for k in range(NSLOT):
+        kp.pion_prefix_store(sid, k, K16, V16)
+    del K16, V16
     Q, Ks, Vs = (torch.from_numpy(a).to(dev) for a in (inp.Q, inp.K_suf, inp.V_suf))
     out = torch.empty((case.H_q, case.D), dtype=torch.float32, device=dev)
     blocks = torch.empty((case.H_kv, case.K_top), dtype=torch.int32, device=dev)
     lib, sidb = kp.lib(), sid.encode()
-    a = (sidb, 0, case.H_q, case.D, case.B, case.K_top, case.H_kv, case.S_suf, Q.data_ptr(),
-         Ks.data_ptr(), Vs.data_ptr(), None, out.data_ptr(), None, blocks.data_ptr())
 
-    def step():
-        rc = lib.pion_prefix_query_sparse_auto(*a, torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
-            raise kp.PionError(rc, "pion_prefix_query_sparse_auto")
+    def make_step(k):
+        a = (sidb, k, case.H_q, case.D, case.B, case.K_top, case.H_kv, case.S_suf, Q.data_ptr(),
+             Ks.data_ptr(), Vs.data_ptr(), None, out.data_ptr(), None, blocks.data_ptr())
 
-    t = Timed(torch, stream, step, 3, False)   # block_score, block_topk, split kernel
-    ms, _ = t.measure(args.steps, args.warmup)
+        def step():
+            rc = lib.pion_prefix_query_sparse_auto(*a, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_prefix_query_sparse_auto")
+        return step
+
+    # 3 launches per query: block_score, block_topk, split kernel (block means cached
+    # per slot by the first query, inside the untimed warm-up)
+    (ms, _), (wms, _) = warm_cold(torch, stream, [make_step(k) for k in range(NSLOT)], 3,
+                                  False, args)
     ref, _, ref_blocks = oracle.prefix_query_sparse_auto(inp.Q, inp.K, inp.V, case.B,
                                                          case.K_top, None, inp.K_suf, inp.V_suf)
     check_close(out.cpu().numpy(), ref, 2e-3, "out")
@@ -335,9 +390,12 @@ def run_sparse(args, torch, kp, synth, dev, stream):
         "value": ms * 1e3, "unit": "us/query", "ms_per_step": ms,
         "dtype": "fp16 K/V, fp32 accumulate",
         "config": {"workload": "sparse-auto fused H_q=8 H_kv=1 D=256 N=65536 B=64 K_top=8 "
-                               "S_suf=64 M=1 (block means cached)", "bytes_per_step": nbytes},
+                               "S_suf=64 M=1 (block means cached)", "bytes_per_step": nbytes,
+                   "memory_side_cache": f"cold: steps rotate over {NSLOT} slots"},
         "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
+        "warm": {"value": round(wms * 1e3, 3), "unit": "us/query",
+                 "note": "one slot every step (memory-side cache warm)"},
         "cpu_baseline": None,
     }
 
@@ -413,6 +471,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
+    if "warm" in r:
+        line["warm"] = r["warm"]
     print(json.dumps(line), flush=True)
 
 

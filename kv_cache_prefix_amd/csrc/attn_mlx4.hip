@@ -119,10 +119,10 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     for (int u = 0; u < U; ++u) {
       const int j = base + u * KPW + kk;
       const size_t jj = j < sp.j1 ? j : sp.j0;  // in-bounds stand-in, masked in consume
-      t.kc[u] = Kc[jj * NG];
-      t.vc[u] = Vc[jj * NG];
-      t.ksb[u] = Ksb[jj * NG];
-      t.vsb[u] = Vsb[jj * NG];
+      t.kc[u] = ld_stream16(Kc + jj * NG);
+      t.vc[u] = ld_stream16(Vc + jj * NG);
+      t.ksb[u] = ld_stream4(Ksb + jj * NG);
+      t.vsb[u] = ld_stream4(Vsb + jj * NG);
     }
   };
 

@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
       const int j = base + u * KPI + kk;
       t.ok[u] = j < sp.j1;
       if (t.ok[u]) {
-        t.k[u] = *(const uint4 *)(Kf + (size_t)j * D + sub * 8);
-        t.v[u] = *(const uint4 *)(Vf + (size_t)j * D + sub * 8);
+        t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
+        t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
       } else {
         t.k[u] = make_uint4(0, 0, 0, 0);
         t.v[u] = make_uint4(0, 0, 0, 0);

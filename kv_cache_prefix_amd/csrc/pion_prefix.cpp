@@ -94,16 +94,18 @@ size_t max_slots() {
   return v;
 }
 
-// Workgroups a launch aims for when it splits keys: one per CU of the MI355X (256 CUs).
-// More, shorter spans add merge work without adding bandwidth (measured on the 32-layer
-// decode launch). Env PION_SPLIT_TARGET overrides it for tuning.
-int split_target() {
+// Workgroups a launch aims for when it splits keys. fp16 prefix: two per CU of the
+// MI355X (512): the kernel holds few bytes in flight per wave, and cold-HBM bandwidth
+// needs more waves per CU (measured on the 32-layer decode launch). mlx4g32 prefix: one
+// per CU (256): its workgroups are larger and its merge dearer per span. Env
+// PION_SPLIT_TARGET overrides both for tuning.
+int split_target(bool mlx4) {
   static int v = [] {
     const char *e = getenv("PION_SPLIT_TARGET");
-    int x = e ? atoi(e) : 256;
-    return x > 0 ? x : 256;
+    int x = e ? atoi(e) : 0;
+    return x > 0 ? x : 0;
   }();
-  return v;
+  return v ? v : (mlx4 ? 256 : 512);
 }
 
 bool getenv_flag(const char *name) {
@@ -231,9 +233,9 @@ int pow2_at_least(int n) {
   return R;
 }
 
-int pick_chunk(long long keys, long long work_rows, int granule) {
+int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4) {
   if (keys <= 0) return granule;
-  const long long target = split_target();
+  const long long target = split_target(mlx4);
   long long c = (keys * work_rows + target - 1) / target;
   c = std::max<long long>(c, granule);
   c = (c + granule - 1) / granule * granule;
@@ -363,14 +365,14 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.pre_chunk = c.B;
     pre_max = c.n_sel;
   } else {
-    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64);
+    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64, mlx4);
     pre_max = (N_max + p.pre_chunk - 1) / p.pre_chunk;
   }
   if (c.S_suf > 0) {
     p.Ksuf = c.Ksuf;
     p.Vsuf = c.Vsuf;
     p.S_suf = c.S_suf;
-    p.suf_chunk = pick_chunk(c.S_suf, Y, 64);
+    p.suf_chunk = pick_chunk(c.S_suf, Y, 64, false);
     p.suf_splits = (c.S_suf + p.suf_chunk - 1) / p.suf_chunk;
   }
   p.S_max = pre_max + p.suf_splits;

@@ -31,6 +31,18 @@ __device__ __forceinline__ float h2f(uint16_t u) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16- and 4-byte loads of K/V data that is streamed once per query: the non-temporal
+// hint keeps it from displacing reused lines in the caches (worth ~14% of cold-HBM
+// decode bandwidth).
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+  const nt_u32x4 v = __builtin_nontemporal_load((const nt_u32x4 *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) {
+  return __builtin_nontemporal_load(p);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
