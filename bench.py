@@ -13,7 +13,8 @@ N(0, 1)); all of it is resident in HBM before the timed region starts.
 
 Other workloads, one call per step (for the design notes; the default run is the one
 above): --config 1 tiny dense query; --config 3 fused batched-Q prefill (TFLOP/s);
---config 4 mlx4g32 decode (GB/s of resident codes/scales/biases); --config 5 sparse-auto
+--config 4 mlx4g32 decode, 16 layers per launch (GB/s of resident codes/scales/biases,
+plus the single-query latency); --config 5 sparse-auto
 fused query (us/query).
 
 Timing: wall clock over K steps between device synchronizations; a HIP event pair on
@@ -25,7 +26,7 @@ one launch over that duration.
 Cold memory-side cache: MI355X keeps up to 256 MB of recently used lines in its
 memory-side (infinity) cache. The M=1 workloads therefore rotate over copies of their
 resident data whose total is well above that (config 2: two 32-layer sets, 537 MB;
-config 4: 16 slots, 671 MB; config 5: 4 slots), so each step reads data the previous
+config 4: two sets of 16 layers, 1.34 GB; config 5: 4 slots), so each step reads data the previous
 steps have evicted; `value` is that cold figure. `warm` repeats one set every step and
 is reported beside it, labelled.
 
@@ -301,50 +302,85 @@ def run_prefill(args, torch, kp, synth, dev, stream):
 def run_mlx4(args, torch, kp, synth, dev, stream):
     import oracle
     case = synth.MLX4_DECODE
+    LAYERS, NSET = 16, 2   # 16 layers per step (671 MB); two sets alternate (1.34 GB)
     inp = synth.generate(case)
     sid = "bench-mlx4"
-    NSLOT = 16   # the same quantized prefix in 16 slots (671 MB)
     K16, V16 = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
-    for k in range(NSLOT):
+    for k in range(NSET * LAYERS):   # the same quantized prefix in every layer slot
         kp.pion_prefix_store(sid, k, K16, V16, kp.PION_KV_MLX4G32)
     del K16, V16
-    Q = torch.from_numpy(inp.Q).to(dev)
-    out = torch.empty((case.H_q, 1, case.D), dtype=torch.float32, device=dev)
-    lse = torch.empty((case.H_q, 1), dtype=torch.float32, device=dev)
+    Q1 = torch.from_numpy(inp.Q).to(dev)
+    Q = Q1.unsqueeze(0).expand(LAYERS, -1, -1, -1).contiguous()
+    out = torch.empty((LAYERS, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((LAYERS, case.H_q, 1), dtype=torch.float32, device=dev)
     lib, sidb = kp.lib(), sid.encode()
 
     def make_step(k):
-        a = (sidb, k, case.H_q, case.D, 1, Q.data_ptr(), None, out.data_ptr(), lse.data_ptr())
+        a = (sidb, LAYERS * k, LAYERS, case.H_q, case.D, 1, Q.data_ptr(), None, out.data_ptr(),
+             lse.data_ptr())
+
+        def step():
+            rc = lib.pion_prefix_query_layers(*a, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_prefix_query_layers")
+        return step
+
+    (ms, launch_us), (wms, wlaunch_us) = warm_cold(
+        torch, stream, [make_step(k) for k in range(NSET)], 1, False, args)
+
+    # single M=1 query per launch, rotating over the 32 slots (cold) - latency figure
+    def make_one(k):
+        a = (sidb, k, case.H_q, case.D, 1, Q1.data_ptr(), None, out[0].data_ptr(),
+             lse[0].data_ptr())
 
         def step():
             rc = lib.pion_prefix_query(*a, torch.cuda.current_stream().cuda_stream)
             if rc != 0:
                 raise kp.PionError(rc, "pion_prefix_query")
         return step
+    one_ms, one_us = Timed(torch, stream, [make_one(k) for k in range(NSET * LAYERS)], 1,
+                           False).measure(args.steps, args.warmup)
 
-    (ms, launch_us), (wms, wlaunch_us) = warm_cold(
-        torch, stream, [make_step(k) for k in range(NSLOT)], 1, False, args)
     Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
     Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
-    ref, _ = oracle.prefix_query(inp.Q, Kh, Vh)
-    check_close(out.cpu().numpy(), ref, 2e-3, "out")
-    nbytes = case.H_kv * case.N * 160
+    ref, ref_lse = oracle.prefix_query(inp.Q, Kh, Vh)
+    o = out.cpu().numpy()
+    for l in (0, LAYERS - 1):
+        check_close(o[l], ref, 2e-3, "out")
+    check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 1e-4, "lse")
+    nbytes_layer = case.H_kv * case.N * 160
+    nbytes = nbytes_layer * LAYERS
+    cpu = None
+    if not args.no_cpu_baseline:
+        def one_layer():
+            oracle.prefix_query(inp.Q, Kh, Vh)
+        n, el = cpu_time(one_layer, args.cpu_seconds)
+        cpu = {"value": round(nbytes_layer * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} single-layer M=1 queries of this workload on the dequantized "
+                         f"K/V ({el:.1f} s, fp64 numpy, 1 thread)"}
     kp.pion_prefix_drop(sid, -1)
     return {
         "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
         "dtype": "int4 codes + fp16 scale/bias, fp32 accumulate",
-        "config": {"workload": "mlx4g32 decode H_q=24 H_kv=8 (h//3) D=128 N=32768 M=1",
+        "config": {"workload": "mlx4g32 decode H_q=24 H_kv=8 (h//3) D=128 N=32768 M=1, "
+                               f"{LAYERS} resident layers queried per step",
+                   "entry": "pion_prefix_query_layers", "launches_per_step": 1,
                    "bytes_per_step": nbytes,
-                   "memory_side_cache": f"cold: steps rotate over {NSLOT} slots "
-                                        f"({NSLOT * nbytes / 1e6:.0f} MB)"},
+                   "memory_side_cache": f"cold: steps alternate over {NSET} sets of {LAYERS} "
+                                        f"slots ({NSET * nbytes / 1e6:.0f} MB)"},
         "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
                      "kernel": "mlx4_split_kernel<128,3,2,8>",
-                     "avg_launch_us": launch_us},
+                     "bytes_per_launch": nbytes, "avg_launch_us": launch_us},
         "warm": {"value": round(nbytes / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
                  "avg_launch_us": round(wlaunch_us, 3),
-                 "note": "one slot every step (memory-side cache warm)"},
-        "cpu_baseline": None,
+                 "note": "one set every step (memory-side cache warm)"},
+        "single_query": {"us_per_query": round(one_ms * 1e3, 3),
+                         "GB/s": round(nbytes_layer / (one_ms * 1e-3) / 1e9, 3),
+                         "note": "one M=1 pion_prefix_query per launch over one 41.9 MB "
+                                 "prefix, rotating over 32 slots (cold)"},
+        "cpu_baseline": cpu,
     }
 
 
@@ -471,8 +507,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    if "warm" in r:
-        line["warm"] = r["warm"]
+    for extra in ("warm", "single_query"):
+        if extra in r:
+            line[extra] = r[extra]
     print(json.dumps(line), flush=True)
 
 

@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import os
 import subprocess
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -30,11 +31,18 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *COMMON]
     if src.endswith(".hip"):
-        cmd += DEVICE_ONLY + ["-x", "hip"]
+        # resource remarks: a kernel that spills registers to scratch is reported below
+        cmd += DEVICE_ONLY + ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    spills = [ln for ln in r.stderr.splitlines()
+              if "ScratchSize [bytes/lane]:" in ln and not ln.rstrip().endswith(": 0")
+              and "ScratchSize [bytes/lane]: 0 " not in ln]
+    if spills:
+        print(f"warning: {src}: a kernel spills registers to scratch (slow):\n  "
+              + "\n  ".join(spills), file=sys.stderr)
     return obj
 
 

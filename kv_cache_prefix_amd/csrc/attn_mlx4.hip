@@ -95,7 +95,8 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
   static_assert(U % 2 == 0, "keys are consumed in pairs");
   __shared__ Mlx4Scratch<D, R, NW> sm;
   constexpr int kParts = Mlx4Scratch<D, R, NW>::kParts;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane % NG, kk = lane / NG;
   const int z = blockIdx.z, y = blockIdx.y;
   const Prob b = get_prob(p, z, y);
@@ -107,22 +108,23 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
   Span sp = get_span(p, x, b.pre_splits, b.N, gk, qi);
   if (sp.suffix) sp.j1 = sp.j0;  // suffix spans belong to the fp16 kernel
 
+  // this kv-head's codes and (scale, bias) pairs as buffer ranges: keys past the span
+  // are masked in consume, keys past N read zero
   const KVView kv = make_view(p.kv_base[z], p.fmt, p.H_kv, b.N, D);
   const size_t t0 = (size_t)gk * b.N;
-  const uint4 *Kc = (const uint4 *)(kv.Kc + t0 * (D / 8)) + g;  // token j at [j * NG]
-  const uint4 *Vc = (const uint4 *)(kv.Vc + t0 * (D / 8)) + g;
-  const uint32_t *Ksb = kv.Ksb + t0 * NG + g;
-  const uint32_t *Vsb = kv.Vsb + t0 * NG + g;
+  const __amdgpu_buffer_rsrc_t rKc = make_rsrc(kv.Kc + t0 * (D / 8), (uint32_t)b.N * (D / 2));
+  const __amdgpu_buffer_rsrc_t rVc = make_rsrc(kv.Vc + t0 * (D / 8), (uint32_t)b.N * (D / 2));
+  const __amdgpu_buffer_rsrc_t rKsb = make_rsrc(kv.Ksb + t0 * NG, (uint32_t)b.N * NG * 4);
+  const __amdgpu_buffer_rsrc_t rVsb = make_rsrc(kv.Vsb + t0 * NG, (uint32_t)b.N * NG * 4);
 
   auto load = [&](Mlx4Tile<U> &t, int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = base + u * KPW + kk;
-      const size_t jj = j < sp.j1 ? j : sp.j0;  // in-bounds stand-in, masked in consume
-      t.kc[u] = ld_stream16(Kc + jj * NG);
-      t.vc[u] = ld_stream16(Vc + jj * NG);
-      t.ksb[u] = ld_stream4(Ksb + jj * NG);
-      t.vsb[u] = ld_stream4(Vsb + jj * NG);
+      const uint32_t e = (uint32_t)(base + u * KPW + kk) * NG + g;  // (key, group) index
+      t.kc[u] = bload_stream16(rKc, e * 16);
+      t.vc[u] = bload_stream16(rVc, e * 16);
+      t.ksb[u] = bload_stream4(rKsb, e * 4);
+      t.vsb[u] = bload_stream4(rVsb, e * 4);
     }
   };
 
@@ -174,6 +176,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     for (int e = 0; e < 32; ++e) acc[r][e] = 0.f;
   }
 
+  // keys past the span end (in its last tile) get -inf
   auto consume = [&](const Mlx4Tile<U> &t, int base) {
     float s[U][R];
 #pragma unroll
@@ -207,19 +210,30 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     }
 
     h2_t P[R][U / 2];
+    float mx[R];
+    bool grow = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float mx = s[0][r];
+      mx[r] = s[0][r];
 #pragma unroll
-      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][r]);
-      if (mx > m[r] + kSlack) {
-        const float a = fast_exp2(m[r] - mx);
+      for (int u = 1; u < U; ++u) mx[r] = fmaxf(mx[r], s[u][r]);
+      grow |= mx[r] > m[r] + kSlack;
+    }
+    if (grow) {  // rare after a slot's first tile: rescale the rows whose max moved
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool gr = mx[r] > m[r] + kSlack;
+        const float nm = gr ? mx[r] : m[r];
+        const float a = fast_exp2(m[r] - nm);
         l[r] *= a;
         bs[r] *= a;
 #pragma unroll
         for (int e = 0; e < 32; ++e) acc[r][e] *= a;
-        m[r] = mx;
+        m[r] = nm;
       }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
       float pw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {

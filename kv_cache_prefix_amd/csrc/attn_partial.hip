@@ -62,7 +62,8 @@ template <int D, int R, int LPR>
 __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Scratch<D, R> &sm,
                                        float (&m)[R], float (&l)[R], float (&acc)[R][8],
                                        const uint8_t *heads, int cnt, int qi, int x) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
   WaveState<D, R> &ws = sm.ws;
 #pragma unroll
@@ -121,7 +122,8 @@ template <int D, int R, int U>
 __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   constexpr int LPR = D / 8, KPI = 64 / LPR, STEP = KPI * U;
   __shared__ Scratch<D, R> sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
   const int z = blockIdx.z, y = blockIdx.y;
   const Prob b = get_prob(p, z, y);

@@ -43,10 +43,14 @@ __device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Row-level lane permutation (DPP). Every control used here (quad_perm, row half-mirror,
+// row mirror, row rotate) reads in-range lanes only, so bound_ctrl (zero for an
+// out-of-range source) never applies; it lets the compiler fold the move into the
+// consuming add or max (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 struct Span {
@@ -117,6 +121,16 @@ constexpr int kSC1 = 16;  // buffer cache-policy bit sc1: coherent across the ag
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
+}
+
+// Streaming (non-temporal) buffer loads: bytes past the range read zero.
+constexpr int kNT = 2;  // buffer cache-policy bit nt
+__device__ __forceinline__ uint4 bload_stream16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload_stream4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNT);
 }
 
 struct PartRsrc {
