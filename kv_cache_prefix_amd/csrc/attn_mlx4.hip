@@ -86,6 +86,14 @@ struct Mlx4Tile {
   uint32_t ksb[U], vsb[U];
 };
 
+// a.x*b.x + a.y*b.y with a zero accumulator operand (the three-operand encoding; the
+// accumulating two-operand form the compiler prefers needs a zeroed register first)
+__device__ __forceinline__ float dot2_first(h2_t a, h2_t b) {
+  float d;
+  __asm__("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 __device__ __forceinline__ float lo_f(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
@@ -185,16 +193,19 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
       const uint32_t w4[4] = {t.kc[u].x, t.kc[u].y, t.kc[u].z, t.kc[u].w};
       float dA[R], dB[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) dA[r] = dB[r] = 0.f;
-#pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t x0 = w4[w], x8 = w4[w] >> 8;
         const h2_t c0 = as_h2(x0 & kLo4), c1 = as_h2(x0 & kHi4);
         const h2_t c2 = as_h2(x8 & kLo4), c3 = as_h2(x8 & kHi4);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          dA[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 0], c0, dA[r], false);
-          dB[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 1], c1, dB[r], false);
+          if (w == 0) {
+            dA[r] = dot2_first(q[r][0], c0);
+            dB[r] = dot2_first(q[r][1], c1);
+          } else {
+            dA[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 0], c0, dA[r], false);
+            dB[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 1], c1, dB[r], false);
+          }
           dA[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 2], c2, dA[r], false);
           dB[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 3], c3, dB[r], false);
         }
@@ -273,12 +284,17 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     }
   };
 
+  // two tiles alternate roles (no copy of the prefetched tile)
+  Mlx4Tile<U> nxt;
   while (base < sp.j1) {
-    const int next = base + NW * STEP;
-    Mlx4Tile<U> nxt;
+    int next = base + NW * STEP;
     if (next < sp.j1) load(nxt, next);
     consume(cur, base);
-    cur = nxt;
+    base = next;
+    if (base >= sp.j1) break;
+    next = base + NW * STEP;
+    if (next < sp.j1) load(cur, next);
+    consume(nxt, base);
     base = next;
   }
 
