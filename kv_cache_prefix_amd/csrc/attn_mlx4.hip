@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
   const int hg = y / p.M, qi = y - hg * p.M;
   const int gk = p.rg.g[hg], cnt = p.rg.cnt[hg];
   const uint8_t *heads = p.rg.heads[hg];
-  Span sp = get_span(p, x, b.pre_splits, b.N, gk, qi);
+  Span sp = get_segment(p, x, b.pre_splits, b.N, gk, qi);  // one segment per span here
   if (sp.suffix) sp.j1 = sp.j0;  // suffix spans belong to the fp16 kernel
 
   // this kv-head's codes and (scale, bias) pairs as buffer ranges: keys past the span

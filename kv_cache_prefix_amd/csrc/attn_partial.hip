@@ -105,10 +105,17 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
       a += f * *(const f32x4 *)&ws.acc[w][r][4 * dq];
       lw = __builtin_fmaf(f, ws.l[w][r], lw);
     }
-    store_part(pr, heads[r], x, dq, a);
-    if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+    if (b.S_total == 1) {  // the only span of its rows: final output, no merge
+      const size_t row = (size_t)heads[r] * p.M + qi;
+      const float inv = 1.f / lw;
+      *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+      if (dq == 0 && b.lse) b.lse[row] = (mm + __log2f(lw)) * 0.69314718055994530942f;
+    } else {
+      store_part(pr, heads[r], x, dq, a);
+      if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+    }
   }
-  ticket_and_merge<D, 256>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, 256>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
 }
 
 // One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.
@@ -132,19 +139,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   const int hg = y / p.M, qi = y - hg * p.M;
   const int g = p.rg.g[hg], cnt = p.rg.cnt[hg];
   const uint8_t *heads = p.rg.heads[hg];
-  Span sp = get_span(p, x, b.pre_splits, b.N, g, qi);
-  if (!sp.suffix && p.fmt != 0) sp.j1 = sp.j0;  // an mlx4g32 prefix has its own kernel
-
-  const uint16_t *Kf, *Vf;
-  if (sp.suffix) {
-    Kf = p.Ksuf + (size_t)g * p.S_suf * D;
-    Vf = p.Vsuf + (size_t)g * p.S_suf * D;
-  } else {
-    const KVView kv = make_view(p.kv_base[z], p.fmt, p.H_kv, b.N, D);
-    Kf = kv.K + (size_t)g * b.N * D;
-    Vf = kv.V + (size_t)g * b.N * D;
-  }
-
   // q of each row: this lane's 8 halves
   h2_t q[R][4];
 #pragma unroll
@@ -166,72 +160,88 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
   }
 
-  auto load = [&](Tile<U> &t, int base) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * KPI + kk;
-      t.ok[u] = j < sp.j1;
-      if (t.ok[u]) {
-        t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
-        t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
-      } else {
-        t.k[u] = make_uint4(0, 0, 0, 0);
-        t.v[u] = make_uint4(0, 0, 0, 0);
-      }
+  // the segments of this span, one after another (wave-uniform loop)
+  const int seg0 = x * p.seg_per_span, seg1 = min(seg0 + p.seg_per_span, b.n_seg);
+  for (int sgi = seg0; sgi < seg1; ++sgi) {
+    const Span sp = get_segment(p, sgi, b.pre_splits, b.N, g, qi);
+    if (!sp.suffix && p.fmt != 0) continue;  // an mlx4g32 prefix has its own kernel
+    const uint16_t *Kf, *Vf;
+    if (sp.suffix) {
+      Kf = p.Ksuf + (size_t)g * p.S_suf * D;
+      Vf = p.Vsuf + (size_t)g * p.S_suf * D;
+    } else {
+      const KVView kv = make_view(p.kv_base[z], p.fmt, p.H_kv, b.N, D);
+      Kf = kv.K + (size_t)g * b.N * D;
+      Vf = kv.V + (size_t)g * b.N * D;
     }
-  };
 
-  auto consume = [&](const Tile<U> &t) {
-    float vals[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t w4[4] = {t.v[u].x, t.v[u].y, t.v[u].z, t.v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vals[u][2 * c] = h2f((uint16_t)(w4[c] & 0xffffu));
-        vals[u][2 * c + 1] = h2f((uint16_t)(w4[c] >> 16));
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float s[U];
+    auto load = [&](Tile<U> &t, int base) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float dsum = __builtin_amdgcn_fdot2(q[r][0], as_h2(t.k[u].x), 0.f, false);
-        dsum = __builtin_amdgcn_fdot2(q[r][1], as_h2(t.k[u].y), dsum, false);
-        dsum = __builtin_amdgcn_fdot2(q[r][2], as_h2(t.k[u].z), dsum, false);
-        dsum = __builtin_amdgcn_fdot2(q[r][3], as_h2(t.k[u].w), dsum, false);
-        dsum = group_sum<LPR>(dsum);
-        s[u] = t.ok[u] ? dsum * p.qscale : -INFINITY;
+        const int j = base + u * KPI + kk;
+        t.ok[u] = j < sp.j1;
+        if (t.ok[u]) {
+          t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
+          t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
+        } else {
+          t.k[u] = make_uint4(0, 0, 0, 0);
+          t.v[u] = make_uint4(0, 0, 0, 0);
+        }
       }
-      float mx = m[r];
-#pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
-      const float alpha = fast_exp2(m[r] - mx);
-      l[r] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-      m[r] = mx;
+    };
+
+    auto consume = [&](const Tile<U> &t) {
+      float vals[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float pe = fast_exp2(s[u] - mx);  // masked: 2^-inf = 0
-        l[r] += pe;
+        const uint32_t w4[4] = {t.v[u].x, t.v[u].y, t.v[u].z, t.v[u].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(pe, vals[u][e], acc[r][e]);
+        for (int c = 0; c < 4; ++c) {
+          vals[u][2 * c] = h2f((uint16_t)(w4[c] & 0xffffu));
+          vals[u][2 * c + 1] = h2f((uint16_t)(w4[c] >> 16));
+        }
       }
-    }
-  };
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float dsum = __builtin_amdgcn_fdot2(q[r][0], as_h2(t.k[u].x), 0.f, false);
+          dsum = __builtin_amdgcn_fdot2(q[r][1], as_h2(t.k[u].y), dsum, false);
+          dsum = __builtin_amdgcn_fdot2(q[r][2], as_h2(t.k[u].z), dsum, false);
+          dsum = __builtin_amdgcn_fdot2(q[r][3], as_h2(t.k[u].w), dsum, false);
+          dsum = group_sum<LPR>(dsum);
+          s[u] = t.ok[u] ? dsum * p.qscale : -INFINITY;
+        }
+        float mx = m[r];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
+        const float alpha = fast_exp2(m[r] - mx);
+        l[r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+        m[r] = mx;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pe = fast_exp2(s[u] - mx);  // masked: 2^-inf = 0
+          l[r] += pe;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(pe, vals[u][e], acc[r][e]);
+        }
+      }
+    };
 
-  int base = sp.j0 + wave * STEP;
-  Tile<U> cur;
-  if (base < sp.j1) load(cur, base);
-  while (base < sp.j1) {
-    const int next = base + 4 * STEP;
-    Tile<U> nxt;
-    if (next < sp.j1) load(nxt, next);
-    consume(cur);
-    cur = nxt;
-    base = next;
+    int base = sp.j0 + wave * STEP;
+    Tile<U> cur;
+    if (base < sp.j1) load(cur, base);
+    while (base < sp.j1) {
+      const int next = base + 4 * STEP;
+      Tile<U> nxt;
+      if (next < sp.j1) load(nxt, next);
+      consume(cur);
+      cur = nxt;
+      base = next;
+    }
   }
   finish<D, R, LPR>(p, b, sm, m, l, acc, heads, cnt, qi, x);
 }

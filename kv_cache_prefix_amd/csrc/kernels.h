@@ -90,9 +90,12 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
 // Split-over-keys attention for up to kMaxBatch independent problems (resident slots
 // of identical H, D and format, e.g. the layers of one session) in one launch.
 // Workgroup (x, y, z): z = problem, y = head group * M + query index, x = key span.
-// Spans [0, pre_splits) cover the prefix (dense chunks of pre_chunk tokens, or with
-// `blocks` one selected block each); spans [pre_splits, pre_splits + suf_splits)
-// cover the fp16 suffix in chunks of suf_chunk tokens, clipped to the causal limit.
+// A problem's keys are segments: [0, pre_splits) cover the prefix (dense chunks of
+// pre_chunk tokens, or with `blocks` one selected block each), then suf_splits chunks
+// of suf_chunk suffix tokens clipped to the causal limit. Span x covers segments
+// [x * seg_per_span, (x + 1) * seg_per_span) (seg_per_span is 1 for an mlx4g32 slot,
+// whose prefix and suffix run in separate launches); a problem with a single span
+// writes out and lse directly.
 // Partials (acc unnormalized against m; m and l in log2 units) of problem z go to
 // part_acc + z*part_stride as [M][H_q][S_max][D] and part_m / part_l + z*ml_stride as
 // [M][H_q][S_max] (query index outermost, so the rows of one query index lie within
@@ -116,6 +119,7 @@ struct PartialParams {
   int K_top, B, n_sel;
   const uint16_t *Ksuf, *Vsuf;  // fp16 [H_kv, S_suf, D] (single problem only)
   int S_suf, suf_chunk, suf_splits;
+  int seg_per_span;       // segments per span (>= 1)
   int S_max;              // span stride of the partial layout
   int x_begin;            // span index of this launch's blockIdx.x == 0
   float *part_acc, *part_m, *part_l;
@@ -175,11 +179,11 @@ hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint3
 
 // Block means of K (fp32 [H, nb, D]) for blocks of B tokens.
 hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t s);
-// score [H_kv, nb] = sum over q-heads h of g of q_h . kmean[g, b]
-hipError_t launch_block_score(const uint16_t *Q, const HeadMap &hm, const float *kmean,
-                              int H_kv, int nb, int D, float *score, hipStream_t s);
-// blocks [H_kv, K_top]: best min(K_top, nb) blocks per kv-head, ascending, -1 padded
-hipError_t launch_block_topk(const float *score, int H_kv, int nb, int K_top,
-                             int32_t *blocks, hipStream_t s);
+// blocks [H_kv, K_top]: per kv-head g the best min(K_top, nb) blocks by the score
+// (sum over q-heads h of g of q_h) . kmean[g, b], ascending, -1 padded. keys: scratch
+// [H_kv, nb]; counters[0, H_kv): zero before, left zero.
+hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float *kmean,
+                               int H_kv, int nb, int D, int K_top, uint32_t *keys,
+                               int *counters, int32_t *blocks, hipStream_t s);
 
 }  // namespace pion

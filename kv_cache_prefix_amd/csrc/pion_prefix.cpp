@@ -12,8 +12,8 @@
 // mlx4g32 prefix with an fp16 suffix takes one launch of each) over workgroups (key
 // span, q-head group sharing one kv-head, query index); each writes (acc, m, l) per (row,
 // span) into a per-stream workspace, and the last workgroup of each row group merges
-// them into out and lse. The sparse-auto call runs block_mean (first use per slot and B),
-// block_score and block_topk first, and the split-KV kernel reads the picked block
+// them into out and lse. The sparse-auto call runs block_mean (first use per slot and B)
+// and block_select first, and the split-KV kernel reads the picked block
 // list on the device.
 #include "pion_prefix.h"
 
@@ -108,6 +108,17 @@ int split_target(bool mlx4) {
   return v ? v : (mlx4 ? 256 : 512);
 }
 
+// A row group whose keys fit in this many tile passes of the fp16 kernel (4 waves, each
+// 2048 / D keys per pass) runs as one span: the serial passes cost less than the store,
+// ticket and merge of a split.
+int one_span_keys(int D) {
+  static int iters = [] {
+    const char *e = getenv("PION_ONE_SPAN_ITERS");
+    return e ? std::max(0, atoi(e)) : 3;
+  }();
+  return iters * 4 * (2048 / D);
+}
+
 bool getenv_flag(const char *name) {
   const char *e = getenv(name);
   return e && e[0] && e[0] != '0';
@@ -156,7 +167,7 @@ hipError_t order_after(hipEvent_t ev, hipStream_t src, bool &done, hipStream_t s
 // Per-stream scratch for the split partials, plus the zeroed ticket counters (the
 // merging workgroup resets its counter, so they stay zero between calls). Grows by
 // reallocating after the stream has drained; never shrinks.
-hipError_t get_ws(hipStream_t st, size_t bytes, void **out) {
+hipError_t get_counters(hipStream_t st, int **out) {
   Workspace &w = g_ws[st];
   if (!w.counters) {
     hipError_t e = hipMalloc(&w.counters, kMaxCounters * sizeof(int));
@@ -168,6 +179,14 @@ hipError_t get_ws(hipStream_t st, size_t bytes, void **out) {
       return e;
     }
   }
+  *out = w.counters;
+  return hipSuccess;
+}
+
+hipError_t get_ws(hipStream_t st, size_t bytes, void **out) {
+  Workspace &w = g_ws[st];
+  int *cnt;
+  if (hipError_t e = get_counters(st, &cnt); e != hipSuccess) return e;
   if (w.cap < bytes) {
     if (w.ptr) {
       hipError_t e = hipStreamSynchronize(st);
@@ -394,6 +413,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   hipError_t e;
   if (mlx4) {
     p.x_begin = 0;
+    p.seg_per_span = 1;
     e = launch_partial_mlx4(p, grp_rows, pre_max, st);
     if (e == hipSuccess && p.suf_splits > 0) {
       p.x_begin = pre_max;  // single problem: its prefix spans are exactly pre_max
@@ -401,7 +421,9 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     }
   } else {
     p.x_begin = 0;
-    e = launch_partial(p, R, p.S_max, st);
+    const long long keys = (c.blocks ? (long long)c.n_sel * c.B : N_max) + c.S_suf;
+    p.seg_per_span = keys <= one_span_keys(c.D) ? p.S_max : 1;
+    e = launch_partial(p, R, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
   }
   return e == hipSuccess ? PION_OK : PION_ERR_HIP;
 }
@@ -705,7 +727,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   }
   // score and block buffers: a per-stream allocation separate from the partials'
   // workspace (run_attention may grow and move that one)
-  const size_t score_bytes = align256((size_t)H_kv * nb * sizeof(float));
+  const size_t score_bytes = align256((size_t)H_kv * nb * sizeof(uint32_t));
   const size_t blk_bytes = align256((size_t)H_kv * K_top * sizeof(int32_t));
   Workspace &w = g_sel_ws[st];
   if (w.cap < score_bytes + blk_bytes) {
@@ -722,17 +744,19 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
     }
     w.cap = cap;
   }
-  float *score = (float *)w.ptr;
+  uint32_t *keys = (uint32_t *)w.ptr;
   int32_t *blocks = blocks_out ? blocks_out : (int32_t *)((char *)w.ptr + score_bytes);
 
   HeadMap hmap;
   memset(&hmap, 0, sizeof(hmap));
   hmap.H_q = H_q;
   for (int h = 0; h < H_q; ++h) hmap.m[h] = (uint8_t)hm[h];
-  if (launch_block_score((const uint16_t *)Q, hmap, it->second.ptr, H_kv, nb, D, score, st) !=
-      hipSuccess)
+  // the selection's tickets use the stream's split counters (zero between launches)
+  int *counters;
+  if (get_counters(st, &counters) != hipSuccess) return PION_ERR_NOMEM;
+  if (launch_block_select((const uint16_t *)Q, hmap, it->second.ptr, H_kv, nb, D, K_top,
+                          keys, counters, blocks, st) != hipSuccess)
     return PION_ERR_HIP;
-  if (launch_block_topk(score, H_kv, nb, K_top, blocks, st) != hipSuccess) return PION_ERR_HIP;
 
   AttnCall c{};
   c.Q = (const uint16_t *)Q;

@@ -4,12 +4,11 @@
 //
 //   block_mean : K_mean[g, b, d] = (sum of K[g, j, d] over the tokens j of block b) / n_b,
 //                summed in token order in fp32; one thread per (g, b, d), coalesced over d.
-//   block_score: score[g, b] = sum over q-heads h with head_map[h] == g of q_h . K_mean[g, b];
-//                one wave per (g, b).
-//   block_topk : per kv-head, the min(K_top, nb) best blocks by (score desc, index asc),
-//                found as K_top successive arg-max passes over the scores (each pass
-//                takes the best block ranked strictly after the previous pick), then
-//                written in ascending index order, -1 past nb.
+//   block_select: score[g, b] = sum over q-heads h with head_map[h] == g of q_h . K_mean[g, b],
+//                computed as (sum of those q_h) . K_mean[g, b] (equal in exact arithmetic),
+//                then per kv-head the min(K_top, nb) best blocks by (score desc, index asc),
+//                written in ascending index order, -1 past nb. One launch: the
+//                workgroups score, the last one of each kv-head selects.
 // The arithmetic of a block depends only on its own data, so identical blocks get
 // identical scores and the lower index wins the tie.
 #include "kernels.h"
@@ -47,96 +46,208 @@ __global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int n
   }
 }
 
-__global__ __launch_bounds__(256) void block_score_kernel(const uint16_t *__restrict__ Q,
-                                                          HeadMap hm,
-                                                          const float *__restrict__ kmean,
-                                                          int nb, int D,
-                                                          float *__restrict__ score) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x * 4 + wave, g = blockIdx.y;
-  if (b >= nb) return;
-  const float *km = kmean + ((size_t)g * nb + b) * D;
-  float acc = 0.f;
-  for (int h = 0; h < hm.H_q; ++h) {
-    if (hm.m[h] != g) continue;
-    float dot = 0.f;
-    for (int d = lane; d < D; d += 64) dot = __builtin_fmaf(h2f(Q[(size_t)h * D + d]), km[d], dot);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) dot += __shfl_xor(dot, o);
-    acc += dot;
-  }
-  if (lane == 0) score[(size_t)g * nb + b] = acc;
+// Order-preserving key of a score: a larger score gets a larger key, -0 counts as +0,
+// and NaN gets 0, below every other score.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) return 0u;
+  uint32_t u = __builtin_bit_cast(uint32_t, s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// (score, index) ordering: a ranks before b.
-__device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
-}
+constexpr int kSelBlocks = 64;  // blocks scored per workgroup
+constexpr int kSelE = 16;       // keys per thread per chunk of the selection
 
-constexpr int kMaxTop = 1024;
+// Score phase, one workgroup per kSelBlocks blocks of one kv-head g: each block's score
+// is qsum . K_mean[g, b] with qsum the fp32 sum of the q-heads mapped to g (in head
+// order), the dot summed by a fixed lane tree so that a score depends only on the
+// block's own data. Scores are written as keys (agent-coherent stores); the last
+// workgroup of g (ticket on counters[g]) selects:
+//   radix select, 8 bits a pass from the top, finds the key T of the K-th best block
+//   (K = min(K_top, nb)) and how many blocks with key T are still needed; then one
+//   scan in block order places each chosen block at
+//     (blocks with key > T before it) + min(blocks with key T before it, need),
+//   which is ascending index order with ties going to the lower index.
+template <int D>
+__global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__restrict__ Q,
+                                                           HeadMap hm,
+                                                           const float *__restrict__ kmean,
+                                                           int nb, int K_top, uint32_t *keys,
+                                                           int *counters,
+                                                           int32_t *__restrict__ blocks) {
+  constexpr int LPB = D / 4 < 64 ? D / 4 : 64;  // lanes per block row
+  constexpr int F = D / (4 * LPB);              // float4 per lane
+  constexpr int RPL = 64 / LPB;                 // block rows per wave load
+  constexpr int NL = kSelBlocks / 4 / RPL;      // wave loads
+  __shared__ float qsum[D];
+  __shared__ int hist[256];
+  __shared__ int wsum[4][2];
+  __shared__ uint32_t st_prefix;
+  __shared__ int st_need, st_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.y;
+  uint32_t *kg = keys + (size_t)g * nb;
 
-__global__ __launch_bounds__(256) void block_topk_kernel(const float *__restrict__ score,
-                                                         int nb, int K_top,
-                                                         int32_t *__restrict__ blocks) {
-  __shared__ int picked[kMaxTop];
-  __shared__ float red_s[4];
-  __shared__ int red_i[4];
-  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float *sc = score + (size_t)g * nb;
-  const int n_sel = min(K_top, nb);
-  float last_s = INFINITY;
-  int last_i = -1;
-  int found = 0;
-  for (int k = 0; k < n_sel; ++k) {
-    float bs = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int b = tid; b < nb; b += 256) {
-      const float s = sc[b];
-      // candidates rank strictly after the previous pick
-      if (ranks_before(last_s, last_i, s, b) && ranks_before(s, b, bs, bi)) {
-        bs = s;
-        bi = b;
-      }
+  for (int d = tid; d < D; d += 256) {
+    float a = 0.f;
+#pragma unroll 8
+    for (int h = 0; h < hm.H_q; ++h) {
+      const float v = h2f(Q[(size_t)h * D + d]);
+      if (hm.m[h] == g) a += v;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float os = __shfl_xor(bs, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ranks_before(os, oi, bs, bi)) {
-        bs = os;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      red_s[wave] = bs;
-      red_i[wave] = bi;
-    }
-    __syncthreads();
-    bs = red_s[0];
-    bi = red_i[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (ranks_before(red_s[w], red_i[w], bs, bi)) {
-        bs = red_s[w];
-        bi = red_i[w];
-      }
-    __syncthreads();
-    if (bi == 0x7fffffff) break;  // nothing left (only with non-finite scores)
-    if (tid == 0) picked[k] = bi;
-    last_s = bs;
-    last_i = bi;
-    found = k + 1;
+    qsum[d] = a;
   }
   __syncthreads();
-  // ascending order: the rank of a pick among distinct picks is its output slot
-  int32_t *out = blocks + (size_t)g * K_top;
-  for (int k = tid; k < found; k += 256) {
-    const int v = picked[k];
-    int rank = 0;
-    for (int j = 0; j < found; ++j) rank += picked[j] < v;
-    out[rank] = v;
+
+  {
+    const int sub = lane % LPB, rl = lane / LPB;
+    float4 qv[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) qv[f] = *(const float4 *)&qsum[4 * (sub + f * LPB)];
+    const int b0 = blockIdx.x * kSelBlocks + wave * (kSelBlocks / 4) + rl;
+    float4 kv[NL][F];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int b = b0 + i * RPL;
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+        kv[i][f] = b < nb ? *(const float4 *)(kmean + ((size_t)g * nb + b) * D + 4 * (sub + f * LPB))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        s = __builtin_fmaf(qv[f].x, kv[i][f].x, s);
+        s = __builtin_fmaf(qv[f].y, kv[i][f].y, s);
+        s = __builtin_fmaf(qv[f].z, kv[i][f].z, s);
+        s = __builtin_fmaf(qv[f].w, kv[i][f].w, s);
+      }
+#pragma unroll
+      for (int o = 1; o < LPB; o <<= 1) s += __shfl_xor(s, o);
+      const int b = b0 + i * RPL;
+      if (sub == 0 && b < nb)
+        __hip_atomic_store(kg + b, score_key(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  for (int k = found + tid; k < K_top; k += 256) out[k] = -1;
+
+  // this wave's key stores have completed before the barrier and the ticket
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    st_last = __hip_atomic_fetch_add(counters + g, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!st_last) return;
+
+  const int K = min(K_top, nb);
+  constexpr int CH = 256 * kSelE;
+  uint32_t kr[kSelE];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int i = c0 + tid * kSelE + e;
+      kr[e] = i < nb ? __hip_atomic_load(kg + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+  };
+  const bool one = nb <= CH;
+  if (one) load_chunk(0);
+
+  uint32_t prefix = 0;
+  int need = K;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : 0xFFFFFFFFu << (shift + 8);
+    hist[tid] = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < nb; c0 += CH) {
+      if (!one) load_chunk(c0);
+#pragma unroll
+      for (int e = 0; e < kSelE; ++e) {
+        const int i = c0 + tid * kSelE + e;
+        if (i < nb && (kr[e] & hmask) == prefix) atomicAdd(&hist[(kr[e] >> shift) & 255u], 1);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // digits in descending order: lane l holds 255 - 4l ... 252 - 4l
+      int c[4], loc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = hist[255 - 4 * lane - i];
+        loc += c[i];
+      }
+      int inc = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+      }
+      int before = inc - loc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (before < need && need <= before + c[i]) {
+          st_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+          st_need = need - before;
+        }
+        before += c[i];
+      }
+    }
+    __syncthreads();
+    prefix = st_prefix;
+    need = st_need;
+  }
+
+  const uint32_t T = prefix;
+  int32_t *out = blocks + (size_t)g * K_top;
+  int gt_run = 0, eq_run = 0;
+  for (int c0 = 0; c0 < nb; c0 += CH) {
+    if (!one) load_chunk(c0);
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int i = c0 + tid * kSelE + e;
+      if (i < nb) {
+        ngt += kr[e] > T;
+        neq += kr[e] == T;
+      }
+    }
+    int igt = ngt, ieq = neq;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(igt, o), b = __shfl_up(ieq, o);
+      if (lane >= o) {
+        igt += a;
+        ieq += b;
+      }
+    }
+    if (lane == 63) {
+      wsum[wave][0] = igt;
+      wsum[wave][1] = ieq;
+    }
+    __syncthreads();
+    int gb = gt_run + igt - ngt, eb = eq_run + ieq - neq;
+    for (int w = 0; w < wave; ++w) {
+      gb += wsum[w][0];
+      eb += wsum[w][1];
+    }
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int i = c0 + tid * kSelE + e;
+      if (i < nb) {
+        const bool gt = kr[e] > T, eq = kr[e] == T;
+        if (gt || (eq && eb < need)) out[gb + min(eb, need)] = i;
+        gb += gt;
+        eb += eq;
+      }
+    }
+    gt_run += wsum[0][0] + wsum[1][0] + wsum[2][0] + wsum[3][0];
+    eq_run += wsum[0][1] + wsum[1][1] + wsum[2][1] + wsum[3][1];
+    __syncthreads();
+  }
+  for (int k = K + tid; k < K_top; k += 256) out[k] = -1;
+  if (tid == 0) __hip_atomic_store(counters + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -152,17 +263,27 @@ hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_block_score(const uint16_t *Q, const HeadMap &hm, const float *kmean,
-                              int H_kv, int nb, int D, float *score, hipStream_t s) {
-  dim3 grid((nb + 3) / 4, H_kv);
-  hipLaunchKernelGGL(block_score_kernel, grid, dim3(256), 0, s, Q, hm, kmean, nb, D, score);
-  return hipGetLastError();
-}
-
-hipError_t launch_block_topk(const float *score, int H_kv, int nb, int K_top, int32_t *blocks,
-                             hipStream_t s) {
-  if (K_top > kMaxTop || K_top < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(block_topk_kernel, dim3(H_kv), dim3(256), 0, s, score, nb, K_top, blocks);
+hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float *kmean,
+                               int H_kv, int nb, int D, int K_top, uint32_t *keys,
+                               int *counters, int32_t *blocks, hipStream_t s) {
+  if (K_top < 1 || nb < 1 || H_kv < 1) return hipErrorInvalidValue;
+  dim3 grid((nb + kSelBlocks - 1) / kSelBlocks, H_kv);
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
+                         keys, counters, blocks);
+      break;
+    case 128:
+      hipLaunchKernelGGL(block_select_kernel<128>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
+                         keys, counters, blocks);
+      break;
+    case 256:
+      hipLaunchKernelGGL(block_select_kernel<256>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
+                         keys, counters, blocks);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -53,15 +53,19 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// A segment is one contiguous key range: a prefix chunk of pre_chunk tokens (or, with
+// `blocks`, one selected block), or a suffix chunk of suf_chunk tokens clipped to the
+// causal limit of query index qi. Span x of a problem covers segments
+// [x * seg_per_span, (x + 1) * seg_per_span).
 struct Span {
   int j0, j1;
   bool suffix;
 };
 
-__device__ __forceinline__ Span get_span(const PartialParams &p, int x, int pre_splits, int N,
-                                         int g, int qi) {
+__device__ __forceinline__ Span get_segment(const PartialParams &p, int x, int pre_segs, int N,
+                                            int g, int qi) {
   Span s;
-  if (x < pre_splits) {
+  if (x < pre_segs) {
     s.suffix = false;
     if (p.blocks) {
       const int nb = (N + p.B - 1) / p.B;
@@ -78,7 +82,7 @@ __device__ __forceinline__ Span get_span(const PartialParams &p, int x, int pre_
     }
   } else {
     s.suffix = true;
-    const int c = x - pre_splits;
+    const int c = x - pre_segs;
     const int lim = p.S_suf - p.M + qi + 1;  // causal, bottom-right aligned
     s.j0 = c * p.suf_chunk;
     s.j1 = min(min(s.j0 + p.suf_chunk, p.S_suf), lim);
@@ -88,7 +92,7 @@ __device__ __forceinline__ Span get_span(const PartialParams &p, int x, int pre_
 
 // Per-problem pointers of this workgroup.
 struct Prob {
-  int N, pre_splits, S_total;
+  int N, pre_splits, n_seg, S_total;  // pre_splits: prefix segments
   const uint16_t *Q;
   float *out, *lse, *part_acc, *part_m, *part_l;
   int *counter;
@@ -98,7 +102,8 @@ __device__ __forceinline__ Prob get_prob(const PartialParams &p, int z, int y) {
   Prob b;
   b.N = p.N[z];
   b.pre_splits = p.blocks ? p.n_sel : (b.N + p.pre_chunk - 1) / p.pre_chunk;
-  b.S_total = b.pre_splits + p.suf_splits;
+  b.n_seg = b.pre_splits + p.suf_splits;
+  b.S_total = (b.n_seg + p.seg_per_span - 1) / p.seg_per_span;
   b.Q = p.Q + z * p.q_stride;
   b.out = p.out + z * p.out_stride;
   b.lse = p.lse ? p.lse + z * p.lse_stride : nullptr;
