@@ -55,6 +55,19 @@ constexpr int kMaxPrefillSplits = 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The value of lane l ^ 32, through the cross-half lane swap (no LDS round trip): the
+// swap leaves lane l holding x[l % 32] in one result and x[l % 32 + 32] in the other.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 
 constexpr int NSTAGE = 2;  // LDS tile stages (loads run NSTAGE - 1 tiles ahead)
 
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       float mt = -INFINITY;  // raw-score max; the scale is positive
 #pragma unroll
       for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.qscale;
+      mt = max_xor32(mt) * p.qscale;
       const bool grow = mt > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rare after the first tiles
         const float m_new = grow ? mt : m_run;
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     if constexpr (NSTAGE > 2)
       if (j + 2 < n_tiles) run_tile(std::integral_constant<int, 2>(), j + 2);
   }
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_xor32(l_run);
 
   const bool row_ok = qi < p.M;
   const size_t row = (size_t)h * p.M + qi_c;
