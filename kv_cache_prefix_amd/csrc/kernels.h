@@ -146,8 +146,10 @@ hipError_t launch_partial_mlx4(const PartialParams &p, int rows_per_group, int x
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
 // causal suffix (bottom-right aligned). A workgroup serves (tile, split): tile = (q-head,
 // block of 128 query rows), split = a range of split_keys tokens of the concatenated key
-// index [0, N + S_suf). With n_splits > 1 the splits' partials ([H_q*M][n_splits][D] and
-// [H_q*M][n_splits]) merge in the last-arriving workgroup of each tile (counters[tile]).
+// index [0, N + S_suf). With n_splits > 1 the splits' partials (acc: [tile][n_splits]
+// [128 * D] in the kernel's register layout; m, l: [H_q*M][n_splits]) merge in the workgroup that draws the last ticket of each tile
+// (counters[tile]) once done[tile] counts the others' stores; both are zero before a
+// launch and left zero.
 // The 1-D grid is ordered so that the workgroups of one kv-head share an XCD:
 // order[] lists the q-heads grouped by kv-head.
 struct PrefillParams {
@@ -160,7 +162,7 @@ struct PrefillParams {
   int n_splits, split_keys;       // split_keys a multiple of 64
   float *out, *lse;
   float *part_acc, *part_m, *part_l;
-  int *counters;
+  int *counters, *done;           // per tile
   HeadMap hm;
   uint8_t order[kMaxHeads];       // q-heads sorted by kv-head
 };

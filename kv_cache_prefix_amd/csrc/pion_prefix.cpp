@@ -299,7 +299,7 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
   p.n_iblk = (c.M + 127) / 128;
   const long long tiles = (long long)c.H_q * p.n_iblk;
-  if (tiles > kMaxCounters) return PION_ERR_UNSUPPORTED;
+  if (tiles > kMaxCounters / 2) return PION_ERR_UNSUPPORTED;  // ticket and done counters
   const long long total = (long long)sl.N + c.S_suf;
   // splits: up to about 1.5 workgroups per CU over the row blocks (two fit on a CU for
   // D <= 128, one for D = 256); each split adds a partial round trip and merge work.
@@ -325,7 +325,8 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   }
   if (p.n_splits > 1) {
     const size_t rows = (size_t)c.H_q * c.M;
-    const size_t acc_bytes = align256(rows * p.n_splits * c.D * sizeof(float));
+    // acc partials per (tile, split): 128 rows x D in the kernel's register layout
+    const size_t acc_bytes = align256((size_t)tiles * 128 * p.n_splits * c.D * sizeof(float));
     const size_t ml_bytes = align256(rows * p.n_splits * sizeof(float));
     void *ws = nullptr;
     if (get_ws(st, acc_bytes + 2 * ml_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
@@ -333,6 +334,7 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
     p.part_m = (float *)((char *)ws + acc_bytes);
     p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
     p.counters = g_ws[st].counters;
+    p.done = g_ws[st].counters + kMaxCounters / 2;
   }
   return launch_prefill(p, st) == hipSuccess ? PION_OK : PION_ERR_HIP;
 }

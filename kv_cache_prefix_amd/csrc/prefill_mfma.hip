@@ -30,8 +30,9 @@
 // would wait for every outstanding one before any LDS read; the loads are issued
 // through inline assembly instead and the kernel waits for them itself (s_waitcnt
 // vmcnt, then a barrier) before a stage is read.
-// Splits of the key range run in different workgroups; the last one of a row block
-// merges their (acc, m, l) partials with the LSE rule, as in the split-KV decode kernel.
+// Splits of the key range run in different workgroups; the one that draws the last
+// ticket of a row block merges the others' (acc, m, l) partials into its own with the
+// LSE rule.
 #include "kernels.h"
 
 #include <type_traits>
@@ -368,27 +369,44 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     return;
   }
 
-  // Split partial (acc unnormalized against m_run; m and l in log2 units) in the
-  // split-KV layout [row][split][D], written with agent-coherent (sc1) 16-byte stores
-  // through a buffer range that covers only this block's valid rows.
+  // Split partial: acc unnormalized against m_run, in the register layout of o (tile,
+  // split, wave, 32-dim block db, quad i, lane: one 16-byte piece per lane, so every
+  // store and load instruction moves 1 KB of consecutive bytes); m and l (log2 units)
+  // per [row][split]. Written and read with agent-coherent (sc1) accesses.
+  //
+  // Order: every workgroup of the tile first takes a ticket; the one that draws the
+  // last ticket merges, all others store their partial and then count it in done[tile].
+  // The merging workgroup keeps its own partial in registers and waits (bounded) until
+  // the other n_splits - 1 are counted; those workgroups are already past their loops,
+  // so the wait only covers their stores.
   const int S = p.n_splits;
   const int rows_valid = min(BQ, p.M - i0);
   const size_t row0 = (size_t)h * p.M + i0;
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.part_acc + row0 * S * D, (uint32_t)(rows_valid * S * D * 4));
+      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
+  // byte offset of (split c, 32-dim block db, quad i) for this lane
+  auto aoff = [&](int c, int db, int i) { return ((((c * 4 + wave) * NDB + db) * 4 + i) * 64 + lane) * 16; };
   const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
-  constexpr int SC1 = 16;  // cache policy: system coherent
-  {
-    const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
+  constexpr int SC1 = 16;  // cache policy: device coherent
+  const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
+  // (for D > 128 the registers cannot hold o through the merge: the merging workgroup
+  // stores its partial too and merges all splits from memory)
+  constexpr bool REG = D <= 128;
+  __syncthreads();
+  if (tid == 0)
+    sm.last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+  __syncthreads();
+  const bool last = sm.last;
+  if (!last || !REG) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4, v), rA,
-            (int)(((r * S + split) * D + 32 * db + 8 * i + 4 * hl) * 4), 0, SC1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
+                                               aoff(split, db, i), 0, SC1);
       }
     if (hl == 0) {
       const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
@@ -397,35 +415,47 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL,
                                             (r * S + split) * 4, 0, SC1);
     }
+    // this wave's stores have completed before the barrier and the count
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!last) {
+      if (tid == 0)
+        __hip_atomic_fetch_add(p.done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
   }
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   if (tid == 0) {
-    const int t = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = (t == S - 1);
+    // bounded: ends after about a second even if a count never arrives
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+      if (__hip_atomic_load(p.done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S - 1)
+        break;
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
   __syncthreads();
-  if (!sm.last) return;
 
-  // Merge, in three phases with the loads of a phase issued together:
-  // (1) m and l of all (row, split) into LDS; (2) per row the weights 2^(m_c - m*) and
-  // 1 / sum_c w_c l_c, and lse; (3) out = sum_c w_c acc_c / L in 16-byte pieces, CB
-  // splits per round (up to 16 pieces in flight per thread).
-  for (int x0 = 0; x0 < rows_valid * S; x0 += 4 * 256) {
-    constexpr int ML = 4;
+  // Merge. (1) m and l of every (row, split) into LDS, this split's from registers;
+  // (2) per row the weights 2^(m_c - m*), 1 / sum_c w_c l_c and lse; (3) in the MFMA
+  // layout of o: out = (w_self o + sum over the other splits of w_c acc_c) / L.
+  constexpr int OWN_REG = REG ? 1 : 0;  // this split's m, l and acc come from registers
+  if (REG && hl == 0 && r < rows_valid) {
+    sm.mg.w[r * S + split] = l_run > 0.f ? m_run : -INFINITY;
+    sm.mg.l[r * S + split] = l_run;
+  }
+  for (int x0 = 0; x0 < rows_valid * S; x0 += (D <= 128 ? 4 : 1) * 256) {
+    constexpr int ML = D <= 128 ? 4 : 1;
     float mv[ML], lv[ML];
 #pragma unroll
     for (int k = 0; k < ML; ++k) {
       const int x = x0 + tid + 256 * k;
-      const bool in = x < rows_valid * S;
+      const bool in = x < rows_valid * S && !(OWN_REG && x % S == split);
       mv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, x * 4, 0, SC1)) : 0.f;
       lv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, x * 4, 0, SC1)) : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < ML; ++k) {
       const int x = x0 + tid + 256 * k;
-      if (x < rows_valid * S) {
+      if (x < rows_valid * S && !(OWN_REG && x % S == split)) {
         sm.mg.w[x] = mv[k];
         sm.mg.l[x] = lv[k];
       }
@@ -445,48 +475,60 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     if (p.lse) p.lse[row0 + tid] = (M + __log2f(L)) * 0.69314718055994530942f;
   }
   __syncthreads();
-  constexpr int Q4 = D / 4;                  // 16-byte pieces per row
-  constexpr int ITER = BQ * Q4 / 256;        // pieces per thread
-  constexpr int CB = ITER >= 16 ? 1 : 16 / ITER;  // splits per round
-  float4 acc[ITER];
+  const int rr = r < rows_valid ? r : 0;  // rows past the end read row 0's weights
+  {
+    const float ws = REG ? sm.mg.w[rr * S + split] : 0.f;
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) acc[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = REG ? o[db][e] * ws : 0.f;
+  }
+  // one round: DBC 32-dim blocks of CB splits (register budget)
+  constexpr int CB = D <= 64 ? 2 : 1, DBC = D <= 128 ? NDB : 2;
   for (int c0 = 0; c0 < S; c0 += CB) {
-    f32x4 v[CB][ITER];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int c = c0 + cb < S ? c0 + cb : c0;  // a past-the-end split repeats c0, weight 0
+    for (int d0 = 0; d0 < NDB; d0 += DBC) {
+      f32x4 v[CB][DBC][4];
 #pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
-        v[cb][it] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, ((r * S + c) * D + 4 * d4) * 4, 0, SC1));
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = c0 + cb;
+        const bool skip = (REG && c == split) || c >= S;  // nothing to add
+#pragma unroll
+        for (int db = 0; db < DBC; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[cb][db][i] = skip ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                      rA, aoff(c, d0 + db, i), 0, SC1));
       }
-    }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      if (c0 + cb >= S) break;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = c0 + cb;
+        const float w = ((REG && c == split) || c >= S) ? 0.f : sm.mg.w[rr * S + c];
 #pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int q = tid + 256 * it, r = q / Q4;
-        const float w = r < rows_valid ? sm.mg.w[r * S + c0 + cb] : 0.f;
-        acc[it].x = __builtin_fmaf(w, v[cb][it].x, acc[it].x);
-        acc[it].y = __builtin_fmaf(w, v[cb][it].y, acc[it].y);
-        acc[it].z = __builtin_fmaf(w, v[cb][it].z, acc[it].z);
-        acc[it].w = __builtin_fmaf(w, v[cb][it].w, acc[it].w);
+        for (int db = 0; db < DBC; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              o[d0 + db][4 * i + jj] = __builtin_fmaf(w, v[cb][db][i][jj], o[d0 + db][4 * i + jj]);
       }
     }
   }
+  if (r < rows_valid) {
+    const float inv = sm.mg.inv[r];
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int q = tid + 256 * it, r = q / Q4, d4 = q - r * Q4;
-    if (r < rows_valid) {
-      const float inv = sm.mg.inv[r];
-      *(float4 *)(p.out + (row0 + r) * D + 4 * d4) =
-          make_float4(acc[it].x * inv, acc[it].y * inv, acc[it].z * inv, acc[it].w * inv);
-    }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(float4 *)(p.out + (row0 + r) * D + 32 * db + 8 * i + 4 * hl) =
+            make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                        o[db][4 * i + 3] * inv);
   }
-  if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.done + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 }  // namespace
