@@ -37,11 +37,11 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    # vector registers spilled to scratch memory (scalar spills go to vector lanes)
     spills = [ln for ln in r.stderr.splitlines()
-              if "ScratchSize [bytes/lane]:" in ln and not ln.rstrip().endswith(": 0")
-              and "ScratchSize [bytes/lane]: 0 " not in ln]
+              if "VGPRs Spill:" in ln and "VGPRs Spill: 0 " not in ln]
     if spills:
-        print(f"warning: {src}: a kernel spills registers to scratch (slow):\n  "
+        print(f"warning: {src}: a kernel spills vector registers to scratch (slow):\n  "
               + "\n  ".join(spills), file=sys.stderr)
     return obj
 
