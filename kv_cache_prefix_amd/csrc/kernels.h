@@ -179,13 +179,4 @@ hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint3
                                    uint16_t *scales, uint16_t *biases, int sb_stride,
                                    hipStream_t s);
 
-// Block means of K (fp32 [H, nb, D]) for blocks of B tokens.
-hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t s);
-// blocks [H_kv, K_top]: per kv-head g the best min(K_top, nb) blocks by the score
-// (sum over q-heads h of g of q_h) . kmean[g, b], ascending, -1 padded. keys: scratch
-// [H_kv, nb]; counters[0, H_kv): zero before, left zero.
-hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float *kmean,
-                               int H_kv, int nb, int D, int K_top, uint32_t *keys,
-                               int *counters, int32_t *blocks, hipStream_t s);
-
 }  // namespace pion

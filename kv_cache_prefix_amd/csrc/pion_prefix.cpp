@@ -30,6 +30,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "sparse.h"
 
 namespace {
 
@@ -730,16 +731,18 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   // score and block buffers: a per-stream allocation separate from the partials'
   // workspace (run_attention may grow and move that one)
   const size_t score_bytes = align256((size_t)H_kv * nb * sizeof(uint32_t));
+  const size_t cand_bytes =
+      align256((size_t)H_kv * ((nb + 63) / 64) * std::min(K_top, 64) * sizeof(uint64_t));
   const size_t blk_bytes = align256((size_t)H_kv * K_top * sizeof(int32_t));
   Workspace &w = g_sel_ws[st];
-  if (w.cap < score_bytes + blk_bytes) {
+  if (w.cap < score_bytes + cand_bytes + blk_bytes) {
     if (w.ptr) {
       if (hipStreamSynchronize(st) != hipSuccess) return PION_ERR_HIP;
       (void)hipFree(w.ptr);
       w.ptr = nullptr;
       w.cap = 0;
     }
-    const size_t cap = align256(score_bytes + blk_bytes + (1 << 16));
+    const size_t cap = align256(score_bytes + cand_bytes + blk_bytes + (1 << 16));
     if (hipMalloc(&w.ptr, cap) != hipSuccess) {
       (void)hipGetLastError();
       return PION_ERR_NOMEM;
@@ -747,7 +750,9 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
     w.cap = cap;
   }
   uint32_t *keys = (uint32_t *)w.ptr;
-  int32_t *blocks = blocks_out ? blocks_out : (int32_t *)((char *)w.ptr + score_bytes);
+  uint64_t *cand = (uint64_t *)((char *)w.ptr + score_bytes);
+  int32_t *blocks =
+      blocks_out ? blocks_out : (int32_t *)((char *)w.ptr + score_bytes + cand_bytes);
 
   HeadMap hmap;
   memset(&hmap, 0, sizeof(hmap));
@@ -757,7 +762,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   int *counters;
   if (get_counters(st, &counters) != hipSuccess) return PION_ERR_NOMEM;
   if (launch_block_select((const uint16_t *)Q, hmap, it->second.ptr, H_kv, nb, D, K_top,
-                          keys, counters, blocks, st) != hipSuccess)
+                          keys, cand, counters, blocks, st) != hipSuccess)
     return PION_ERR_HIP;
 
   AttnCall c{};

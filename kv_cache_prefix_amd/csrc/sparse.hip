@@ -11,7 +11,7 @@
 //                workgroups score, the last one of each kv-head selects.
 // The arithmetic of a block depends only on its own data, so identical blocks get
 // identical scores and the lower index wins the tie.
-#include "kernels.h"
+#include "sparse.h"
 
 namespace pion {
 namespace {
@@ -46,6 +46,33 @@ __global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int n
   }
 }
 
+// Lane moves without LDS: DPP within rows of 16 lanes, swaps across rows (gfx950).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+__device__ __forceinline__ float add_swapped(float v, bool by32) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// Sum over each aligned group of W lanes (W = 16, 32 or 64), in every lane of the group:
+// quad sums, row half-mirror and row mirror give the 16-lane sum; the row swaps pair
+// rows 16 and 32 apart. Every group adds in the same order, so a group's result depends
+// only on its own values.
+template <int W>
+__device__ __forceinline__ float lane_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  if constexpr (W >= 32) v = add_swapped(v, false);
+  if constexpr (W >= 64) v = add_swapped(v, true);
+  return v;
+}
+
 // Order-preserving key of a score: a larger score gets a larger key, -0 counts as +0,
 // and NaN gets 0, below every other score.
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -57,15 +84,21 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 constexpr int kSelBlocks = 64;  // blocks scored per workgroup
 constexpr int kSelE = 16;       // keys per thread per chunk of the selection
+constexpr int kSelCand = 512;   // candidate merge: at most this many candidates
 
 // Score phase, one workgroup per kSelBlocks blocks of one kv-head g: each block's score
 // is qsum . K_mean[g, b] with qsum the fp32 sum of the q-heads mapped to g (in head
 // order), the dot summed by a fixed lane tree so that a score depends only on the
 // block's own data. Scores are written as keys (agent-coherent stores); the last
 // workgroup of g (ticket on counters[g]) selects:
-//   radix select, 8 bits a pass from the top, finds the key T of the K-th best block
-//   (K = min(K_top, nb)) and how many blocks with key T are still needed; then one
-//   scan in block order places each chosen block at
+//   candidate merge (K_top <= 64 and few candidates): each workgroup also ranks its own
+//   blocks by (key desc, index asc) and stores its best min(K, blocks) as 64-bit
+//   composites key << 32 | ~index (larger is better); the last workgroup ranks every
+//   candidate among all of them (the global best K are among the candidates) and
+//   writes the chosen blocks in ascending index order;
+//   otherwise radix select, 8 bits a pass from the top, finds the key T of the K-th
+//   best block (K = min(K_top, nb)) and how many blocks with key T are still needed;
+//   then one scan in block order places each chosen block at
 //     (blocks with key > T before it) + min(blocks with key T before it, need),
 //   which is ascending index order with ties going to the lower index.
 template <int D>
@@ -73,7 +106,7 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
                                                            HeadMap hm,
                                                            const float *__restrict__ kmean,
                                                            int nb, int K_top, uint32_t *keys,
-                                                           int *counters,
+                                                           uint64_t *cand, int *counters,
                                                            int32_t *__restrict__ blocks) {
   constexpr int LPB = D / 4 < 64 ? D / 4 : 64;  // lanes per block row
   constexpr int F = D / (4 * LPB);              // float4 per lane
@@ -84,9 +117,17 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
   __shared__ int wsum[4][2];
   __shared__ uint32_t st_prefix;
   __shared__ int st_need, st_last;
+  __shared__ uint32_t wkey[kSelBlocks];
+  __shared__ int wrank[4][kSelBlocks];
+  __shared__ uint64_t cx[kSelCand];
+  __shared__ uint32_t sel[kSelBlocks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.y;
   uint32_t *kg = keys + (size_t)g * nb;
+  const int K = min(K_top, nb);
+  const int KC = min(K_top, kSelBlocks);  // candidate slots per workgroup
+  const bool fast = K_top <= kSelBlocks && (int)gridDim.x * KC <= kSelCand;
+  const int w0 = blockIdx.x * kSelBlocks, nv = min(kSelBlocks, nb - w0);
 
   for (int d = tid; d < D; d += 256) {
     float a = 0.f;
@@ -124,11 +165,34 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
         s = __builtin_fmaf(qv[f].z, kv[i][f].z, s);
         s = __builtin_fmaf(qv[f].w, kv[i][f].w, s);
       }
-#pragma unroll
-      for (int o = 1; o < LPB; o <<= 1) s += __shfl_xor(s, o);
+      s = lane_sum<LPB>(s);
       const int b = b0 + i * RPL;
-      if (sub == 0 && b < nb)
+      if (sub == 0 && b < nb) {
         __hip_atomic_store(kg + b, score_key(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wkey[b - w0] = score_key(s);
+      }
+    }
+  }
+  if (fast) {
+    // local rank of block i among this workgroup's blocks, in four quarters
+    __syncthreads();
+    const int i = tid & (kSelBlocks - 1), q = tid >> 6;
+    if (i < nv) {
+      const uint32_t ki = wkey[i];
+      int cnt = 0;
+      for (int j = q * 16; j < min(nv, q * 16 + 16); ++j) {
+        const uint32_t kj = wkey[j];
+        cnt += (kj > ki) || (kj == ki && j < i);
+      }
+      wrank[q][i] = cnt;
+    }
+    __syncthreads();
+    if (tid < nv) {
+      const int rank = wrank[0][tid] + wrank[1][tid] + wrank[2][tid] + wrank[3][tid];
+      if (rank < min(K, nv))
+        __hip_atomic_store(cand + ((size_t)g * gridDim.x + blockIdx.x) * KC + rank,
+                           ((uint64_t)wkey[tid] << 32) | (uint32_t)~(uint32_t)(w0 + tid),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -141,7 +205,36 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
   __syncthreads();
   if (!st_last) return;
 
-  const int K = min(K_top, nb);
+  int32_t *out = blocks + (size_t)g * K_top;
+  if (fast) {
+    const int C = gridDim.x * KC;
+    for (int x = tid; x < C; x += 256) {
+      const int w = x / KC, r = x - w * KC;
+      const int kc = min(K, min(kSelBlocks, nb - w * kSelBlocks));  // valid slots of w
+      cx[x] = r < kc ? __hip_atomic_load(cand + (size_t)g * C + x, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 0ull;  // below every valid composite
+    }
+    __syncthreads();
+    for (int x = tid; x < C; x += 256) {
+      const uint64_t X = cx[x];
+      if (X == 0ull) continue;
+      int rank = 0;
+      for (int j = 0; j < C; ++j) rank += cx[j] > X;
+      if (rank < K) sel[rank] = ~(uint32_t)X;
+    }
+    __syncthreads();
+    if (tid < K) {
+      const uint32_t v = sel[tid];
+      int pos = 0;
+      for (int j = 0; j < K; ++j) pos += sel[j] < v;
+      out[pos] = (int32_t)v;
+    }
+    for (int k = K + tid; k < K_top; k += 256) out[k] = -1;
+    if (tid == 0) __hip_atomic_store(counters + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
   constexpr int CH = 256 * kSelE;
   uint32_t kr[kSelE];
   auto load_chunk = [&](int c0) {
@@ -200,7 +293,6 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
   }
 
   const uint32_t T = prefix;
-  int32_t *out = blocks + (size_t)g * K_top;
   int gt_run = 0, eq_run = 0;
   for (int c0 = 0; c0 < nb; c0 += CH) {
     if (!one) load_chunk(c0);
@@ -265,21 +357,21 @@ hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t 
 
 hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float *kmean,
                                int H_kv, int nb, int D, int K_top, uint32_t *keys,
-                               int *counters, int32_t *blocks, hipStream_t s) {
+                               uint64_t *cand, int *counters, int32_t *blocks, hipStream_t s) {
   if (K_top < 1 || nb < 1 || H_kv < 1) return hipErrorInvalidValue;
   dim3 grid((nb + kSelBlocks - 1) / kSelBlocks, H_kv);
   switch (D) {
     case 64:
       hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, counters, blocks);
+                         keys, cand, counters, blocks);
       break;
     case 128:
       hipLaunchKernelGGL(block_select_kernel<128>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, counters, blocks);
+                         keys, cand, counters, blocks);
       break;
     case 256:
       hipLaunchKernelGGL(block_select_kernel<256>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, counters, blocks);
+                         keys, cand, counters, blocks);
       break;
     default:
       return hipErrorInvalidValue;
