@@ -41,6 +41,34 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Combine each lane with the lanes that differ from it in the bits >= LPR of the lane
+// index (the slots of a wave holding the same dims), without LDS: lane ^ 8 by a row
+// rotation, lane ^ 16 and lane ^ 32 by the row swaps. Every lane gets the result.
+__device__ __forceinline__ float swap_pair_max(float v, bool by32) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float swap_pair_sum(float v, bool by32) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+template <int LPR>
+__device__ __forceinline__ float slots_max(float v) {
+  if constexpr (LPR <= 8) v = fmaxf(v, dpp<0x128>(v));  // row rotate by 8: lane ^ 8
+  if constexpr (LPR <= 16) v = swap_pair_max(v, false);
+  return swap_pair_max(v, true);
+}
+template <int LPR>
+__device__ __forceinline__ float slots_sum(float v) {
+  if constexpr (LPR <= 8) v += dpp<0x128>(v);
+  if constexpr (LPR <= 16) v = swap_pair_sum(v, false);
+  return swap_pair_sum(v, true);
+}
+
 template <int D, int R>
 struct WaveState {
   float m[4][R];
@@ -68,20 +96,11 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
   WaveState<D, R> &ws = sm.ws;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float M = m[r];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float M = slots_max<LPR>(m[r]);
     const float f = fast_exp2(m[r] - M);
-    float lr = l[r] * f;
+    const float lr = slots_sum<LPR>(l[r] * f);
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) lr += __shfl_xor(lr, o);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[r][e] * f;
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      acc[r][e] = v;
-    }
+    for (int e = 0; e < 8; ++e) acc[r][e] = slots_sum<LPR>(acc[r][e] * f);
     if (kk == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ws.acc[wave][r][sub * 8 + e] = acc[r][e];
