@@ -75,11 +75,23 @@ def prefix_query_sparse_auto(Q, K, V, B: int, K_top: int, head_map=None,
     km = block_means(K, B)
     score = block_scores(Q[:, 0, :], km, hm)
     blocks = np.full((H_kv, K_top), -1, dtype=np.int64)
-    chosen = []
     for g in range(H_kv):
         sel = select_blocks(score[g], K_top)
         blocks[g, :len(sel)] = sel
-        chosen.append(np.concatenate([np.arange(b * B, min((b + 1) * B, N)) for b in sel]))
+    out, lse = prefix_query_blocks(Q, K, V, B, blocks, hm, K_suf, V_suf)
+    return out, lse, blocks
+
+
+def prefix_query_blocks(Q, K, V, B: int, blocks, head_map=None, K_suf=None, V_suf=None):
+    """M=1 attention of each q-head over the tokens of the given blocks of its kv-head
+    (blocks [H_kv, *], entries < 0 ignored) plus the whole suffix, if any: the attention
+    step of the sparse-auto query once its blocks are chosen."""
+    H_q, _, D = Q.shape
+    H_kv, N, _ = K.shape
+    hm = resolve_head_map(H_q, H_kv, head_map)
+    tau = softmax_scale(D)
+    chosen = [np.concatenate([np.arange(b * B, min((b + 1) * B, N)) for b in row if b >= 0]
+                            + [np.zeros(0, np.int64)]).astype(np.int64) for row in blocks]
     out = np.empty((H_q, D))
     lse = np.empty(H_q)
     S_suf = 0 if K_suf is None else K_suf.shape[1]
@@ -91,7 +103,7 @@ def prefix_query_sparse_auto(Q, K, V, B: int, K_top: int, head_map=None,
             keys = np.concatenate([keys, f64(K_suf[g])])
             vals = np.concatenate([vals, f64(V_suf[g])])
         out[h], lse[h] = attend(Q[h, 0], keys, vals, tau)
-    return out, lse, blocks
+    return out, lse
 
 
 def prefix_query_sparse(Q, K, V, indices, counts):

@@ -360,6 +360,62 @@ def test_sparse_auto_edges(kp, N, B, K_top):
     check(out, lse, ref, ref_lse)
 
 
+def check_selection(blocks, Q, K, B, K_top, head_map=None):
+    """The chosen blocks are a valid top-K: ascending, distinct, -1 padded, and every
+    chosen block scores (oracle, fp64) at least as high as every other block, up to the
+    rounding bound of an fp32 score (2^-12 of the sum of |q_h| . |K_mean| per block).
+    Blocks whose scores differ by less than that bound may rank either way."""
+    H_q, _, D = Q.shape
+    H_kv, N, _ = K.shape
+    hm = oracle.resolve_head_map(H_q, H_kv, head_map)
+    km = oracle.block_means(K, B)
+    score = oracle.block_scores(Q[:, 0, :], km, hm)
+    bound = 2.0 ** -12 * oracle.block_scores(np.abs(Q[:, 0, :].astype(np.float64)), np.abs(km), hm)
+    nb = km.shape[1]
+    n = min(K_top, nb)
+    for g in range(H_kv):
+        row = blocks[g]
+        assert (row[n:] == -1).all()
+        sel = row[:n]
+        assert (np.diff(sel) > 0).all() and sel[0] >= 0 and sel[-1] < nb
+        rest = np.setdiff1d(np.arange(nb), sel)
+        if len(rest):
+            worst = np.argmin(score[g, sel] + bound[g, sel])
+            best = np.argmax(score[g, rest] - bound[g, rest])
+            assert score[g, sel][worst] + bound[g, sel][worst] >= score[g, rest][best] - bound[g, rest][best]
+
+
+@pytest.mark.parametrize("N,B,K_top", [(20000, 16, 100), (70000, 16, 20)])
+def test_sparse_auto_radix_select(kp, N, B, K_top):
+    # K_top above 64, or more per-workgroup candidates than the candidate merge holds:
+    # the selection runs the radix select
+    inp = synth.generate(synth.SPARSE, 6, N=N, H_q=4, H_kv=2, D=64, S_suf=12, n_needles=2)
+    kp.pion_prefix_store("t", 16, dev(inp.K), dev(inp.V))
+    out, lse, blocks = sparse_call(kp, "t", 16, inp, B, K_top, 2)
+    check_selection(blocks, inp.Q, inp.K, B, K_top, inp.head_map)
+    planted = synth.SPARSE.B // B  # needles are planted per 64-token block
+    for g in range(2):
+        assert {planted * n + i for n in inp.needles[g] for i in range(planted)} <= set(blocks[g])
+    ref, ref_lse = oracle.prefix_query_blocks(inp.Q, inp.K, inp.V, B, blocks, inp.head_map,
+                                              inp.K_suf, inp.V_suf)
+    check(out, lse, ref, ref_lse)
+
+
+@pytest.mark.parametrize("K_top", [10, 100])
+def test_sparse_auto_all_blocks_tied(kp, K_top):
+    # identical blocks score identically: the lowest indices win (candidate merge for 10,
+    # radix select for 100)
+    inp = synth.generate(synth.SPARSE, 7, N=16 * 300, H_q=2, H_kv=1, D=64, S_suf=0, n_needles=0)
+    K = np.broadcast_to(inp.K[:, :1, :], inp.K.shape).copy()
+    kp.pion_prefix_store("t", 17, dev(K), dev(inp.V))
+    inp.K = K
+    out, lse, blocks = sparse_call(kp, "t", 17, inp, 16, K_top, 1, suffix=False)
+    np.testing.assert_array_equal(blocks[0], np.arange(K_top))
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(inp.Q, K, inp.V, 16, K_top)
+    np.testing.assert_array_equal(ref_blocks[0], np.arange(K_top))
+    check(out, lse, ref, ref_lse)
+
+
 def test_sparse_auto_tie_goes_to_lower_block(kp):
     inp = synth.generate(synth.SPARSE, 3, N=64 * 20, H_q=2, H_kv=1, D=128, S_suf=0, n_needles=0)
     K = inp.K.copy()
