@@ -51,8 +51,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "a76a50291e94fd23d4b5068394e8bb456c392a4b9e8f4ac4705e42a962304a1f",
-                  "bytes_per_launch": 269464552}
+DECODE_TRAFFIC = {"sources_sha256": "0f29e1c386a55e02ea0e9a95664f72c5b0521e65635e0d3f8a6159978cdd1162",
+                  "bytes_per_launch": 269474315}
 
 
 def kernel_sources_sha256():
