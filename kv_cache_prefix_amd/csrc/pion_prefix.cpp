@@ -29,6 +29,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "attn_gqa.h"
 #include "kernels.h"
 #include "sparse.h"
 
@@ -425,8 +426,31 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   } else {
     p.x_begin = 0;
     const long long keys = (c.blocks ? (long long)c.n_sel * c.B : N_max) + c.S_suf;
-    p.seg_per_span = keys <= one_span_keys(c.D) ? p.S_max : 1;
-    e = launch_partial(p, R, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
+    // row groups of 6 to 8 q-heads at M = 1 and D <= 128 run on the MFMA kernel, whose
+    // key work does not grow with the rows (measured 11-15% faster there; slower for
+    // 4 rows or D = 256). PION_GQA_MFMA forces it for any group of 4 or more rows,
+    // PION_NO_GQA_MFMA turns it off. It addresses a kv-head's K, V and suffix through
+    // 32-bit buffer ranges.
+    const long long row_bytes = 2LL * c.D;
+    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && N_max * row_bytes < (1LL << 31) &&
+                        (long long)c.S_suf * row_bytes < (1LL << 31) &&
+                        !getenv_flag("PION_NO_GQA_MFMA");
+    const bool gqa = gqa_ok && ((grp_rows >= 6 && c.D <= 128) || getenv_flag("PION_GQA_MFMA"));
+    if (gqa) {
+      // one span when each wave gets at most PION_GQA_ONE_SPAN (default 2) sub-tiles of
+      // 32 keys: a wave keeps one sub-tile in flight ahead, which does not cover the load
+      // latency, so more keys are better spread over workgroups and merged
+      static const int one_span_sub = [] {
+        const char *e = getenv("PION_GQA_ONE_SPAN");
+        return e ? std::max(0, atoi(e)) : 2;
+      }();
+      const long long one_span = (long long)(c.D == 256 ? 2 : 4) * 32 * one_span_sub;
+      p.seg_per_span = keys <= one_span && p.S_max <= kGqaMaxSegs ? p.S_max : 1;
+      e = launch_gqa_mfma(p, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
+    } else {
+      p.seg_per_span = keys <= one_span_keys(c.D) ? p.S_max : 1;
+      e = launch_partial(p, R, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
+    }
   }
   return e == hipSuccess ? PION_OK : PION_ERR_HIP;
 }

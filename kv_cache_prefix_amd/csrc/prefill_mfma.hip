@@ -34,15 +34,13 @@
 // ticket of a row block merges the others' (acc, m, l) partials into its own with the
 // LSE rule.
 #include "kernels.h"
+#include "mfma_common.h"
 
 #include <type_traits>
 
 namespace pion {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Note: the result of __builtin_amdgcn_raw_buffer_load_b128 is reinterpreted as a whole
@@ -55,19 +53,6 @@ constexpr int BK = 64;    // keys per tile
 constexpr int kMaxPrefillSplits = 16;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// The value of lane l ^ 32, through the cross-half lane swap (no LDS round trip): the
-// swap leaves lane l holding x[l % 32] in one result and x[l % 32 + 32] in the other.
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
 
 
 constexpr int NSTAGE = 2;  // LDS tile stages (loads run NSTAGE - 1 tiles ahead)
@@ -85,38 +70,6 @@ struct PrefillSmem {
   };
   int last;
 };
-
-// Physical 16-byte chunk of logical chunk c in tile row r is c ^ swz(r) (found by an
-// exhaustive search for conflict-free K reads and transposed V reads, 64 banks).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 64) return ((r & 3) << 1) ^ ((r >> 1) & 7);
-  else return ((r & 3) << 2) ^ ((r >> 2) & 3);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));  // builtin type
-#define LDS_PTR(T, x) ((__attribute__((address_space(3))) T *)(x))
-
-// Raw buffer descriptor words (as make_rsrc) for the LDS-writing loads.
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
-}
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (lds uniform);
-// past the buffer's end the bytes are zero. One wait state separates the M0 write from
-// the load that reads it.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                   :
-                   : "v"(voff), "s"(lds), "s"(rsrc)
-                   : "memory", "m0");
-}
-
-// A row max may grow by this much (log2 units, a factor 2^8) before the accumulators
-// are rescaled: weights up to 2^8 stay exact enough in fp16 and the fp32 sums cannot
-// overflow, and after the first tiles a rescale is rare.
-constexpr float kRescaleSlack = 8.0f;
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return zero, which
 // masks the tails of the prefix and suffix without branches. 0x00020000 is the raw

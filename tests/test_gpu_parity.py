@@ -176,6 +176,38 @@ def test_decode_gqa_and_arbitrary_maps(kp, H_q, H_kv):
     check(out, None, ref, None)
 
 
+@pytest.mark.parametrize("N", [1, 31, 33, 777, 5000])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("H_q,H_kv", [(8, 2), (16, 2), (24, 3)])
+def test_decode_gqa_mfma(kp, monkeypatch, N, D, H_q, H_kv):
+    # the MFMA kernel for row groups of 4 to 8 q-heads at M = 1 (forced for every D and
+    # group size here): one span for a few sub-tiles, split spans with the merge beyond;
+    # with and without a fused suffix
+    monkeypatch.setenv("PION_GQA_MFMA", "1")
+    inp = synth.generate(synth.PREFILL, 12, N=N, M=1, S_suf=40, D=D, H_q=H_q, H_kv=H_kv)
+    kp.pion_prefix_store("t", 6, dev(inp.K), dev(inp.V))
+    out, lse = query(kp, "t", 6, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, inp.K, inp.V))
+    out, lse = empty((H_q, 1, D)), empty((H_q, 1))
+    kp.pion_prefix_query_fused("t", 6, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf))
+
+
+def test_decode_gqa_mfma_agrees_with_valu_path(kp, monkeypatch):
+    inp = synth.generate(synth.DECODE, 13, N=3000, H_q=32, H_kv=4)
+    hm = synth.random_head_map(32, 4, 3)
+    kp.pion_prefix_store("t", 7, dev(inp.K), dev(inp.V))
+    monkeypatch.setenv("PION_GQA_MFMA", "1")
+    a, la = query(kp, "t", 7, inp.Q, head_map=hm)
+    monkeypatch.delenv("PION_GQA_MFMA")
+    monkeypatch.setenv("PION_NO_GQA_MFMA", "1")
+    b, lb = query(kp, "t", 7, inp.Q, head_map=hm)
+    ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V, hm)
+    check(a, la, ref, ref_lse)
+    check(b, lb, ref, ref_lse)
+    assert np.max(np.abs(a - b)) <= 2 * OUT_TOL
+
+
 def test_restore_replaces_and_unknown_session(kp):
     import kv_cache_prefix_amd as k
     a = synth.generate(synth.DECODE, 1, N=100, H_q=2, H_kv=2)
