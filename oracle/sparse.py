@@ -106,14 +106,27 @@ def prefix_query_blocks(Q, K, V, B: int, blocks, head_map=None, K_suf=None, V_su
     return out, lse
 
 
-def prefix_query_sparse(Q, K, V, indices, counts):
+def prefix_query_sparse(Q, K, V, indices, counts, K_sparse_max=None):
     """ATTEND.PREFIX.QUERY_SPARSE: M=1 attention of q-head h over the caller-supplied
-    token indices[h, :counts[h]] of kv-head h (ATTEND.* page, QUERY_SPARSE row)."""
+    token indices of kv-head h (ATTEND.* page, QUERY_SPARSE row: per-head indices
+    [H, K_sparse_max] and counts [H]).
+
+    Readings where the page is silent: head h lists indices[h, :c] with
+    c = min(max(counts[h], 0), K_sparse_max); an index outside [0, N) names no token and
+    is skipped; an index listed twice is a key twice; a head with no key gets out = 0
+    and lse = -inf (the empty softmax)."""
     H, M, D = Q.shape
+    N = K.shape[1]
+    indices = np.asarray(indices)
+    if K_sparse_max is None:
+        K_sparse_max = indices.shape[1]
     tau = softmax_scale(D)
-    out = np.empty((H, D))
-    lse = np.empty(H)
+    out = np.zeros((H, D))
+    lse = np.full(H, -np.inf)
     for h in range(H):
-        idx = np.asarray(indices[h][:counts[h]], dtype=np.int64)
-        out[h], lse[h] = attend(Q[h, 0], f64(K[h])[idx], f64(V[h])[idx], tau)
+        c = min(max(int(counts[h]), 0), K_sparse_max)
+        idx = np.asarray(indices[h][:c], dtype=np.int64)
+        idx = idx[(idx >= 0) & (idx < N)]
+        if len(idx):
+            out[h], lse[h] = attend(Q[h, 0], f64(K[h])[idx], f64(V[h])[idx], tau)
     return out, lse

@@ -114,3 +114,62 @@ def test_planted_needles_are_selected_full_size():
     km32 = inp.K.astype(np.float32).reshape(1, -1, case.B, case.D).sum(2) / np.float32(case.B)
     sc32 = (km32[0] @ inp.Q[:, 0].astype(np.float32).sum(0)).astype(np.float32)
     np.testing.assert_array_equal(np.sort(np.argsort(-sc32, kind="stable")[:8]), inp.needles[0])
+
+
+# ------------------------------------------------------------------ caller-supplied indices
+def _sdpa_weighted(q, K, V, w):
+    """torch SDPA of one query row where key j carries multiplicity w_j (additive mask
+    ln w_j), in fp64; returns (out, lse)."""
+    qt = torch.from_numpy(q.astype(np.float64))[None, None, None, :]
+    Kt = torch.from_numpy(K.astype(np.float64))[None, None]
+    Vt = torch.from_numpy(V.astype(np.float64))[None, None]
+    mask = torch.from_numpy(np.log(np.asarray(w, np.float64)))[None, None, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask)
+    s = (Kt[0, 0] @ qt[0, 0, 0]) / np.sqrt(q.shape[-1]) + mask[0, 0, 0]
+    return out[0, 0, 0].numpy(), float(torch.logsumexp(s, dim=-1))
+
+
+def test_query_sparse_all_indices_is_dense():
+    inp = synth.generate(synth.DECODE, 3, N=70, H_q=3, H_kv=3, D=64)
+    idx = np.tile(np.arange(70), (3, 1))
+    out, lse = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, [70, 70, 70])
+    ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+    np.testing.assert_allclose(out, ref[:, 0], atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse[:, 0], atol=1e-13)
+
+
+def test_query_sparse_is_library_sdpa_over_the_listed_tokens():
+    rng = np.random.default_rng(5)
+    inp = synth.generate(synth.DECODE, 4, N=200, H_q=2, H_kv=2, D=32)
+    idx = rng.integers(0, 200, size=(2, 40))
+    idx[0, 7] = idx[0, 3]                       # a token listed twice weighs twice
+    idx[1, 5] = -1                              # out of range: skipped
+    idx[1, 9] = 200
+    counts = [40, 25]                           # head 1 uses the first 25 only
+    out, lse = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
+    for h in range(2):
+        sel = [int(t) for t in idx[h, :counts[h]] if 0 <= t < 200]
+        uniq, mult = np.unique(sel, return_counts=True)
+        ref, ref_lse = _sdpa_weighted(inp.Q[h, 0], inp.K[h, uniq], inp.V[h, uniq], mult)
+        np.testing.assert_allclose(out[h], ref, atol=1e-12)
+        assert abs(lse[h] - ref_lse) < 1e-12
+
+
+def test_query_sparse_order_of_indices_is_irrelevant():
+    rng = np.random.default_rng(6)
+    inp = synth.generate(synth.DECODE, 5, N=90, H_q=2, H_kv=2, D=64)
+    idx = rng.integers(0, 90, size=(2, 30))
+    a = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, [30, 30])
+    b = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx[:, ::-1], [30, 30])
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+
+
+def test_query_sparse_counts_clamp_and_empty_head():
+    inp = synth.generate(synth.DECODE, 6, N=50, H_q=3, H_kv=3, D=32)
+    idx = np.tile(np.arange(10), (3, 1))
+    out, lse = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, [0, -4, 99])
+    assert (out[:2] == 0).all() and np.isneginf(lse[:2]).all()
+    ref, ref_lse = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, [0, 0, 10])
+    np.testing.assert_array_equal(out[2], ref[2])     # 99 clamps to K_sparse_max = 10
+    assert lse[2] == ref_lse[2]
