@@ -146,6 +146,21 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D,
                                   const int32_t *head_map, float *out, float *lse,
                                   int32_t *blocks_out, void *stream);
 
+/* ATTEND.PREFIX.QUERY_SPARSE <sid> <layer> <H> <D> <K_sparse_max> <Q> <indices> <counts>:
+ * M = 1 attention of each head over caller-supplied tokens (ATTEND.* page,
+ * QUERY_SPARSE rows: per-head indices, for learned-router consumers).
+ *   Q        fp16 [H, 1, D]; H is the stored H (q-head h reads kv-head h).
+ *   indices  int32 [H, K_sparse_max], device memory; counts int32 [H], device memory.
+ *   Head h attends tokens indices[h, j] for j < min(max(counts[h], 0), K_sparse_max);
+ *   an index outside [0, N) names no token and is skipped, a repeated index is a key
+ *   as many times as it is listed; a head with no key gets out 0 and lse -inf.
+ *   out fp32 [H, D]; lse fp32 [H] or NULL.
+ * Errors: as pion_prefix_query, plus INVALID for H != stored H, K_sparse_max < 1 or
+ * > 2^24, null indices or counts; UNSUPPORTED for an mlx4g32 slot. */
+int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_sparse_max,
+                             const void *Q, const int32_t *indices, const int32_t *counts,
+                             float *out, float *lse, void *stream);
+
 /* mlx4g32 encoder ("Shared KV Cache Serving", Quantized tier - mlx4g32; V-store page,
  * The mlx4g32 tier): int4 codes in groups of 32, affine, fp16 scale and bias per group,
  * the scale rounded to fp16 before codes are chosen. Per group, in fp32 with IEEE

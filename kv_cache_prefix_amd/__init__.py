@@ -39,6 +39,8 @@ SIGNATURES = {
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pion_prefix_query_sparse_auto": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,
                                              _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query_sparse": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+                                        _vp, _vp]),
     "pion_kv_quantize_mlx4g32": (_int, [_vp, ctypes.c_int64, _int, _vp, _vp, _vp, _vp]),
     "pion_status_str": (ctypes.c_char_p, [_int]),
 }
@@ -211,6 +213,23 @@ def pion_prefix_query_sparse_auto(sid, layer: int, Q, B: int, K_top: int, out, l
         None if blocks_out is None else _dev(blocks_out, torch.int32, "blocks_out", (H_kv, K_top)),
         _stream(stream))
     return _check(rc, "pion_prefix_query_sparse_auto")
+
+
+def pion_prefix_query_sparse(sid, layer: int, Q, indices, counts, out, lse=None,
+                             stream=None) -> int:
+    """ATTEND.PREFIX.QUERY_SPARSE: Q fp16 [H, 1, D], indices int32 [H, K_sparse_max],
+    counts int32 [H] -> out fp32 [H, D], lse fp32 [H]."""
+    import torch
+    H, M, D = Q.shape
+    if M != 1:
+        raise ValueError("QUERY_SPARSE takes one query row per head")
+    K_sparse_max = indices.shape[1]
+    rc = lib().pion_prefix_query_sparse(
+        _sid(sid), layer, H, D, K_sparse_max, _dev(Q, torch.float16, "Q"),
+        _dev(indices, torch.int32, "indices", (H, K_sparse_max)),
+        _dev(counts, torch.int32, "counts", (H,)), _dev(out, torch.float32, "out", (H, D)),
+        None if lse is None else _dev(lse, torch.float32, "lse", (H,)), _stream(stream))
+    return _check(rc, "pion_prefix_query_sparse")
 
 
 def pion_kv_quantize_mlx4g32(x, codes, scales, biases, stream=None) -> int:

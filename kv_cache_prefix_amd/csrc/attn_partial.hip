@@ -126,9 +126,10 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
     }
     if (b.S_total == 1) {  // the only span of its rows: final output, no merge
       const size_t row = (size_t)heads[r] * p.M + qi;
-      const float inv = 1.f / lw;
+      const float inv = lw > 0.f ? 1.f / lw : 0.f;  // no key at all: out 0, lse -inf
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-      if (dq == 0 && b.lse) b.lse[row] = (mm + __log2f(lw)) * 0.69314718055994530942f;
+      if (dq == 0 && b.lse)
+        b.lse[row] = lw > 0.f ? (mm + __log2f(lw)) * 0.69314718055994530942f : -INFINITY;
     } else {
       store_part(pr, heads[r], x, dq, a);
       if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
@@ -144,10 +145,11 @@ struct Tile {
   bool ok[U];
 };
 
-template <int D, int R, int U>
+template <int D, int R, int U, bool GATHER>
 __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   constexpr int LPR = D / 8, KPI = 64 / LPR, STEP = KPI * U;
   __shared__ Scratch<D, R> sm;
+  __shared__ int gsp[GATHER ? kGatherChunk : 1];  // the span's token indices
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
@@ -182,8 +184,16 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   // the segments of this span, one after another (wave-uniform loop)
   const int seg0 = x * p.seg_per_span, seg1 = min(seg0 + p.seg_per_span, b.n_seg);
   for (int sgi = seg0; sgi < seg1; ++sgi) {
-    const Span sp = get_segment(p, sgi, b.pre_splits, b.N, g, qi);
+    Span sp = get_segment(p, sgi, b.pre_splits, b.N, g, qi);
     if (!sp.suffix && p.fmt != 0) continue;  // an mlx4g32 prefix has its own kernel
+    if constexpr (GATHER) {  // list positions [j0, j1) of q-head heads[0]'s token list
+      const int h = heads[0];
+      sp.j1 = min(sp.j1, max(sp.j0, min(p.gcount[h], p.gmax)));
+      __syncthreads();  // the previous segment is done with gsp
+      for (int t = threadIdx.x; t < sp.j1 - sp.j0; t += 256)
+        gsp[t] = p.gidx[(size_t)h * p.gmax + sp.j0 + t];
+      __syncthreads();
+    }
     const uint16_t *Kf, *Vf;
     if (sp.suffix) {
       Kf = p.Ksuf + (size_t)g * p.S_suf * D;
@@ -197,8 +207,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
     auto load = [&](Tile<U> &t, int base) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = base + u * KPI + kk;
+        int j = base + u * KPI + kk;
         t.ok[u] = j < sp.j1;
+        if constexpr (GATHER) {  // the listed token; one outside [0, N) is skipped
+          const int tok = t.ok[u] ? gsp[j - sp.j0] : 0;
+          t.ok[u] = t.ok[u] && tok >= 0 && tok < b.N;
+          j = tok;
+        }
         if (t.ok[u]) {
           t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
           t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
@@ -268,7 +283,10 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
 template <int D, int R>
 hipError_t launch_partial_d(const PartialParams &p, int x_count, hipStream_t s) {
   dim3 grid(x_count, p.y_groups, p.n_prob);
-  hipLaunchKernelGGL((attn_split_kernel<D, R, 4>), grid, dim3(256), 0, s, p);
+  if (p.gidx)
+    hipLaunchKernelGGL((attn_split_kernel<D, 1, 4, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, R, 4, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -299,6 +317,10 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
                           hipStream_t s) {
   if (x_count < 1 || p.y_groups < 1 || p.n_prob < 1) return hipSuccess;
   if (p.S_max > kMaxSplits || p.n_prob > kMaxBatch) return hipErrorInvalidValue;
+  // a token list: one q-head per row group, one segment per span of at most kGatherChunk
+  if (p.gidx && (rows_per_group != 1 || p.seg_per_span != 1 || p.pre_chunk > kGatherChunk ||
+                 p.n_prob != 1 || p.fmt != 0))
+    return hipErrorInvalidValue;
   switch (p.D) {
     case 64: return launch_partial_r<64>(p, rows_per_group, x_count, s);
     case 128: return launch_partial_r<128>(p, rows_per_group, x_count, s);

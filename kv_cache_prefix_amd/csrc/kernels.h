@@ -21,6 +21,7 @@ struct RowGroups {
 };
 
 constexpr int kMaxBatch = 64;     // problems (layers) per launch
+constexpr int kGatherChunk = 2048;  // token-list positions per span
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -117,6 +118,11 @@ struct PartialParams {
   int pre_chunk;
   const int32_t *blocks;  // [H_kv, K_top] or null (single problem only)
   int K_top, B, n_sel;
+  // caller-supplied token lists (single problem, one q-head per kv-head): q-head h
+  // attends tokens gidx[h, j] for j < min(max(gcount[h], 0), gmax); indices outside
+  // [0, N) are skipped. The prefix segments then chunk the list positions [0, gmax).
+  const int32_t *gidx, *gcount;  // [H, gmax], [H] or null
+  int gmax;
   const uint16_t *Ksuf, *Vsuf;  // fp16 [H_kv, S_suf, D] (single problem only)
   int S_suf, suf_chunk, suf_splits;
   int seg_per_span;       // segments per span (>= 1)

@@ -275,6 +275,8 @@ struct AttnCall {
   int S_suf;
   const int32_t *blocks;  // device [H_kv, K_top] or null
   int n_sel, K_top, B;
+  const int32_t *gidx, *gcount;  // device [H, gmax], [H] or null
+  int gmax;
   float *out, *lse;
   size_t out_stride, lse_stride;
 };
@@ -380,7 +382,13 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   p.lse = c.lse;
   p.lse_stride = c.lse_stride;
   int pre_max;
-  if (c.blocks) {
+  if (c.gidx) {  // a caller's token list per head: chunks of list positions
+    p.gidx = c.gidx;
+    p.gcount = c.gcount;
+    p.gmax = c.gmax;
+    p.pre_chunk = std::min(pick_chunk(c.gmax, (long long)Y, 64, false), kGatherChunk);
+    pre_max = (c.gmax + p.pre_chunk - 1) / p.pre_chunk;
+  } else if (c.blocks) {
     p.blocks = c.blocks;
     p.K_top = c.K_top;
     p.B = c.B;
@@ -425,14 +433,15 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     }
   } else {
     p.x_begin = 0;
-    const long long keys = (c.blocks ? (long long)c.n_sel * c.B : N_max) + c.S_suf;
+    const long long keys =
+        (c.gidx ? (long long)c.gmax : c.blocks ? (long long)c.n_sel * c.B : N_max) + c.S_suf;
     // row groups of 6 to 8 q-heads at M = 1 and D <= 128 run on the MFMA kernel, whose
     // key work does not grow with the rows (measured 11-15% faster there; slower for
     // 4 rows or D = 256). PION_GQA_MFMA forces it for any group of 4 or more rows,
     // PION_NO_GQA_MFMA turns it off. It addresses a kv-head's K, V and suffix through
     // 32-bit buffer ranges.
     const long long row_bytes = 2LL * c.D;
-    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && N_max * row_bytes < (1LL << 31) &&
+    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && N_max * row_bytes < (1LL << 31) &&
                         (long long)c.S_suf * row_bytes < (1LL << 31) &&
                         !getenv_flag("PION_NO_GQA_MFMA");
     const bool gqa = gqa_ok && ((grp_rows >= 6 && c.D <= 128) || getenv_flag("PION_GQA_MFMA"));
@@ -448,7 +457,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
       p.seg_per_span = keys <= one_span && p.S_max <= kGqaMaxSegs ? p.S_max : 1;
       e = launch_gqa_mfma(p, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
     } else {
-      p.seg_per_span = keys <= one_span_keys(c.D) ? p.S_max : 1;
+      p.seg_per_span = keys <= one_span_keys(c.D) && !c.gidx ? p.S_max : 1;
       e = launch_partial(p, R, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
     }
   }
@@ -803,6 +812,41 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   c.n_sel = n_sel;
   c.K_top = K_top;
   c.B = B;
+  c.out = out;
+  c.lse = lse;
+  return run_attention({sl}, c, st);
+}
+
+int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_sparse_max,
+                             const void *Q, const int32_t *indices, const int32_t *counts,
+                             float *out, float *lse, void *stream) {
+  int rc = check_query_args(sid, H, D, 1, Q, out);
+  if (rc != PION_OK) return rc;
+  if (K_sparse_max < 1 || K_sparse_max > (1 << 24) || !indices || !counts) return PION_ERR_INVALID;
+  if (!aligned(indices, 4) || !aligned(counts, 4) || (lse && !aligned(lse, 4)))
+    return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Slot *sl = find_slot(sid, layer);
+  if (!sl) return PION_ERR_NOT_FOUND;
+  if (sl->D != D || sl->H != H) return PION_ERR_INVALID;
+  if (sl->fmt != PION_KV_FP16) return PION_ERR_UNSUPPORTED;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse)) || !on_device(indices) ||
+      !on_device(counts))
+    return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+  std::vector<int> hm(H);
+  for (int h = 0; h < H; ++h) hm[h] = h;
+  AttnCall c{};
+  c.Q = (const uint16_t *)Q;
+  c.H_q = H;
+  c.M = 1;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = H;
+  c.gidx = indices;
+  c.gcount = counts;
+  c.gmax = K_sparse_max;
   c.out = out;
   c.lse = lse;
   return run_attention({sl}, c, st);

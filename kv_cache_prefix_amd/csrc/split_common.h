@@ -76,9 +76,9 @@ __device__ __forceinline__ Span get_segment(const PartialParams &p, int x, int p
         s.j0 = b * p.B;
         s.j1 = min(s.j0 + p.B, N);
       }
-    } else {
+    } else {  // dense chunks of the prefix, or of a caller's token list
       s.j0 = x * p.pre_chunk;
-      s.j1 = min(s.j0 + p.pre_chunk, N);
+      s.j1 = min(s.j0 + p.pre_chunk, p.gidx ? p.gmax : N);
     }
   } else {
     s.suffix = true;
@@ -101,7 +101,7 @@ struct Prob {
 __device__ __forceinline__ Prob get_prob(const PartialParams &p, int z, int y) {
   Prob b;
   b.N = p.N[z];
-  b.pre_splits = p.blocks ? p.n_sel : (b.N + p.pre_chunk - 1) / p.pre_chunk;
+  b.pre_splits = p.blocks ? p.n_sel : ((p.gidx ? p.gmax : b.N) + p.pre_chunk - 1) / p.pre_chunk;
   b.n_seg = b.pre_splits + p.suf_splits;
   b.S_total = (b.n_seg + p.seg_per_span - 1) / p.seg_per_span;
   b.Q = p.Q + z * p.q_stride;
@@ -263,11 +263,11 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
       }
       __syncthreads();
     }
-    if (ph == 0) {
+    if (ph == 0) {  // a row with no key at all (an empty token list): out 0, lse -inf
       const size_t row = (size_t)h * p.M + qi;
-      const float inv = 1.f / l;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-      if (dq == 0 && b.lse) b.lse[row] = (m + __log2f(l)) * 0.69314718055994530942f;
+      if (dq == 0 && b.lse) b.lse[row] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 }

@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n

@@ -476,6 +476,68 @@ def test_sparse_auto_mlx4g32_slot(kp):
     check(out, lse, ref, ref_lse)
 
 
+# ------------------------------------------------------------------ caller-supplied indices
+def sparse_indices(rng, H, N, K_sparse_max):
+    idx = rng.integers(-3, N + 3, size=(H, K_sparse_max)).astype(np.int32)  # a few out of range
+    if K_sparse_max > 4:
+        idx[:, 1] = idx[:, 0]                                            # a repeated token
+    counts = rng.integers(0, K_sparse_max + 1, size=H).astype(np.int32)
+    counts[0] = K_sparse_max
+    if H > 2:
+        counts[1] = 0                                                    # an empty head
+        counts[2] = K_sparse_max + 5                                     # clamps
+    return idx, counts
+
+
+def check_sparse(out, lse, ref, ref_lse):
+    empty = np.isneginf(ref_lse)
+    assert (out[empty] == 0).all() and np.isneginf(lse[empty]).all()
+    check(out[~empty], lse[~empty], ref[~empty], ref_lse[~empty])
+
+
+@pytest.mark.parametrize("K_sparse_max", [1, 63, 700, 3000])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_query_sparse_indices(kp, D, K_sparse_max):
+    import torch
+    rng = np.random.default_rng(D + K_sparse_max)
+    H, N = 4, 5000
+    inp = synth.generate(synth.DECODE, 14, N=N, D=D, H_q=H, H_kv=H)
+    kp.pion_prefix_store("t", 18, dev(inp.K), dev(inp.V))
+    idx, counts = sparse_indices(rng, H, N, K_sparse_max)
+    out, lse = empty((H, D)), empty((H,))
+    kp.pion_prefix_query_sparse("t", 18, dev(inp.Q), dev(idx), dev(counts), out, lse)
+    ref, ref_lse = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
+    check_sparse(host(out), host(lse), ref, ref_lse)
+
+
+def test_query_sparse_all_tokens_equals_dense_query(kp):
+    inp = synth.generate(synth.DECODE, 15, N=3000, H_q=8, H_kv=8)
+    kp.pion_prefix_store("t", 19, dev(inp.K), dev(inp.V))
+    idx = np.tile(np.arange(3000, dtype=np.int32), (8, 1))
+    out = empty((8, 128))
+    kp.pion_prefix_query_sparse("t", 19, dev(inp.Q), dev(idx), dev(np.full(8, 3000, np.int32)), out)
+    dense, _ = query(kp, "t", 19, inp.Q, want_lse=False)
+    assert np.max(np.abs(host(out) - dense[:, 0])) <= 2e-4
+    check(host(out), None, oracle.prefix_query(inp.Q, inp.K, inp.V)[0][:, 0], None)
+
+
+def test_query_sparse_rejects_bad_arguments(kp):
+    import kv_cache_prefix_amd as k
+    inp = synth.generate(synth.DECODE, 16, N=100, H_q=2, H_kv=2, D=64)
+    kp.pion_prefix_store("t", 20, dev(inp.K), dev(inp.V))
+    idx, counts = dev(np.zeros((2, 4), np.int32)), dev(np.ones(2, np.int32))
+    out = empty((2, 64))
+    with pytest.raises(k.PionError) as e:  # H differs from the stored H
+        kp.pion_prefix_query_sparse("t", 20, dev(np.zeros((3, 1, 64), np.float16)),
+                                    dev(np.zeros((3, 4), np.int32)), dev(np.ones(3, np.int32)),
+                                    empty((3, 64)))
+    assert e.value.status == k.PION_ERR_INVALID
+    kp.pion_prefix_store("t", 21, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    with pytest.raises(k.PionError) as e:
+        kp.pion_prefix_query_sparse("t", 21, dev(inp.Q), idx, counts, out)
+    assert e.value.status == k.PION_ERR_UNSUPPORTED
+
+
 # ------------------------------------------------------------------ streams
 def test_store_on_one_stream_query_on_another(kp):
     import torch
