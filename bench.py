@@ -15,7 +15,8 @@ Other workloads, one call per step (for the design notes; the default run is the
 above): --config 1 tiny dense query; --config 3 fused batched-Q prefill (TFLOP/s);
 --config 4 mlx4g32 decode, 16 layers per launch (GB/s of resident codes/scales/biases,
 plus the single-query latency); --config 5 sparse-auto
-fused query (us/query).
+fused query (us/query); --config 6 QUERY_SPARSE over caller-supplied indices (us/query,
+GB/s of gathered rows; not a headline workload).
 
 Timing: wall clock over K steps between device synchronizations; a HIP event pair on
 the launch stream brackets the same timed region, and its elapsed time over the number
@@ -51,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "0f29e1c386a55e02ea0e9a95664f72c5b0521e65635e0d3f8a6159978cdd1162",
-                  "bytes_per_launch": 269474315}
+DECODE_TRAFFIC = {"sources_sha256": "3d36951da55e6491dfffb84580033b52718e1226371c4e3d189ceeb45ee57826",
+                  "bytes_per_launch": 269455604}
 
 
 def kernel_sources_sha256():
@@ -71,7 +72,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="calls mode: no graph")
@@ -461,6 +462,67 @@ def run_tiny(args, torch, kp, synth, dev, stream):
             "roofline": None, "cpu_baseline": None}
 
 
+def run_query_sparse(args, torch, kp, synth, dev, stream):
+    """QUERY_SPARSE (caller-supplied indices): H = 8 heads, N = 65536 fp16 tokens, D = 128,
+    K_sparse_max = 2048 uniform random token indices per head (all counted), M = 1.
+    Not one of the five headline workloads; it measures the QUERY_SPARSE row. Bytes are
+    the gathered K and V rows: H * K_sparse_max * 2 * D * 2."""
+    import numpy as np
+    import oracle
+    H, N, D, KS = 8, 65536, 128, 2048
+    NSLOT = 4   # 4 slots of 268 MB each (1.07 GB)
+    inp = synth.generate(synth.DECODE, 21, N=N, H_q=H, H_kv=H, D=D)
+    rng = np.random.default_rng(21)
+    idx = rng.integers(0, N, size=(H, KS)).astype(np.int32)
+    counts = np.full(H, KS, np.int32)
+    K16, V16 = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
+    sid = "bench-qsparse"
+    for k in range(NSLOT):
+        kp.pion_prefix_store(sid, k, K16, V16)
+    del K16, V16
+    Q = torch.from_numpy(inp.Q).to(dev)
+    ti, tc = torch.from_numpy(idx).to(dev), torch.from_numpy(counts).to(dev)
+    out = torch.empty((H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((H,), dtype=torch.float32, device=dev)
+    lib, sidb = kp.lib(), sid.encode()
+
+    def make_step(k):
+        a = (sidb, k, H, D, KS, Q.data_ptr(), ti.data_ptr(), tc.data_ptr(), out.data_ptr(),
+             lse.data_ptr())
+
+        def step():
+            rc = lib.pion_prefix_query_sparse(*a, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_prefix_query_sparse")
+        return step
+
+    (ms, launch_us), (wms, _) = warm_cold(torch, stream, [make_step(k) for k in range(NSLOT)],
+                                          1, False, args)
+    ref, _ = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
+    check_close(out.cpu().numpy(), ref, 2e-3, "out")
+    nbytes = H * KS * 2 * D * 2
+    cpu = None
+    if not args.no_cpu_baseline:
+        def one_query():
+            oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
+        n, el = cpu_time(one_query, args.cpu_seconds)
+        cpu = {"value": round(el / n * 1e6, 1), "unit": "us/query", "cores": 1, "kind": "oracle",
+               "sample": f"{n} whole queries of this workload ({el:.1f} s)"}
+    kp.pion_prefix_drop(sid, -1)
+    return {
+        "value": ms * 1e3, "unit": "us/query", "ms_per_step": ms, "dtype": "fp16 K/V, fp32 accumulate",
+        "config": {"workload": f"QUERY_SPARSE H={H} N={N} D={D} K_sparse_max={KS} uniform random "
+                               "indices M=1", "bytes_per_step": nbytes,
+                   "memory_side_cache": f"cold: steps rotate over {NSLOT} slots"},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "avg_launch_us": launch_us},
+        "warm": {"value": round(wms * 1e3, 3), "unit": "us/query",
+                 "note": "one slot every step (memory-side cache warm)"},
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -482,7 +544,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
-    runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse}[args.config]
+    runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse,
+              6: run_query_sparse}[args.config]
     r = runner(args, torch, kp, synth, dev, stream)
     roof = r["roofline"]
     if roof is not None:
