@@ -23,7 +23,10 @@
  *     lse = ln(e^lse1 + e^lse2), out = e^(lse1-lse) out1 + e^(lse2-lse) out2.
  *   - head_map: int32 per q-head naming its kv-head (GQA); NULL means
  *     h -> h / (H_q / H_kv), which requires H_kv to divide H_q.
- *   - Supported head dims: D in {64, 128, 256}; other values -> PION_ERR_UNSUPPORTED.
+ *   - Supported head dims: D in {32, 64, 96, 128, 160, 192, 256, 512} (the native SDPA
+ *     head-dim set of the "Shared KV Cache Serving" page); other values ->
+ *     PION_ERR_UNSUPPORTED. Batched-Q (M >= 32) fp16 queries run on matrix cores for
+ *     D in {64, 128, 256} and on the vector split kernel otherwise (same results).
  *   - Calls are thread-safe (one library-wide lock guards the slot table).
  */
 #ifndef PION_PREFIX_H
@@ -61,7 +64,7 @@ enum { PION_KV_FP16 = 0, PION_KV_MLX4G32 = 1 };
  * cached block means. The library owns the slot memory; K and V may be freed once
  * `stream` has passed the call. sid is a NUL-terminated string of 1..255 bytes.
  * Errors: INVALID (null/empty sid, H/N/D <= 0, H > 255, kv_format unknown, D % 32 != 0
- * for MLX4G32), UNSUPPORTED (D), NOMEM (allocation, or more than PION_MAX_SLOTS slots;
+ * for MLX4G32), UNSUPPORTED (D; MLX4G32 with N * D >= 2^33), NOMEM (allocation, or more than PION_MAX_SLOTS slots;
  * default 4096, env PION_MAX_SLOTS), HIP. */
 int pion_prefix_store(const char *sid, int layer, int H, int N, int D,
                       const void *K, const void *V, int kv_format, void *stream);

@@ -4,11 +4,13 @@
 // mlx4g32): element e of group g of token j is s_jg * c_je + b_jg, with fp16 scale s
 // and bias b, integer code c in [0, 15].
 //
-// Layout. A key row of D elements is NG = D/32 groups; lane (slot kk, group g) owns
-// group g of its keys. It reads the group's 16 code bytes and its 4-byte (scale, bias)
-// pair per key and side, so dequantization needs no other lane's data. A wave covers
-// KPW = 64/NG keys per load instruction; each lane takes U keys per tile (keys
-// base + u*KPW + kk), and the next tile is loaded before the current one is consumed.
+// Layout. A key row of D elements is NG = D/32 groups, read by NGP lanes (NG rounded up
+// to a power of two; for D = 96, 160, 192 the lanes past NG hold no group and load
+// nothing); lane (slot kk, group g) owns group g of its keys. It reads the group's 16
+// code bytes and its 4-byte (scale, bias) pair per key and side, so dequantization
+// needs no other lane's data. A wave covers KPW = 64/NGP keys per load instruction;
+// each lane takes U keys per tile (keys base + u*KPW + kk), and the next tile is loaded
+// before the current one is consumed.
 //
 // Arithmetic, per row (q-head) and key j:
 //   q . k_j = sum_g  s_jg (q_g . c_jg) + b_jg sum(q_g)
@@ -27,9 +29,10 @@
 // when a tile's max exceeds it by more than kSlack (log2 units), so p <= 2^kSlack and
 // p * s stays within fp16 range for any fp16 scale (s <= 131008 / 15).
 //
-// End of span: the slots of each 16-lane row merge with DPP row rotations, the row
-// partials of the workgroup (4 per wave) merge through LDS, and the workgroup
-// stores its partial, takes its ticket, and the last one merges the row group.
+// End of span: the slots of a wave merge without LDS (DPP row rotations within each
+// 16-lane row, then the lane swaps across rows), the wave partials merge through LDS,
+// and the workgroup stores its partial, takes its ticket, and the last one merges the
+// row group.
 #include "split_common.h"
 
 namespace pion {
@@ -39,39 +42,55 @@ constexpr float kSlack = 2.0f;
 constexpr uint32_t kLo4 = 0x000F000Fu;  // nibble 0 of each half
 constexpr uint32_t kHi4 = 0x00F000F0u;  // nibble 1 of each half
 
-// Sum over each group of W consecutive lanes (W = 2, 4 or 8): quad_perm [1,0,3,2],
-// quad_perm [2,3,0,1], then row half-mirror (which pairs the two quads of 8 lanes).
+// Sum over each group of W consecutive lanes (W = 1 .. 16): quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row half-mirror (which pairs the two quads of 8 lanes), row
+// mirror (the two halves of 16).
 template <int W>
 __device__ __forceinline__ float lane_group_sum(float v) {
-  v += dpp<0xB1>(v);
+  if constexpr (W >= 2) v += dpp<0xB1>(v);
   if constexpr (W >= 4) v += dpp<0x4E>(v);
   if constexpr (W >= 8) v += dpp<0x141>(v);
+  if constexpr (W >= 16) v += dpp<0x140>(v);
   return v;
 }
 
-// Combine lanes of a 16-lane row that are NG apart (the slots holding the same group):
-// row rotations by NG, 2 NG, ..., 8.
-template <int NG>
-__device__ __forceinline__ float row_slots_max(float v) {
-  if constexpr (NG <= 1) v = fmaxf(v, dpp<0x121>(v));
-  if constexpr (NG <= 2) v = fmaxf(v, dpp<0x122>(v));
-  if constexpr (NG <= 4) v = fmaxf(v, dpp<0x124>(v));
-  if constexpr (NG <= 8) v = fmaxf(v, dpp<0x128>(v));
-  return v;
+// The max / sum of lanes l and l ^ 16 (by32: l ^ 32) in every lane, by the row swaps.
+__device__ __forceinline__ float swap_max(float v, bool by32) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
-template <int NG>
-__device__ __forceinline__ float row_slots_sum(float v) {
-  if constexpr (NG <= 1) v += dpp<0x121>(v);
-  if constexpr (NG <= 2) v += dpp<0x122>(v);
-  if constexpr (NG <= 4) v += dpp<0x124>(v);
-  if constexpr (NG <= 8) v += dpp<0x128>(v);
-  return v;
+__device__ __forceinline__ float swap_sum(float v, bool by32) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                      : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Row partials of a workgroup of NW waves: 4 rows of 16 lanes per wave.
+// Combine the lanes of a wave that are NGP apart (the slots holding the same group):
+// row rotations by NGP, 2 NGP, ..., 8 inside each 16-lane row, then the two row swaps.
+template <int NGP>
+__device__ __forceinline__ float wave_slots_max(float v) {
+  if constexpr (NGP <= 1) v = fmaxf(v, dpp<0x121>(v));
+  if constexpr (NGP <= 2) v = fmaxf(v, dpp<0x122>(v));
+  if constexpr (NGP <= 4) v = fmaxf(v, dpp<0x124>(v));
+  if constexpr (NGP <= 8) v = fmaxf(v, dpp<0x128>(v));
+  return swap_max(swap_max(v, false), true);
+}
+template <int NGP>
+__device__ __forceinline__ float wave_slots_sum(float v) {
+  if constexpr (NGP <= 1) v += dpp<0x121>(v);
+  if constexpr (NGP <= 2) v += dpp<0x122>(v);
+  if constexpr (NGP <= 4) v += dpp<0x124>(v);
+  if constexpr (NGP <= 8) v += dpp<0x128>(v);
+  return swap_sum(swap_sum(v, false), true);
+}
+
+// Wave partials of a workgroup of NW waves.
 template <int D, int R, int NW>
 struct Mlx4Scratch {
-  static constexpr int kParts = 4 * NW;
+  static constexpr int kParts = NW;
   float m[kParts][R], l[kParts][R];
   union {
     alignas(16) float acc[kParts][R][D];
@@ -99,13 +118,14 @@ __device__ __forceinline__ float hi_f(uint32_t w) { return h2f((uint16_t)(w >> 1
 
 template <int D, int R, int U, int NW>
 __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
-  constexpr int NG = D / 32, KPW = 64 / NG, STEP = KPW * U, NT = 64 * NW;
+  constexpr int NG = D / 32, NGP = pow2_ceil(NG), KPW = 64 / NGP, STEP = KPW * U, NT = 64 * NW;
   static_assert(U % 2 == 0, "keys are consumed in pairs");
   __shared__ Mlx4Scratch<D, R, NW> sm;
   constexpr int kParts = Mlx4Scratch<D, R, NW>::kParts;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int g = lane % NG, kk = lane / NG;
+  const int g = lane % NGP, kk = lane / NGP;
+  const bool grp = g < NG;  // this lane owns a group of its keys
   const int z = blockIdx.z, y = blockIdx.y;
   const Prob b = get_prob(p, z, y);
   const int x = blockIdx.x + p.x_begin;
@@ -129,10 +149,15 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t e = (uint32_t)(base + u * KPW + kk) * NG + g;  // (key, group) index
-      t.kc[u] = bload_stream16(rKc, e * 16);
-      t.vc[u] = bload_stream16(rVc, e * 16);
-      t.ksb[u] = bload_stream4(rKsb, e * 4);
-      t.vsb[u] = bload_stream4(rVsb, e * 4);
+      if (grp) {
+        t.kc[u] = bload_stream16(rKc, e * 16);
+        t.vc[u] = bload_stream16(rVc, e * 16);
+        t.ksb[u] = bload_stream4(rKsb, e * 4);
+        t.vsb[u] = bload_stream4(rVsb, e * 4);
+      } else {  // no group: zero codes, scale and bias
+        t.kc[u] = t.vc[u] = make_uint4(0, 0, 0, 0);
+        t.ksb[u] = t.vsb[u] = 0;
+      }
     }
   };
 
@@ -148,11 +173,11 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = heads[r < cnt ? r : 0];
-    const uint4 *qp = (const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + 32 * g);
+    const uint4 *qp = (const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + 32 * (grp ? g : 0));
     float qs = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint4 qq = qp[w];
+      const uint4 qq = grp ? qp[w] : make_uint4(0, 0, 0, 0);
       const uint32_t u4[4] = {qq.x, qq.y, qq.z, qq.w};
       uint16_t e[8];
 #pragma unroll
@@ -215,7 +240,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
       for (int r = 0; r < R; ++r) {
         const float dot = __builtin_fmaf(0.0625f, dB[r], dA[r]);  // dB is in 2^-20 units
         float v = __builtin_fmaf(ks, dot, kb * qsq[r]);
-        v = lane_group_sum<NG>(v);
+        v = lane_group_sum<NGP>(v);
         s[u][r] = ok ? v : -INFINITY;
       }
     }
@@ -298,21 +323,21 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     base = next;
   }
 
-  // back to value units, bias added; slots of the 16-lane row merged
+  // back to value units, bias added; slots of the wave merged
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float M = row_slots_max<NG>(m[r]);
+    const float M = wave_slots_max<NGP>(m[r]);
     const float f = fast_exp2(m[r] - M);
-    l[r] = row_slots_sum<NG>(l[r] * f);
+    l[r] = wave_slots_sum<NGP>(l[r] * f);
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const float v = __builtin_fmaf(acc[r][e], (e & 1) ? 1048576.0f : 16777216.0f, bs[r]);
-      acc[r][e] = row_slots_sum<NG>(v * f);
+      acc[r][e] = wave_slots_sum<NGP>(v * f);
     }
     m[r] = M;
   }
-  const int part = wave * 4 + (lane >> 4);
-  if ((lane & 15) < NG) {
+  const int part = wave;
+  if (lane < NG) {  // slot 0's groups (lane = g)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float4 *dst = (float4 *)&sm.acc[part][r][32 * g];
@@ -377,9 +402,14 @@ hipError_t launch_partial_mlx4(const PartialParams &p, int rows_per_group, int x
   if (p.S_max > kMaxSplits || p.n_prob > kMaxBatch) return hipErrorInvalidValue;
   if (rows_per_group < 1 || rows_per_group > kMlx4Rows) return hipErrorInvalidValue;
   switch (p.D) {
+    case 32: return launch_mlx4_r<32>(p, rows_per_group, x_count, s);
     case 64: return launch_mlx4_r<64>(p, rows_per_group, x_count, s);
+    case 96: return launch_mlx4_r<96>(p, rows_per_group, x_count, s);
     case 128: return launch_mlx4_r<128>(p, rows_per_group, x_count, s);
+    case 160: return launch_mlx4_r<160>(p, rows_per_group, x_count, s);
+    case 192: return launch_mlx4_r<192>(p, rows_per_group, x_count, s);
     case 256: return launch_mlx4_r<256>(p, rows_per_group, x_count, s);
+    case 512: return launch_mlx4_r<512>(p, rows_per_group, x_count, s);
     default: return hipErrorInvalidValue;
   }
 }

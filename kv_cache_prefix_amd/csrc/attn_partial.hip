@@ -8,11 +8,12 @@
 // with s_j = log2(e)/sqrt(D) * (q . k_j), the scaled logit in log2 units. The spans of
 // a row are merged by the LSE rule (split_common.h).
 //
-// Layout and schedule. A key row of D halves is read by D/8 consecutive lanes, 16 bytes
-// each (one wave-wide load covers 64/(D/8) whole rows, fully coalesced). Each group of
-// D/8 lanes is a "slot" that runs its own online softmax over the keys it sees, so the
-// inner loop needs no cross-lane max: only the D/8-lane dot-product sum, done with DPP
-// row operations. K and V of the next tile are loaded before the current tile is
+// Layout and schedule. A key row of D halves is read by LPR consecutive lanes, 16 bytes
+// each, LPR = D/8 rounded up to a power of two (for D = 96, 160, 192 the lanes past D/8
+// hold no dims and load nothing); one wave-wide load covers 64/LPR whole rows, fully
+// coalesced. Each group of LPR lanes is a "slot" that runs its own online softmax over
+// the keys it sees, so the inner loop needs no cross-lane max: only the LPR-lane
+// dot-product sum, done with DPP row operations and lane swaps. K and V of the next tile are loaded before the current tile is
 // consumed. At the end the slots of a wave and the 4 waves of the workgroup merge (LDS),
 // and the workgroup stores its partial. All q-heads that read the same kv-head share a
 // workgroup, so K/V bytes are read once per kv-head (GQA).
@@ -25,25 +26,7 @@
 namespace pion {
 namespace {
 
-// Sum over each group of W consecutive lanes (W = 8, 16 or 32); every lane of a group
-// receives the group sum. quad_perm [1,0,3,2] and [2,3,0,1] give quad sums, row
-// half-mirror pairs the two quads of 8 lanes, row mirror the two halves of 16, and a
-// swizzle with xor 16 the two rows of 32.
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  if constexpr (W >= 16) v += dpp<0x140>(v);
-  if constexpr (W >= 32)
-    v += __builtin_bit_cast(float,
-                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-  return v;
-}
-
-// Combine each lane with the lanes that differ from it in the bits >= LPR of the lane
-// index (the slots of a wave holding the same dims), without LDS: lane ^ 8 by a row
-// rotation, lane ^ 16 and lane ^ 32 by the row swaps. Every lane gets the result.
+// The sum / max of lanes l and l ^ 16 (by32: l ^ 32) in every lane, by the row swaps.
 __device__ __forceinline__ float swap_pair_max(float v, bool by32) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   const auto r = by32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
@@ -56,17 +39,42 @@ __device__ __forceinline__ float swap_pair_sum(float v, bool by32) {
                       : __builtin_amdgcn_permlane16_swap(u, u, false, false);
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
+// Sum over each group of W consecutive lanes (W = 4 .. 64); every lane of a group
+// receives the group sum. quad_perm [1,0,3,2] and [2,3,0,1] give quad sums, row
+// half-mirror pairs the two quads of 8 lanes, row mirror the two halves of 16, a
+// swizzle with xor 16 the two rows of 32, and the cross-half swap the halves of 64.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  if constexpr (W >= 8) v += dpp<0x141>(v);
+  if constexpr (W >= 16) v += dpp<0x140>(v);
+  if constexpr (W >= 32)
+    v += __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if constexpr (W >= 64) v = swap_pair_sum(v, true);
+  return v;
+}
+
+// Combine each lane with the lanes that differ from it in the bits >= LPR of the lane
+// index (the slots of a wave holding the same dims), without LDS: within a 16-lane row
+// by rotations (by 4, then 8: together every lane of the same index mod LPR), lane ^ 16
+// and lane ^ 32 by the row swaps. Every lane gets the result; LPR = 64 is one slot.
 template <int LPR>
 __device__ __forceinline__ float slots_max(float v) {
+  if constexpr (LPR <= 4) v = fmaxf(v, dpp<0x124>(v));  // row rotate by 4
   if constexpr (LPR <= 8) v = fmaxf(v, dpp<0x128>(v));  // row rotate by 8: lane ^ 8
   if constexpr (LPR <= 16) v = swap_pair_max(v, false);
-  return swap_pair_max(v, true);
+  if constexpr (LPR <= 32) v = swap_pair_max(v, true);
+  return v;
 }
 template <int LPR>
 __device__ __forceinline__ float slots_sum(float v) {
+  if constexpr (LPR <= 4) v += dpp<0x124>(v);
   if constexpr (LPR <= 8) v += dpp<0x128>(v);
   if constexpr (LPR <= 16) v = swap_pair_sum(v, false);
-  return swap_pair_sum(v, true);
+  if constexpr (LPR <= 32) v = swap_pair_sum(v, true);
+  return v;
 }
 
 template <int D, int R>
@@ -101,7 +109,7 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
     const float lr = slots_sum<LPR>(l[r] * f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[r][e] = slots_sum<LPR>(acc[r][e] * f);
-    if (kk == 0) {
+    if (kk == 0 && sub < D / 8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ws.acc[wave][r][sub * 8 + e] = acc[r][e];
     }
@@ -147,12 +155,13 @@ struct Tile {
 
 template <int D, int R, int U, bool GATHER>
 __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
-  constexpr int LPR = D / 8, KPI = 64 / LPR, STEP = KPI * U;
+  constexpr int LPR = fp16_row_lanes(D), KPI = 64 / LPR, STEP = KPI * U;
   __shared__ Scratch<D, R> sm;
   __shared__ int gsp[GATHER ? kGatherChunk : 1];  // the span's token indices
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
+  const bool dims = sub < D / 8;  // this lane holds 8 dims of a row
   const int z = blockIdx.z, y = blockIdx.y;
   const Prob b = get_prob(p, z, y);
   const int x = blockIdx.x + p.x_begin;
@@ -165,7 +174,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = heads[r < cnt ? r : 0];
-    const uint4 qq = *(const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + sub * 8);
+    const uint4 qq = dims ? *(const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + sub * 8)
+                          : make_uint4(0, 0, 0, 0);
     q[r][0] = as_h2(qq.x);
     q[r][1] = as_h2(qq.y);
     q[r][2] = as_h2(qq.z);
@@ -214,7 +224,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
           t.ok[u] = t.ok[u] && tok >= 0 && tok < b.N;
           j = tok;
         }
-        if (t.ok[u]) {
+        if (t.ok[u] && dims) {
           t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
           t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
         } else {
@@ -322,9 +332,14 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
                  p.n_prob != 1 || p.fmt != 0))
     return hipErrorInvalidValue;
   switch (p.D) {
+    case 32: return launch_partial_r<32>(p, rows_per_group, x_count, s);
     case 64: return launch_partial_r<64>(p, rows_per_group, x_count, s);
+    case 96: return launch_partial_r<96>(p, rows_per_group, x_count, s);
     case 128: return launch_partial_r<128>(p, rows_per_group, x_count, s);
+    case 160: return launch_partial_r<160>(p, rows_per_group, x_count, s);
+    case 192: return launch_partial_r<192>(p, rows_per_group, x_count, s);
     case 256: return launch_partial_r<256>(p, rows_per_group, x_count, s);
+    case 512: return launch_partial_r<512>(p, rows_per_group, x_count, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,21 @@ struct RowGroups {
 };
 
 constexpr int kMaxBatch = 64;     // problems (layers) per launch
+
+// Head dims served: the pages' full set. Every one is a multiple of 32 (one mlx4g32
+// group), so a row is whole 16-byte pieces of fp16 and whole groups of codes.
+__host__ __device__ constexpr bool head_dim_supported(int D) {
+  return D == 32 || D == 64 || D == 96 || D == 128 || D == 160 || D == 192 || D == 256 ||
+         D == 512;
+}
+__host__ __device__ constexpr int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p *= 2;
+  return p;
+}
+// Lanes that read one fp16 key row in the VALU kernels: one per 16 bytes, rounded up to
+// a power of two (lanes past D/8 hold no dims).
+__host__ __device__ constexpr int fp16_row_lanes(int D) { return pow2_ceil(D / 8); }
 constexpr int kGatherChunk = 2048;  // token-list positions per span
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -85,7 +85,10 @@ bool sid_ok(const char *sid) {
   return n >= 1 && n <= 255;
 }
 
-bool d_supported(int D) { return D == 64 || D == 128 || D == 256; }
+bool d_supported(int D) { return head_dim_supported(D); }
+// Head dims of the MFMA kernels (batched-Q prefill and grouped-query decode); a query
+// at another head dim runs on the split kernels.
+bool mfma_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
 size_t max_slots() {
   static size_t v = [] {
@@ -111,14 +114,14 @@ int split_target(bool mlx4) {
 }
 
 // A row group whose keys fit in this many tile passes of the fp16 kernel (4 waves, each
-// 2048 / D keys per pass) runs as one span: the serial passes cost less than the store,
-// ticket and merge of a split.
+// 4 x 64 / LPR keys per pass, LPR lanes per key row) runs as one span: the serial passes
+// cost less than the store, ticket and merge of a split.
 int one_span_keys(int D) {
   static int iters = [] {
     const char *e = getenv("PION_ONE_SPAN_ITERS");
     return e ? std::max(0, atoi(e)) : 3;
   }();
-  return iters * 4 * (2048 / D);
+  return iters * 4 * (256 / fp16_row_lanes(D));
 }
 
 bool getenv_flag(const char *name) {
@@ -349,6 +352,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   // (the MFMA kernel addresses a kv-head's K, V and suffix through 32-bit buffer ranges)
   const long long row_bytes = 2LL * c.D;
   if (slots.size() == 1 && slots[0]->fmt == PION_KV_FP16 && !c.blocks && c.M >= kMfmaMinRows &&
+      mfma_dim(c.D) &&
       slots[0]->N * row_bytes < (1LL << 31) && c.S_suf * row_bytes < (1LL << 31) &&
       !getenv_flag("PION_NO_MFMA"))
     return run_prefill(*slots[0], c, st);
@@ -441,7 +445,8 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     // PION_NO_GQA_MFMA turns it off. It addresses a kv-head's K, V and suffix through
     // 32-bit buffer ranges.
     const long long row_bytes = 2LL * c.D;
-    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && N_max * row_bytes < (1LL << 31) &&
+    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && mfma_dim(c.D) &&
+                        N_max * row_bytes < (1LL << 31) &&
                         (long long)c.S_suf * row_bytes < (1LL << 31) &&
                         !getenv_flag("PION_NO_GQA_MFMA");
     const bool gqa = gqa_ok && ((grp_rows >= 6 && c.D <= 128) || getenv_flag("PION_GQA_MFMA"));
@@ -518,6 +523,9 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
   if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
   const size_t elems = (size_t)H * N * D;
   if ((size_t)N * D > ((size_t)1 << 40)) return PION_ERR_INVALID;
+  // the mlx4g32 kernel addresses a kv-head's codes (N * D / 2 bytes) through a 32-bit
+  // buffer range
+  if (kv_format == PION_KV_MLX4G32 && (size_t)N * D >= ((size_t)1 << 33)) return PION_ERR_UNSUPPORTED;
   if (!aligned(K, 16) || !aligned(V, 16)) return PION_ERR_INVALID;
   if (!on_device(K) || !on_device(V)) return PION_ERR_INVALID;
   hipStream_t st = (hipStream_t)stream;

@@ -58,16 +58,16 @@ __device__ __forceinline__ float add_swapped(float v, bool by32) {
                       : __builtin_amdgcn_permlane16_swap(u, u, false, false);
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
-// Sum over each aligned group of W lanes (W = 16, 32 or 64), in every lane of the group:
-// quad sums, row half-mirror and row mirror give the 16-lane sum; the row swaps pair
-// rows 16 and 32 apart. Every group adds in the same order, so a group's result depends
+// Sum over each aligned group of W lanes (W = 8 .. 64), in every lane of the group:
+// quad sums and row half-mirror give the 8-lane sum, row mirror the 16-lane sum; the
+// row swaps pair rows 16 and 32 apart. Every group adds in the same order, so a group's result depends
 // only on its own values.
 template <int W>
 __device__ __forceinline__ float lane_sum(float v) {
   v += dpp_f<0xB1>(v);
   v += dpp_f<0x4E>(v);
   v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
+  if constexpr (W >= 16) v += dpp_f<0x140>(v);
   if constexpr (W >= 32) v = add_swapped(v, false);
   if constexpr (W >= 64) v = add_swapped(v, true);
   return v;
@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
                                                            int nb, int K_top, uint32_t *keys,
                                                            uint64_t *cand, int *counters,
                                                            int32_t *__restrict__ blocks) {
-  constexpr int LPB = D / 4 < 64 ? D / 4 : 64;  // lanes per block row
+  // lanes per block row: the largest power of two (at most 64) that divides D / 4, so
+  // that each lane holds F whole float4 of the row
+  constexpr int LPB = (D / 4) % 64 == 0 ? 64 : (D / 4) % 32 == 0 ? 32 : (D / 4) % 16 == 0 ? 16 : 8;
   constexpr int F = D / (4 * LPB);              // float4 per lane
   constexpr int RPL = 64 / LPB;                 // block rows per wave load
   constexpr int NL = kSelBlocks / 4 / RPL;      // wave loads
@@ -360,22 +362,24 @@ hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float
                                uint64_t *cand, int *counters, int32_t *blocks, hipStream_t s) {
   if (K_top < 1 || nb < 1 || H_kv < 1) return hipErrorInvalidValue;
   dim3 grid((nb + kSelBlocks - 1) / kSelBlocks, H_kv);
+#define PION_SELECT_D(DD)                                                                    \
+  case DD:                                                                                 \
+    hipLaunchKernelGGL(block_select_kernel<DD>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top, \
+                       keys, cand, counters, blocks);                                      \
+    break;
   switch (D) {
-    case 64:
-      hipLaunchKernelGGL(block_select_kernel<64>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, cand, counters, blocks);
-      break;
-    case 128:
-      hipLaunchKernelGGL(block_select_kernel<128>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, cand, counters, blocks);
-      break;
-    case 256:
-      hipLaunchKernelGGL(block_select_kernel<256>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top,
-                         keys, cand, counters, blocks);
-      break;
+    PION_SELECT_D(32)
+    PION_SELECT_D(64)
+    PION_SELECT_D(96)
+    PION_SELECT_D(128)
+    PION_SELECT_D(160)
+    PION_SELECT_D(192)
+    PION_SELECT_D(256)
+    PION_SELECT_D(512)
     default:
       return hipErrorInvalidValue;
   }
+#undef PION_SELECT_D
   return hipGetLastError();
 }
 

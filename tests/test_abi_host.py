@@ -65,7 +65,11 @@ def test_store_argument_validation(lib):
     assert st(b"s", 0, 2, 8, 64, None, FAKE, 0, None) == kp.PION_ERR_INVALID
     assert st(b"s", 0, 2, 8, 64, FAKE, FAKE, 7, None) == kp.PION_ERR_INVALID
     assert st(b"s", 0, 2, 8, 48, FAKE, FAKE, 1, None) == kp.PION_ERR_INVALID    # D % 32
-    assert st(b"s", 0, 2, 8, 96, FAKE, FAKE, 0, None) == kp.PION_ERR_UNSUPPORTED
+    assert st(b"s", 0, 2, 8, 48, FAKE, FAKE, 0, None) == kp.PION_ERR_UNSUPPORTED  # D set
+    for D in (32, 96, 160, 192, 512):  # supported: fails later, on the fake pointers
+        assert st(b"s", 0, 2, 8, D, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID
+    # mlx4g32 codes of one kv-head past a 32-bit buffer range
+    assert st(b"s", 0, 1, 1 << 24, 512, FAKE, FAKE, 1, None) == kp.PION_ERR_UNSUPPORTED
     # a host pointer is not device memory
     buf = np.zeros(2 * 8 * 64, np.float16)
     hp = ctypes.c_void_p(buf.ctypes.data)
