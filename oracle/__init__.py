@@ -10,6 +10,7 @@ Parity pins (what each function is checked against, besides itself) live in
 merge consistency), the causal alignment for M < S_suf (the plain bottom-right
 reading), and ``top_k`` / ``fa_window`` (not implemented).
 """
+from .cold_tier import ColdTier
 from .attention import (attend, combine, f64, merge, prefix_query, prefix_query_fused,
                         resolve_head_map, softmax_scale, suffix_visible)
 from .mlx4g32 import dequantize, quantize, record_bytes, unpack_codes
@@ -17,6 +18,7 @@ from .sparse import (block_means, block_scores, n_blocks, prefix_query_blocks,
                      prefix_query_sparse, prefix_query_sparse_auto, select_blocks)
 
 __all__ = [
+    "ColdTier",
     "attend", "combine", "f64", "merge", "prefix_query", "prefix_query_fused",
     "resolve_head_map", "softmax_scale", "suffix_visible", "dequantize", "quantize",
     "record_bytes", "unpack_codes", "block_means", "block_scores", "n_blocks", "prefix_query_blocks",
