@@ -38,18 +38,34 @@
 extern "C" {
 #endif
 
-/* Status codes. The wire's "-ERR session not found" is PION_ERR_NOT_FOUND; +HIT/+MISS
- * are the 1/0 results of pion_prefix_lookup (ATTEND.* page, ATTEND.PREFIX.LOOKUP row;
- * "Shared KV Cache Serving", Cold-tier state machine). PION_ERR_COLDMISS is reserved:
- * this library keeps no cold tier, so it never returns it. */
+/* Status codes. The wire's "-ERR session not found" is PION_ERR_NOT_FOUND and its
+ * "-COLDMISS" is PION_ERR_COLDMISS; +HIT/+COLD/+MISS are the 1/2/0 results of
+ * pion_prefix_lookup (ATTEND.* page, ATTEND.PREFIX.LOOKUP row; "Shared KV Cache
+ * Serving", Cold-tier state machine).
+ *
+ * Capacity and cold tier (same section). The slot table holds at most max_slots slots
+ * and, when max_bytes > 0, at most max_bytes of resident K/V bytes (block-mean caches
+ * not counted); defaults 4096 slots, no byte budget, 1024 cold entries (env
+ * PION_MAX_SLOTS, PION_MAX_BYTES, PION_COLD_SLOTS at load; pion_prefix_set_capacity).
+ * Every store and every successful query stamps its slot(s) with a logical clock. A
+ * store that would exceed the capacity first demotes the least recently stamped slots
+ * (never the key being stored): each one's device memory is released and its shape
+ * moves to the cold registry (WARM -> COLD). When the registry overflows, its least
+ * recently stamped entry is forgotten (MISSING). A query of a cold key returns
+ * PION_ERR_COLDMISS and changes nothing; storing it again (from the caller's copy of
+ * K/V) makes it warm and the most recent (COLD -> WARM, a rehydrate). Lookups, info and
+ * failed queries stamp nothing. A device allocation failure also demotes, least
+ * recently used first, before NOMEM is returned. Demotion frees memory that queued
+ * work may still read only after that work has finished. */
 enum {
     PION_OK = 0,
-    PION_ERR_NOT_FOUND = -1,   /* no resident slot for (sid, layer) */
+    PION_ERR_NOT_FOUND = -1,   /* no slot for (sid, layer), warm or cold */
     PION_ERR_INVALID = -2,     /* bad argument: null pointer, shape mismatch, range */
     PION_ERR_UNSUPPORTED = -3, /* valid request this build does not implement (D, ...) */
-    PION_ERR_NOMEM = -4,       /* device allocation failed or slot table full */
+    PION_ERR_NOMEM = -4,       /* device memory short with nothing left to demote, or
+                                  a slot larger than the byte budget */
     PION_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
-    PION_ERR_COLDMISS = -6     /* reserved (cold tier) */
+    PION_ERR_COLDMISS = -6     /* the key was demoted to the cold tier: store it again */
 };
 
 /* Resident formats. FP16 keeps K and V as given. MLX4G32 is the int4 group-32 affine
@@ -59,28 +75,49 @@ enum { PION_KV_FP16 = 0, PION_KV_MLX4G32 = 1 };
 
 /* ATTEND.PREFIX.STORE <sid> <layer> <H> <N> <D> <K_blob> <V_blob>.
  * Copies K and V, fp16 [H, N, D] each, into a library-owned slot keyed (sid, layer)
- * and keeps them resident until pion_prefix_drop or library unload (the command
- * table: "resident until DROP"). Storing a live key replaces its slot and drops any
- * cached block means. The library owns the slot memory; K and V may be freed once
+ * and keeps them resident until pion_prefix_drop, demotion (see Capacity above) or
+ * library unload (the command table: "resident until DROP"). Storing a live key
+ * replaces its slot and drops any cached block means; storing a cold key rehydrates it. The library owns the slot memory; K and V may be freed once
  * `stream` has passed the call. sid is a NUL-terminated string of 1..255 bytes.
  * Errors: INVALID (null/empty sid, H/N/D <= 0, H > 255, kv_format unknown, D % 32 != 0
- * for MLX4G32), UNSUPPORTED (D; MLX4G32 with N * D >= 2^33), NOMEM (allocation, or more than PION_MAX_SLOTS slots;
- * default 4096, env PION_MAX_SLOTS), HIP. */
+ * for MLX4G32), UNSUPPORTED (D; MLX4G32 with N * D >= 2^33), NOMEM (larger than the
+ * byte budget, or device memory short with nothing left to demote; a cold key stays
+ * cold), HIP. */
 int pion_prefix_store(const char *sid, int layer, int H, int N, int D,
                       const void *K, const void *V, int kv_format, void *stream);
 
-/* ATTEND.PREFIX.LOOKUP <sid> <layer> -> 1 (+HIT) if a slot exists, 0 (+MISS) if not,
- * PION_ERR_INVALID for a null sid. Host-only. */
+/* ATTEND.PREFIX.LOOKUP <sid> <layer> -> 1 (+HIT) if a warm slot exists, 2 (+COLD) if
+ * the key is in the cold registry, 0 (+MISS) otherwise; PION_ERR_INVALID for a null
+ * sid. Host-only; stamps nothing. */
 int pion_prefix_lookup(const char *sid, int layer);
 
-/* Frees the slot (sid, layer); layer < 0 frees every layer of sid. Returns the number
- * of slots freed (0 if none: dropping an absent key is not an error), or INVALID.
- * Waits for queued work on the device before freeing. */
+/* Frees the slot (sid, layer), warm or cold; layer < 0 frees every layer of sid.
+ * Returns the number of keys removed (0 if none: dropping an absent key is not an
+ * error), or INVALID. Waits for queued work on the device before freeing. */
 int pion_prefix_drop(const char *sid, int layer);
 
 /* Shape of a resident slot: writes H, N, D and kv_format (any pointer may be NULL).
- * NOT_FOUND if absent. Host-only. */
+ * For a cold key writes the shape it had and returns COLDMISS; NOT_FOUND if absent.
+ * Host-only. */
 int pion_prefix_info(const char *sid, int layer, int *H, int *N, int *D, int *kv_format);
+
+/* Slot-table telemetry (the KV.PREFIX.INFO cold-tier fields of "Shared KV Cache
+ * Serving": live slots, demoted entries, lifetime demotions and rehydrates), plus the
+ * resident K/V bytes and the capacity in force. Host-only. */
+typedef struct {
+    int64_t warm_slots;      /* live (warm) slots */
+    int64_t cold_slots;      /* entries in the cold registry */
+    int64_t demotions;       /* lifetime WARM -> COLD transitions */
+    int64_t rehydrates;      /* lifetime COLD -> WARM transitions */
+    int64_t resident_bytes;  /* device K/V bytes of the warm slots */
+    int64_t max_slots, max_bytes, cold_capacity;
+} pion_prefix_stats_t;
+int pion_prefix_stats(pion_prefix_stats_t *stats);
+
+/* Sets the capacity (max_slots >= 1; max_bytes >= 0, 0 = no byte budget; cold_slots
+ * >= 0) and demotes least recently used slots at once until it holds (then trims the
+ * cold registry). INVALID for out-of-range values. */
+int pion_prefix_set_capacity(int64_t max_slots, int64_t max_bytes, int64_t cold_slots);
 
 /* ATTEND.PREFIX.QUERY <sid> <layer> <H> <D> <top_k> <Q_blob>, in its M=1 and batched-Q
  * forms ("Shared KV Cache Serving", Wire-protocol details: Q is (H, M, D), the reply is
@@ -92,7 +129,8 @@ int pion_prefix_info(const char *sid, int layer, int *H, int *N, int *D, int *kv
  *   lse      fp32 [H_q, M] or NULL.
  * top_k and fa_window are not taken: the pages measure only top_k = N (dense).
  * Errors: INVALID (pointers, M < 1, H_q < 1 or > 128, D != stored D, head_map entry
- * outside [0, H_kv), H_kv not dividing H_q without a head_map), NOT_FOUND, HIP. */
+ * outside [0, H_kv), H_kv not dividing H_q without a head_map), NOT_FOUND, COLDMISS,
+ * HIP. Every query form below also returns COLDMISS for a cold key. */
 int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M,
                       const void *Q, const int32_t *head_map,
                       float *out, float *lse, void *stream);

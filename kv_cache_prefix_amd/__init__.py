@@ -32,6 +32,8 @@ SIGNATURES = {
     "pion_prefix_lookup": (_int, [_c_char_p, _int]),
     "pion_prefix_drop": (_int, [_c_char_p, _int]),
     "pion_prefix_info": (_int, [_c_char_p, _int, _vp, _vp, _vp, _vp]),
+    "pion_prefix_stats": (_int, [_vp]),
+    "pion_prefix_set_capacity": (_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "pion_prefix_query": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "pion_prefix_query_layers": (_int, [_c_char_p, _int, _int, _int, _int, _int, _vp, _vp, _vp,
                                         _vp, _vp]),
@@ -138,6 +140,25 @@ def pion_prefix_info(sid, layer: int):
     rc = lib().pion_prefix_info(_sid(sid), layer, *[ctypes.byref(v) for v in vals])
     _check(rc, "pion_prefix_info")
     return tuple(v.value for v in vals)   # (H, N, D, kv_format)
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "warm_slots", "cold_slots", "demotions", "rehydrates", "resident_bytes",
+        "max_slots", "max_bytes", "cold_capacity")]
+
+
+def pion_prefix_stats() -> dict:
+    """Slot-table telemetry: warm/cold counts, lifetime demotions and rehydrates,
+    resident K/V bytes and the capacity in force."""
+    st = _Stats()
+    _check(lib().pion_prefix_stats(ctypes.byref(st)), "pion_prefix_stats")
+    return {n: getattr(st, n) for n, _ in _Stats._fields_}
+
+
+def pion_prefix_set_capacity(max_slots: int, max_bytes: int = 0, cold_slots: int = 1024) -> int:
+    return _check(lib().pion_prefix_set_capacity(max_slots, max_bytes, cold_slots),
+                  "pion_prefix_set_capacity")
 
 
 def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=None) -> int:

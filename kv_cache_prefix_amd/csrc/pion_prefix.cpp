@@ -8,6 +8,14 @@
 // mlx4g32 arrays (codes [H, N, D/8] and (scale, bias) pairs [H, N, D/32], per side),
 // plus the per-B block-mean cache of the sparse-auto query.
 //
+// Capacity and cold tier ("Shared KV Cache Serving", Cold-tier state machine): the
+// table holds at most a number of slots and, optionally, a budget of resident K/V
+// bytes. A store that would exceed either first demotes the least recently used
+// slots (last access = a logical clock advanced by every store and successful query):
+// their device memory is released and their shape kept in a bounded cold registry.
+// A query of a cold key answers PION_ERR_COLDMISS, a lookup answers 2 (+COLD); a store
+// of a cold key makes it warm again (a rehydrate) and the most recent.
+//
 // Launch plan of an attention call: one split-KV kernel (fp16 or mlx4g32 prefix; an
 // mlx4g32 prefix with an fp16 suffix takes one launch of each) over workgroups (key
 // span, q-head group sharing one kv-head, query index); each writes (acc, m, l) per (row,
@@ -52,6 +60,7 @@ struct Slot {
   int H = 0, N = 0, D = 0, fmt = 0;
   void *mem = nullptr;
   size_t bytes = 0;
+  uint64_t last = 0;  // logical clock of the last store or successful query
   KVView view{};
   hipEvent_t ready = nullptr;
   hipStream_t stream = nullptr;
@@ -67,8 +76,15 @@ struct Workspace {
 
 constexpr int kMaxCounters = 65536;  // one per workgroup row (grid.y <= 65535)
 
+// A demoted slot: its shape and last access (the K/V bytes are gone).
+struct ColdEntry {
+  int H = 0, N = 0, D = 0, fmt = 0;
+  uint64_t last = 0;
+};
+
 std::mutex g_mu;
 std::unordered_map<std::string, Slot> g_slots;
+std::unordered_map<std::string, ColdEntry> g_cold;
 std::unordered_map<hipStream_t, Workspace> g_ws;      // split partials
 std::unordered_map<hipStream_t, Workspace> g_sel_ws;  // sparse-auto scores and picks
 
@@ -90,14 +106,21 @@ bool d_supported(int D) { return head_dim_supported(D); }
 // at another head dim runs on the split kernels.
 bool mfma_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
-size_t max_slots() {
-  static size_t v = [] {
-    const char *e = getenv("PION_MAX_SLOTS");
-    long x = e ? atol(e) : 4096;
-    return (size_t)(x > 0 ? x : 4096);
-  }();
-  return v;
+// Capacity (env PION_MAX_SLOTS, PION_MAX_BYTES, PION_COLD_SLOTS at load; then
+// pion_prefix_set_capacity) and the cold-tier counters; all under g_mu.
+long long env_ll(const char *name, long long dflt, long long lo) {
+  const char *e = getenv(name);
+  const long long x = e ? atoll(e) : dflt;
+  return x >= lo ? x : dflt;
 }
+struct Tier {
+  long long max_slots = env_ll("PION_MAX_SLOTS", 4096, 1);
+  long long max_bytes = env_ll("PION_MAX_BYTES", 0, 0);  // 0: no byte budget
+  long long cold_slots = env_ll("PION_COLD_SLOTS", 1024, 0);
+  uint64_t clock = 0;
+  long long demotions = 0, rehydrates = 0;
+  size_t resident = 0;  // K/V bytes of the warm slots
+} g_tier;
 
 // Workgroups a launch aims for when it splits keys. fp16 prefix: two per CU of the
 // MI355X (512): the kernel holds few bytes in flight per wave, and cold-HBM bandwidth
@@ -155,6 +178,45 @@ void free_slot(Slot &s) {
   s.mem = nullptr;
   s.ready = nullptr;
 }
+
+void trim_cold() {
+  while ((long long)g_cold.size() > g_tier.cold_slots) {
+    auto old = g_cold.begin();
+    for (auto it = g_cold.begin(); it != g_cold.end(); ++it)
+      if (it->second.last < old->second.last) old = it;
+    g_cold.erase(old);
+  }
+}
+
+// Demote the least recently used warm slot other than `keep`: free its memory, keep its
+// shape in the cold registry. False when there is none.
+bool demote_lru(const std::string &keep) {
+  auto lru = g_slots.end();
+  for (auto it = g_slots.begin(); it != g_slots.end(); ++it)
+    if (it->first != keep && (lru == g_slots.end() || it->second.last < lru->second.last)) lru = it;
+  if (lru == g_slots.end()) return false;
+  Slot &s = lru->second;
+  ColdEntry c;
+  c.H = s.H;
+  c.N = s.N;
+  c.D = s.D;
+  c.fmt = s.fmt;
+  c.last = s.last;
+  g_tier.resident -= s.bytes;
+  free_slot(s);
+  g_cold[lru->first] = c;
+  g_slots.erase(lru);
+  ++g_tier.demotions;
+  trim_cold();
+  return true;
+}
+
+// Status of a query whose key has no warm slot.
+int absent_status(const char *sid, int layer) {
+  return g_cold.count(key_of(sid, layer)) ? PION_ERR_COLDMISS : PION_ERR_NOT_FOUND;
+}
+
+void touch(Slot *s) { s->last = ++g_tier.clock; }
 
 // Make `st` wait for work recorded on another stream (store or block-mean build).
 hipError_t order_after(hipEvent_t ev, hipStream_t src, bool &done, hipStream_t st) {
@@ -530,21 +592,47 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
   if (!on_device(K) || !on_device(V)) return PION_ERR_INVALID;
   hipStream_t st = (hipStream_t)stream;
 
+  const SlotLayout L = slot_layout(kv_format, H, N, D);
   std::lock_guard<std::mutex> lk(g_mu);
+  if (g_tier.max_bytes > 0 && L.bytes > (size_t)g_tier.max_bytes) return PION_ERR_NOMEM;
   const std::string key = key_of(sid, layer);
-  const bool replacing = g_slots.count(key) > 0;
-  if (!replacing && g_slots.size() >= max_slots()) return PION_ERR_NOMEM;
+  auto old = g_slots.find(key);
+  const bool replacing = old != g_slots.end();
+  const size_t old_bytes = replacing ? old->second.bytes : 0;
+  // a cold key leaves the registry now (so that demotions below cannot drop it); it is
+  // put back if the store fails
+  ColdEntry was_cold;
+  auto ci = g_cold.find(key);
+  const bool rehydrate = ci != g_cold.end();
+  if (rehydrate) {
+    was_cold = ci->second;
+    g_cold.erase(ci);
+  }
+  auto fail = [&](int rc) {
+    if (rehydrate) {
+      g_cold[key] = was_cold;
+      trim_cold();
+    }
+    return rc;
+  };
+  // room: demote least recently used slots until the count and the byte budget hold
+  // (a replaced slot's bytes count as freed)
+  while ((long long)(g_slots.size() - (replacing ? 1 : 0) + 1) > g_tier.max_slots ||
+         (g_tier.max_bytes > 0 &&
+          g_tier.resident - old_bytes + L.bytes > (size_t)g_tier.max_bytes))
+    if (!demote_lru(key)) break;
 
   Slot sl;
   sl.H = H;
   sl.N = N;
   sl.D = D;
   sl.fmt = kv_format;
-  const SlotLayout L = slot_layout(kv_format, H, N, D);
   sl.bytes = L.bytes;
-  if (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
+  // device memory short: demote further, least recently used first
+  while (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
     (void)hipGetLastError();
-    return PION_ERR_NOMEM;
+    sl.mem = nullptr;
+    if (!demote_lru(key)) return fail(PION_ERR_NOMEM);
   }
   char *base = (char *)sl.mem;
   sl.view = make_view(sl.mem, kv_format, H, N, D);
@@ -568,10 +656,16 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
   if (e != hipSuccess) {
     (void)hipGetLastError();
     free_slot(sl);
-    return PION_ERR_HIP;
+    return fail(PION_ERR_HIP);
   }
   sl.stream = st;
-  if (replacing) free_slot(g_slots[key]);
+  if (replacing) {
+    g_tier.resident -= old_bytes;
+    free_slot(g_slots[key]);
+  }
+  if (rehydrate) ++g_tier.rehydrates;
+  g_tier.resident += sl.bytes;
+  sl.last = ++g_tier.clock;
   g_slots[key] = sl;
   return PION_OK;
 }
@@ -579,7 +673,7 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
 int pion_prefix_lookup(const char *sid, int layer) {
   if (!sid_ok(sid)) return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
-  return find_slot(sid, layer) ? 1 : 0;
+  return find_slot(sid, layer) ? 1 : g_cold.count(key_of(sid, layer)) ? 2 : 0;
 }
 
 int pion_prefix_drop(const char *sid, int layer) {
@@ -587,19 +681,30 @@ int pion_prefix_drop(const char *sid, int layer) {
   std::lock_guard<std::mutex> lk(g_mu);
   int n = 0;
   if (layer >= 0) {
-    auto it = g_slots.find(key_of(sid, layer));
+    const std::string key = key_of(sid, layer);
+    auto it = g_slots.find(key);
     if (it != g_slots.end()) {
+      g_tier.resident -= it->second.bytes;
       free_slot(it->second);
       g_slots.erase(it);
       n = 1;
     }
-    return n;
+    return n + (int)g_cold.erase(key);
   }
   const std::string prefix = std::string(sid) + '\0';
   for (auto it = g_slots.begin(); it != g_slots.end();) {
     if (it->first.compare(0, prefix.size(), prefix) == 0) {
+      g_tier.resident -= it->second.bytes;
       free_slot(it->second);
       it = g_slots.erase(it);
+      ++n;
+    } else {
+      ++it;
+    }
+  }
+  for (auto it = g_cold.begin(); it != g_cold.end();) {
+    if (it->first.compare(0, prefix.size(), prefix) == 0) {
+      it = g_cold.erase(it);
       ++n;
     } else {
       ++it;
@@ -612,11 +717,46 @@ int pion_prefix_info(const char *sid, int layer, int *H, int *N, int *D, int *kv
   if (!sid_ok(sid)) return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
   const Slot *s = find_slot(sid, layer);
-  if (!s) return PION_ERR_NOT_FOUND;
+  if (!s) {
+    auto c = g_cold.find(key_of(sid, layer));
+    if (c == g_cold.end()) return PION_ERR_NOT_FOUND;
+    if (H) *H = c->second.H;  // the shape the demoted slot had
+    if (N) *N = c->second.N;
+    if (D) *D = c->second.D;
+    if (kv_format) *kv_format = c->second.fmt;
+    return PION_ERR_COLDMISS;
+  }
   if (H) *H = s->H;
   if (N) *N = s->N;
   if (D) *D = s->D;
   if (kv_format) *kv_format = s->fmt;
+  return PION_OK;
+}
+
+int pion_prefix_stats(pion_prefix_stats_t *out) {
+  if (!out) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  out->warm_slots = (int64_t)g_slots.size();
+  out->cold_slots = (int64_t)g_cold.size();
+  out->demotions = g_tier.demotions;
+  out->rehydrates = g_tier.rehydrates;
+  out->resident_bytes = (int64_t)g_tier.resident;
+  out->max_slots = g_tier.max_slots;
+  out->max_bytes = g_tier.max_bytes;
+  out->cold_capacity = g_tier.cold_slots;
+  return PION_OK;
+}
+
+int pion_prefix_set_capacity(int64_t max_slots, int64_t max_bytes, int64_t cold_slots) {
+  if (max_slots < 1 || max_bytes < 0 || cold_slots < 0) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_tier.max_slots = max_slots;
+  g_tier.max_bytes = max_bytes;
+  g_tier.cold_slots = cold_slots;
+  while ((long long)g_slots.size() > g_tier.max_slots ||
+         (g_tier.max_bytes > 0 && g_tier.resident > (size_t)g_tier.max_bytes))
+    if (!demote_lru(std::string())) break;
+  trim_cold();
   return PION_OK;
 }
 
@@ -627,7 +767,7 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const v
   if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
   Slot *sl = find_slot(sid, layer);
-  if (!sl) return PION_ERR_NOT_FOUND;
+  if (!sl) return absent_status(sid, layer);
   if (sl->D != D) return PION_ERR_INVALID;
   std::vector<int> hm;
   if (!resolve_map(head_map, H_q, sl->H, hm)) return PION_ERR_INVALID;
@@ -643,7 +783,9 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const v
   c.H_kv = sl->H;
   c.out = out;
   c.lse = lse;
-  return run_attention({sl}, c, st);
+  rc = run_attention({sl}, c, st);
+  if (rc == PION_OK) touch(sl);
+  return rc;
 }
 
 int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q, int D, int M,
@@ -657,7 +799,7 @@ int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q,
   std::vector<const Slot *> slots(n_layers);
   for (int i = 0; i < n_layers; ++i) {
     Slot *sl = find_slot(sid, layer0 + i);
-    if (!sl) return PION_ERR_NOT_FOUND;
+    if (!sl) return absent_status(sid, layer0 + i);
     slots[i] = sl;
   }
   const Slot &s0 = *slots[0];
@@ -683,7 +825,10 @@ int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q,
   c.out_stride = (size_t)H_q * M * D;
   c.lse = lse;
   c.lse_stride = (size_t)H_q * M;
-  return run_attention(slots, c, st);
+  rc = run_attention(slots, c, st);
+  if (rc == PION_OK)
+    for (int i = 0; i < n_layers; ++i) touch(find_slot(sid, layer0 + i));
+  return rc;
 }
 
 int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, int S_suf,
@@ -699,7 +844,7 @@ int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, i
   if (!resolve_map(head_map, H_q, H_kv, hm)) return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
   Slot *sl = find_slot(sid, layer);
-  if (!sl) return PION_ERR_NOT_FOUND;
+  if (!sl) return absent_status(sid, layer);
   if (sl->D != D || sl->H != H_kv) return PION_ERR_INVALID;
   if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
   if (S_suf > 0 && (!on_device(K_suf) || !on_device(V_suf))) return PION_ERR_INVALID;
@@ -717,7 +862,9 @@ int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, i
   c.S_suf = S_suf;
   c.out = out;
   c.lse = lse;
-  return run_attention({sl}, c, st);
+  rc = run_attention({sl}, c, st);
+  if (rc == PION_OK) touch(sl);
+  return rc;
 }
 
 int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, int B, int K_top,
@@ -736,7 +883,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   if (!resolve_map(head_map, H_q, H_kv, hm)) return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
   Slot *sl = find_slot(sid, layer);
-  if (!sl) return PION_ERR_NOT_FOUND;
+  if (!sl) return absent_status(sid, layer);
   if (sl->D != D || sl->H != H_kv) return PION_ERR_INVALID;
   if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
   if (S_suf > 0 && (!on_device(K_suf) || !on_device(V_suf))) return PION_ERR_INVALID;
@@ -822,7 +969,9 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   c.B = B;
   c.out = out;
   c.lse = lse;
-  return run_attention({sl}, c, st);
+  rc = run_attention({sl}, c, st);
+  if (rc == PION_OK) touch(sl);
+  return rc;
 }
 
 int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_sparse_max,
@@ -835,7 +984,7 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
     return PION_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_mu);
   Slot *sl = find_slot(sid, layer);
-  if (!sl) return PION_ERR_NOT_FOUND;
+  if (!sl) return absent_status(sid, layer);
   if (sl->D != D || sl->H != H) return PION_ERR_INVALID;
   if (sl->fmt != PION_KV_FP16) return PION_ERR_UNSUPPORTED;
   if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse)) || !on_device(indices) ||
@@ -857,7 +1006,9 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
   c.gmax = K_sparse_max;
   c.out = out;
   c.lse = lse;
-  return run_attention({sl}, c, st);
+  rc = run_attention({sl}, c, st);
+  if (rc == PION_OK) touch(sl);
+  return rc;
 }
 
 }  // extern "C"

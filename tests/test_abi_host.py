@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -50,6 +50,22 @@ def test_lookup_and_drop_of_absent_session(lib):
     assert lib.pion_prefix_lookup(b"x" * 256, 0) == kp.PION_ERR_INVALID
     H = ctypes.c_int()
     assert lib.pion_prefix_info(b"nope", 0, ctypes.byref(H), None, None, None) == kp.PION_ERR_NOT_FOUND
+
+
+def test_capacity_and_stats_without_slots(lib):
+    assert lib.pion_prefix_stats(None) == kp.PION_ERR_INVALID
+    set_cap = lib.pion_prefix_set_capacity
+    assert set_cap(0, 0, 0) == kp.PION_ERR_INVALID          # at least one slot
+    assert set_cap(5, -1, 0) == kp.PION_ERR_INVALID
+    assert set_cap(5, 0, -1) == kp.PION_ERR_INVALID
+    before = kp.pion_prefix_stats()
+    assert set_cap(5, 1 << 20, 3) == kp.PION_OK
+    s = kp.pion_prefix_stats()
+    assert (s["max_slots"], s["max_bytes"], s["cold_capacity"]) == (5, 1 << 20, 3)
+    assert s["warm_slots"] == s["cold_slots"] == s["resident_bytes"] == 0
+    assert s["demotions"] == before["demotions"] and s["rehydrates"] == before["rehydrates"]
+    assert set_cap(before["max_slots"], before["max_bytes"], before["cold_capacity"]) == kp.PION_OK
+    assert kp.status_str(kp.PION_ERR_COLDMISS) == "cold miss"
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
