@@ -11,6 +11,7 @@ merge consistency), the causal alignment for M < S_suf (the plain bottom-right
 reading), and ``top_k`` / ``fa_window`` (not implemented).
 """
 from .cold_tier import ColdTier
+from . import vstore
 from .attention import (attend, combine, f64, merge, prefix_query, prefix_query_fused,
                         resolve_head_map, softmax_scale, suffix_visible)
 from .mlx4g32 import dequantize, quantize, record_bytes, unpack_codes
@@ -18,7 +19,7 @@ from .sparse import (block_means, block_scores, n_blocks, prefix_query_blocks,
                      prefix_query_sparse, prefix_query_sparse_auto, select_blocks)
 
 __all__ = [
-    "ColdTier",
+    "ColdTier", "vstore",
     "attend", "combine", "f64", "merge", "prefix_query", "prefix_query_fused",
     "resolve_head_map", "softmax_scale", "suffix_visible", "dequantize", "quantize",
     "record_bytes", "unpack_codes", "block_means", "block_scores", "n_blocks", "prefix_query_blocks",
