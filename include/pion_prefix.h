@@ -202,6 +202,39 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
                              const void *Q, const int32_t *indices, const int32_t *counts,
                              float *out, float *lse, void *stream);
 
+/* V-store rows of one layer, as the rehydrate and fetch calls below take them: one row
+ * per token, kv_dim = H * D values wide, either
+ *   PION_KV_FP16     fp16 [n_rows, kv_dim] (16-byte aligned), or
+ *   PION_KV_MLX4G32  the per-token record of the V-store page ("The mlx4g32 tier"):
+ *                    kv_dim/8 uint32 code words, then kv_dim/32 fp16 scales, then
+ *                    kv_dim/32 fp16 biases, little-endian, 5 * kv_dim / 8 bytes per
+ *                    token (4-byte aligned), as pion_kv_quantize_mlx4g32 encodes a row.
+ * Dequantized values are s * q + b rounded once to fp32 (an fp16 slot then rounds that
+ * to fp16, nearest even). */
+
+/* V.FETCH <sid> <layer> RANGE <start> <end> ("Shared KV Cache Serving"): the
+ * concatenated dequantized fp32 values of tokens start .. end - 1.
+ *   rows  device, n_rows V-store rows in format fmt (see above).
+ *   out   device fp32 [end - start, kv_dim], 16-byte aligned.
+ * Errors: INVALID (pointers, fmt, kv_dim <= 0 or not a multiple of 8 (fp16) / 32
+ * (mlx4g32), range outside [0, n_rows], alignment), HIP. An empty range is a no-op
+ * (rows and out may then be NULL). */
+int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim,
+                          int64_t start, int64_t end, float *out, void *stream);
+
+/* KV.PREFIX.WARM, one layer ("Shared KV Cache Serving"): rehydrate the slot (sid, layer)
+ * from the layer's V-store rows of K and of V (N tokens each, src_format, kv_dim = H * D),
+ * transposed from the V-store layout [N, H * D] into the STORE layout [H, N, D]:
+ *   kv_format FP16     the dequantized values (fp16 rows: the values themselves);
+ *   kv_format MLX4G32  from mlx4g32 rows: the codes, scales and biases unchanged (the same
+ *                      slot a STORE of the original fp16 K/V with MLX4G32 makes); from
+ *                      fp16 rows: encoded as pion_prefix_store does.
+ * The slot then behaves as one made by pion_prefix_store (capacity rules, replacing a
+ * live key, rehydrating a cold one). Errors: those of pion_prefix_store, and INVALID for
+ * an unknown src_format or a misaligned or non-device row pointer. */
+int pion_prefix_warm(const char *sid, int layer, int H, int N, int D, int src_format,
+                     const void *K_rows, const void *V_rows, int kv_format, void *stream);
+
 /* mlx4g32 encoder ("Shared KV Cache Serving", Quantized tier - mlx4g32; V-store page,
  * The mlx4g32 tier): int4 codes in groups of 32, affine, fp16 scale and bias per group,
  * the scale rounded to fp16 before codes are chosen. Per group, in fp32 with IEEE

@@ -44,6 +44,9 @@ SIGNATURES = {
     "pion_prefix_query_sparse": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
                                         _vp, _vp]),
     "pion_kv_quantize_mlx4g32": (_int, [_vp, ctypes.c_int64, _int, _vp, _vp, _vp, _vp]),
+    "pion_vstore_fetch_f32": (_int, [_vp, _int, ctypes.c_int64, _int, ctypes.c_int64,
+                                     ctypes.c_int64, _vp, _vp]),
+    "pion_prefix_warm": (_int, [_c_char_p, _int, _int, _int, _int, _int, _vp, _vp, _int, _vp]),
     "pion_status_str": (ctypes.c_char_p, [_int]),
 }
 
@@ -159,6 +162,42 @@ def pion_prefix_stats() -> dict:
 def pion_prefix_set_capacity(max_slots: int, max_bytes: int = 0, cold_slots: int = 1024) -> int:
     return _check(lib().pion_prefix_set_capacity(max_slots, max_bytes, cold_slots),
                   "pion_prefix_set_capacity")
+
+
+def _vstore_rows(rows, fmt: int, kv_dim: int, name: str) -> int:
+    """Pointer of a layer's V-store rows: fp16 [n, kv_dim] or uint8 mlx4g32 records
+    [n, 5 * kv_dim / 8]."""
+    import torch
+    fp16 = fmt == PION_KV_FP16
+    width = kv_dim if fp16 else kv_dim * 5 // 8
+    if rows.dim() != 2 or rows.shape[1] != width:
+        raise ValueError(f"{name} must be [n, {width}]")
+    return _dev(rows, torch.float16 if fp16 else torch.uint8, name)
+
+
+def pion_vstore_fetch_f32(rows, fmt: int, kv_dim: int, start: int, end: int, out,
+                          stream=None) -> int:
+    """V.FETCH RANGE: a layer's V-store rows (fp16 [n, kv_dim], or uint8 mlx4g32 records
+    [n, 5 * kv_dim / 8]) -> out fp32 [end - start, kv_dim]."""
+    import torch
+    rp = _vstore_rows(rows, fmt, kv_dim, "rows")
+    op = _dev(out, torch.float32, "out", (max(end - start, 0), kv_dim))
+    rc = lib().pion_vstore_fetch_f32(rp, fmt, rows.shape[0], kv_dim, start, end, op,
+                                     _stream(stream))
+    return _check(rc, "pion_vstore_fetch_f32")
+
+
+def pion_prefix_warm(sid, layer: int, H: int, D: int, K_rows, V_rows, src_format: int,
+                     kv_format: int = PION_KV_FP16, stream=None) -> int:
+    """KV.PREFIX.WARM for one layer: V-store rows of K and V (N tokens, src_format) ->
+    slot (sid, layer) in kv_format, layout [H, N, D]."""
+    kp_ = _vstore_rows(K_rows, src_format, H * D, "K_rows")
+    vp_ = _vstore_rows(V_rows, src_format, H * D, "V_rows")
+    if V_rows.shape != K_rows.shape:
+        raise ValueError("K_rows and V_rows must have the same shape")
+    rc = lib().pion_prefix_warm(_sid(sid), layer, H, K_rows.shape[0], D, src_format, kp_, vp_,
+                                kv_format, _stream(stream))
+    return _check(rc, "pion_prefix_warm")
 
 
 def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=None) -> int:

@@ -190,6 +190,18 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 
+// V-store rows of one layer (kv = H * D values per token): fmt 0 = fp16 [N, kv], fmt 1 =
+// mlx4g32 records of 5 * kv / 8 bytes. Fetch: fp32 [count, kv] of tokens start ..
+// start + count - 1. Relayout into a slot: fp16 [H, N, D] (dequantized and rounded for
+// fmt 1), or, from fmt 1, mlx4g32 codes [H, N, D/8] and (scale | bias << 16) pairs
+// [H, N, D/32].
+hipError_t launch_vstore_fetch(const void *rows, int fmt, int kv, int64_t start, int64_t count,
+                               float *out, hipStream_t s);
+hipError_t launch_rows_to_fp16_slot(const void *rows, int fmt, int64_t N, int H, int D,
+                                    uint16_t *dst, hipStream_t s);
+hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, uint32_t *codes,
+                                    uint32_t *pairs, hipStream_t s);
+
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);
 

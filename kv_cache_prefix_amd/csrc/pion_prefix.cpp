@@ -531,6 +531,107 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   return e == hipSuccess ? PION_OK : PION_ERR_HIP;
 }
 
+// Shape checks shared by STORE and WARM.
+int check_slot_shape(const char *sid, int H, int N, int D, int kv_format) {
+  if (!sid_ok(sid) || H < 1 || H > 255 || N < 1 || D <= 0) return PION_ERR_INVALID;
+  if (kv_format != PION_KV_FP16 && kv_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
+  if (kv_format == PION_KV_MLX4G32 && D % 32) return PION_ERR_INVALID;
+  if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
+  if ((size_t)N * D > ((size_t)1 << 40)) return PION_ERR_INVALID;
+  // the mlx4g32 kernel addresses a kv-head's codes (N * D / 2 bytes) through a 32-bit
+  // buffer range
+  if (kv_format == PION_KV_MLX4G32 && (size_t)N * D >= ((size_t)1 << 33)) return PION_ERR_UNSUPPORTED;
+  return PION_OK;
+}
+
+// Write a slot's arrays from fp16 K, V [H, N, D]: copies, or the mlx4g32 encoder with
+// scale and bias interleaved as (scale | bias << 16) words.
+hipError_t fill_from_fp16(char *base, const SlotLayout &L, int kv_format, const void *K,
+                          const void *V, size_t elems, int D, hipStream_t st) {
+  if (kv_format == PION_KV_FP16) {
+    hipError_t e = hipMemcpyAsync(base + L.off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+    return hipMemcpyAsync(base + L.off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
+  }
+  const int64_t rows = (int64_t)(elems / D);
+  uint16_t *ksb = (uint16_t *)(base + L.off[1]), *vsb = (uint16_t *)(base + L.off[3]);
+  hipError_t e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D,
+                                         (uint32_t *)(base + L.off[0]), ksb, ksb + 1, 2, st);
+  if (e != hipSuccess) return e;
+  return launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[2]), vsb,
+                                 vsb + 1, 2, st);
+}
+
+// Allocate the slot (sid, layer), let `fill` write its arrays on stream `st`, and install
+// it under the capacity rules: least recently used slots are demoted first when the
+// count or the byte budget would be exceeded, or when device memory is short; a
+// replaced slot is freed after the new one is ready; a cold key is rehydrated.
+template <typename Fill>
+int install_slot(const char *sid, int layer, int H, int N, int D, int kv_format, hipStream_t st,
+                 const Fill &fill) {
+  const SlotLayout L = slot_layout(kv_format, H, N, D);
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_tier.max_bytes > 0 && L.bytes > (size_t)g_tier.max_bytes) return PION_ERR_NOMEM;
+  const std::string key = key_of(sid, layer);
+  auto old = g_slots.find(key);
+  const bool replacing = old != g_slots.end();
+  const size_t old_bytes = replacing ? old->second.bytes : 0;
+  // a cold key leaves the registry now (so that demotions below cannot drop it); it is
+  // put back if the store fails
+  ColdEntry was_cold;
+  auto ci = g_cold.find(key);
+  const bool rehydrate = ci != g_cold.end();
+  if (rehydrate) {
+    was_cold = ci->second;
+    g_cold.erase(ci);
+  }
+  auto fail = [&](int rc) {
+    if (rehydrate) {
+      g_cold[key] = was_cold;
+      trim_cold();
+    }
+    return rc;
+  };
+  // room: demote least recently used slots until the count and the byte budget hold
+  // (a replaced slot's bytes count as freed)
+  while ((long long)(g_slots.size() - (replacing ? 1 : 0) + 1) > g_tier.max_slots ||
+         (g_tier.max_bytes > 0 &&
+          g_tier.resident - old_bytes + L.bytes > (size_t)g_tier.max_bytes))
+    if (!demote_lru(key)) break;
+
+  Slot sl;
+  sl.H = H;
+  sl.N = N;
+  sl.D = D;
+  sl.fmt = kv_format;
+  sl.bytes = L.bytes;
+  // device memory short: demote further, least recently used first
+  while (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    sl.mem = nullptr;
+    if (!demote_lru(key)) return fail(PION_ERR_NOMEM);
+  }
+  sl.view = make_view(sl.mem, kv_format, H, N, D);
+  hipError_t e = fill((char *)sl.mem, L, st);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(sl.ready, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free_slot(sl);
+    return fail(PION_ERR_HIP);
+  }
+  sl.stream = st;
+  if (replacing) {
+    g_tier.resident -= old_bytes;
+    free_slot(g_slots[key]);
+  }
+  if (rehydrate) ++g_tier.rehydrates;
+  g_tier.resident += sl.bytes;
+  sl.last = ++g_tier.clock;
+  g_slots[key] = sl;
+  return PION_OK;
+}
+
 Slot *find_slot(const char *sid, int layer) {
   auto it = g_slots.find(key_of(sid, layer));
   return it == g_slots.end() ? nullptr : &it->second;
@@ -579,95 +680,73 @@ int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D, uint32_t *codes
 
 int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const void *K,
                       const void *V, int kv_format, void *stream) {
-  if (!sid_ok(sid) || H < 1 || H > 255 || N < 1 || D <= 0 || !K || !V) return PION_ERR_INVALID;
-  if (kv_format != PION_KV_FP16 && kv_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
-  if (kv_format == PION_KV_MLX4G32 && D % 32) return PION_ERR_INVALID;
-  if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
-  const size_t elems = (size_t)H * N * D;
-  if ((size_t)N * D > ((size_t)1 << 40)) return PION_ERR_INVALID;
-  // the mlx4g32 kernel addresses a kv-head's codes (N * D / 2 bytes) through a 32-bit
-  // buffer range
-  if (kv_format == PION_KV_MLX4G32 && (size_t)N * D >= ((size_t)1 << 33)) return PION_ERR_UNSUPPORTED;
-  if (!aligned(K, 16) || !aligned(V, 16)) return PION_ERR_INVALID;
+  int rc = check_slot_shape(sid, H, N, D, kv_format);
+  if (rc != PION_OK) return rc;
+  if (!K || !V || !aligned(K, 16) || !aligned(V, 16)) return PION_ERR_INVALID;
   if (!on_device(K) || !on_device(V)) return PION_ERR_INVALID;
-  hipStream_t st = (hipStream_t)stream;
+  const size_t elems = (size_t)H * N * D;
+  return install_slot(sid, layer, H, N, D, kv_format, (hipStream_t)stream,
+                      [&](char *base, const SlotLayout &L, hipStream_t st) {
+                        return fill_from_fp16(base, L, kv_format, K, V, elems, D, st);
+                      });
+}
 
-  const SlotLayout L = slot_layout(kv_format, H, N, D);
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (g_tier.max_bytes > 0 && L.bytes > (size_t)g_tier.max_bytes) return PION_ERR_NOMEM;
-  const std::string key = key_of(sid, layer);
-  auto old = g_slots.find(key);
-  const bool replacing = old != g_slots.end();
-  const size_t old_bytes = replacing ? old->second.bytes : 0;
-  // a cold key leaves the registry now (so that demotions below cannot drop it); it is
-  // put back if the store fails
-  ColdEntry was_cold;
-  auto ci = g_cold.find(key);
-  const bool rehydrate = ci != g_cold.end();
-  if (rehydrate) {
-    was_cold = ci->second;
-    g_cold.erase(ci);
-  }
-  auto fail = [&](int rc) {
-    if (rehydrate) {
-      g_cold[key] = was_cold;
-      trim_cold();
-    }
-    return rc;
-  };
-  // room: demote least recently used slots until the count and the byte budget hold
-  // (a replaced slot's bytes count as freed)
-  while ((long long)(g_slots.size() - (replacing ? 1 : 0) + 1) > g_tier.max_slots ||
-         (g_tier.max_bytes > 0 &&
-          g_tier.resident - old_bytes + L.bytes > (size_t)g_tier.max_bytes))
-    if (!demote_lru(key)) break;
+int pion_prefix_warm(const char *sid, int layer, int H, int N, int D, int src_format,
+                     const void *K_rows, const void *V_rows, int kv_format, void *stream) {
+  int rc = check_slot_shape(sid, H, N, D, kv_format);
+  if (rc != PION_OK) return rc;
+  if (src_format != PION_KV_FP16 && src_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
+  if (src_format == PION_KV_MLX4G32 && D % 32) return PION_ERR_INVALID;
+  const uintptr_t al = src_format == PION_KV_FP16 ? 16 : 4;
+  if (!K_rows || !V_rows || !aligned(K_rows, al) || !aligned(V_rows, al)) return PION_ERR_INVALID;
+  if (!on_device(K_rows) || !on_device(V_rows)) return PION_ERR_INVALID;
+  return install_slot(
+      sid, layer, H, N, D, kv_format, (hipStream_t)stream,
+      [&](char *base, const SlotLayout &L, hipStream_t st) -> hipError_t {
+        if (kv_format == PION_KV_FP16) {  // dequantized (if need be) and transposed
+          hipError_t e = launch_rows_to_fp16_slot(K_rows, src_format, N, H, D,
+                                                  (uint16_t *)(base + L.off[0]), st);
+          if (e != hipSuccess) return e;
+          return launch_rows_to_fp16_slot(V_rows, src_format, N, H, D,
+                                          (uint16_t *)(base + L.off[1]), st);
+        }
+        if (src_format == PION_KV_MLX4G32) {  // codes, scales and biases move unchanged
+          hipError_t e = launch_rows_to_mlx4_slot(K_rows, N, H, D, (uint32_t *)(base + L.off[0]),
+                                                  (uint32_t *)(base + L.off[1]), st);
+          if (e != hipSuccess) return e;
+          return launch_rows_to_mlx4_slot(V_rows, N, H, D, (uint32_t *)(base + L.off[2]),
+                                          (uint32_t *)(base + L.off[3]), st);
+        }
+        // fp16 rows into an mlx4g32 slot: transpose into a scratch [H, N, D], then encode
+        const size_t elems = (size_t)H * N * D;
+        void *tmp[2] = {nullptr, nullptr};
+        hipError_t e = hipSuccess;
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipMalloc(&tmp[i], elems * 2);
+        if (e == hipSuccess)
+          e = launch_rows_to_fp16_slot(K_rows, PION_KV_FP16, N, H, D, (uint16_t *)tmp[0], st);
+        if (e == hipSuccess)
+          e = launch_rows_to_fp16_slot(V_rows, PION_KV_FP16, N, H, D, (uint16_t *)tmp[1], st);
+        if (e == hipSuccess) e = fill_from_fp16(base, L, kv_format, tmp[0], tmp[1], elems, D, st);
+        for (void *t : tmp)
+          if (t) (void)hipFree(t);  // waits for the encoder
+        return e;
+      });
+}
 
-  Slot sl;
-  sl.H = H;
-  sl.N = N;
-  sl.D = D;
-  sl.fmt = kv_format;
-  sl.bytes = L.bytes;
-  // device memory short: demote further, least recently used first
-  while (hipMalloc(&sl.mem, sl.bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    sl.mem = nullptr;
-    if (!demote_lru(key)) return fail(PION_ERR_NOMEM);
-  }
-  char *base = (char *)sl.mem;
-  sl.view = make_view(sl.mem, kv_format, H, N, D);
-  hipError_t e;
-  if (kv_format == PION_KV_FP16) {
-    e = hipMemcpyAsync(base + L.off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(base + L.off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
-  } else {
-    const int64_t rows = (int64_t)H * N;
-    // scale and bias interleaved as (scale | bias << 16) words
-    uint16_t *ksb = (uint16_t *)(base + L.off[1]), *vsb = (uint16_t *)(base + L.off[3]);
-    e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D, (uint32_t *)(base + L.off[0]), ksb,
-                                ksb + 1, 2, st);
-    if (e == hipSuccess)
-      e = launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[2]),
-                                  vsb, vsb + 1, 2, st);
-  }
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ready, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(sl.ready, st);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    free_slot(sl);
-    return fail(PION_ERR_HIP);
-  }
-  sl.stream = st;
-  if (replacing) {
-    g_tier.resident -= old_bytes;
-    free_slot(g_slots[key]);
-  }
-  if (rehydrate) ++g_tier.rehydrates;
-  g_tier.resident += sl.bytes;
-  sl.last = ++g_tier.clock;
-  g_slots[key] = sl;
-  return PION_OK;
+int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim, int64_t start,
+                          int64_t end, float *out, void *stream) {
+  if (n_rows < 0 || kv_dim <= 0) return PION_ERR_INVALID;
+  if (fmt != PION_KV_FP16 && fmt != PION_KV_MLX4G32) return PION_ERR_INVALID;
+  if (kv_dim % (fmt == PION_KV_FP16 ? 8 : 32)) return PION_ERR_INVALID;
+  if (start < 0 || end < start || end > n_rows) return PION_ERR_INVALID;
+  if (end == start) return PION_OK;  // nothing read or written
+  if (!rows || !out) return PION_ERR_INVALID;
+  if (!aligned(rows, fmt == PION_KV_FP16 ? 16 : 4) || !aligned(out, 16)) return PION_ERR_INVALID;
+  if (!on_device(rows) || !on_device(out)) return PION_ERR_INVALID;
+  return launch_vstore_fetch(rows, fmt, kv_dim, start, end - start, out, (hipStream_t)stream) ==
+                 hipSuccess
+             ? PION_OK
+             : PION_ERR_HIP;
 }
 
 int pion_prefix_lookup(const char *sid, int layer) {

@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -157,3 +157,22 @@ def test_binding_rejects_cpu_tensors():
     K = torch.zeros(2, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         kp.pion_prefix_store("s", 0, K, K)
+
+
+def test_vstore_argument_validation(lib):
+    f = lib.pion_vstore_fetch_f32
+    assert f(None, 0, 10, 64, 0, 1, FAKE, None) == kp.PION_ERR_INVALID
+    assert f(FAKE, 7, 10, 64, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # format
+    assert f(FAKE, 1, 10, 48, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # mlx4g32: kv % 32
+    assert f(FAKE, 0, 10, 12, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # fp16: kv % 8
+    assert f(FAKE, 0, 10, 64, 5, 11, FAKE, None) == kp.PION_ERR_INVALID       # past n_rows
+    assert f(FAKE, 0, 10, 64, 5, 4, FAKE, None) == kp.PION_ERR_INVALID        # end < start
+    assert f(FAKE, 0, 10, 64, 3, 3, FAKE, None) == kp.PION_OK                 # empty range
+    assert f(ctypes.c_void_p(0x1004), 0, 10, 64, 0, 1, FAKE, None) == kp.PION_ERR_INVALID
+    w = lib.pion_prefix_warm
+    assert w(b"s", 0, 2, 8, 64, 7, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID  # src format
+    assert w(b"s", 0, 2, 8, 64, 0, FAKE, FAKE, 5, None) == kp.PION_ERR_INVALID  # slot format
+    assert w(b"s", 0, 2, 8, 48, 0, FAKE, FAKE, 0, None) == kp.PION_ERR_UNSUPPORTED
+    assert w(b"s", 0, 2, 8, 64, 0, None, FAKE, 0, None) == kp.PION_ERR_INVALID
+    assert w(b"s", 0, 2, 8, 64, 0, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID  # not device memory
+    assert lib.pion_prefix_lookup(b"s", 0) == 0
