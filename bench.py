@@ -16,7 +16,9 @@ above): --config 1 tiny dense query; --config 3 fused batched-Q prefill (TFLOP/s
 --config 4 mlx4g32 decode, 16 layers per launch (GB/s of resident codes/scales/biases,
 plus the single-query latency); --config 5 sparse-auto
 fused query (us/query); --config 6 QUERY_SPARSE over caller-supplied indices (us/query,
-GB/s of gathered rows; not a headline workload).
+GB/s of gathered rows); --config 7 V-store fetch of whole layers from mlx4g32 records to
+fp32 (GB/s read + written), with the whole-call time of a WARM rehydrate beside it
+(configs 6 and 7 are not headline workloads).
 
 Timing: wall clock over K steps between device synchronizations; a HIP event pair on
 the launch stream brackets the same timed region, and its elapsed time over the number
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="calls mode: no graph")
@@ -523,6 +525,95 @@ def run_query_sparse(args, torch, kp, synth, dev, stream):
     }
 
 
+def run_vstore(args, torch, kp, synth, dev, stream):
+    """V-store side of the decode shape: 32 layers, K and V, H = 8, N = 2048, D = 128
+    (kv = 1024, the 640 B/token mlx4g32 record). A step fetches every layer-side's whole
+    token range as fp32 (64 launches of the dequantizing fetch). Bytes per launch: records
+    read (640 B/token) + fp32 written (4 kv B/token). Steps rotate over 4 copies of the
+    records (336 MB) so the reads are cold. Beside it, `warm_call`: the whole-call time of
+    pion_prefix_warm (K and V of one layer into an fp16 slot, replacing the live slot:
+    allocation, two relayout launches, the free of the old slot), host work included."""
+    import numpy as np
+    import oracle
+    from oracle import vstore as ovs
+    L, H, N, D = 32, 8, 2048, 128
+    kv = H * D
+    NCOPY = 4
+    recs = []
+    for l in range(L):
+        inp = synth.generate(synth.DECODE, l, N=N, D=D, H_q=H, H_kv=H)
+        for x in (inp.K, inp.V):
+            rows = np.ascontiguousarray(x.transpose(1, 0, 2).reshape(N, kv))
+            recs.append(ovs.pack_records(*oracle.quantize(rows)))
+    rb = recs[0].shape[1]
+    dev_recs = [[torch.from_numpy(r).to(dev) for r in recs] for _ in range(NCOPY)]
+    out = [torch.empty((N, kv), dtype=torch.float32, device=dev) for _ in range(2)]
+    lib = kp.lib()
+
+    def make_step(c):
+        calls = [(dev_recs[c][i].data_ptr(), out[i % 2].data_ptr()) for i in range(2 * L)]
+
+        def step():
+            s = torch.cuda.current_stream().cuda_stream
+            for rp, op in calls:
+                rc = lib.pion_vstore_fetch_f32(rp, 1, N, kv, 0, N, op, s)
+                if rc != 0:
+                    raise kp.PionError(rc, "pion_vstore_fetch_f32")
+        return step
+
+    (ms, launch_us), (wms, _) = warm_cold(torch, stream, [make_step(c) for c in range(NCOPY)],
+                                          2 * L, False, args)
+    got = out[1].cpu().numpy()                      # the last launch: layer 31, V
+    want = ovs.fetch_f32(recs[-1], ovs.MLX4G32, kv, 0, N)
+    if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
+        raise SystemExit("bench fetch disagrees with the oracle")
+    per_launch = N * (rb + 4 * kv)
+    nbytes = 2 * L * per_launch
+
+    # whole WARM calls (replacing live slots), one layer per call
+    sid = "bench-warm"
+    for l in range(L):
+        kp.pion_prefix_warm(sid, l, H, D, dev_recs[0][2 * l], dev_recs[0][2 * l + 1], 1)
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            for l in range(L):
+                kp.pion_prefix_warm(sid, l, H, D, dev_recs[1][2 * l], dev_recs[1][2 * l + 1], 1)
+    torch.cuda.synchronize()
+    warm_us = (time.perf_counter() - t0) * 1e6 / (reps * L)
+    kp.pion_prefix_drop(sid, -1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        i = [0]
+
+        def one_layer_side():
+            ovs.fetch_f32(recs[i[0] % len(recs)], ovs.MLX4G32, kv, 0, N)
+            i[0] += 1
+        n, el = cpu_time(one_layer_side, args.cpu_seconds)
+        cpu = {"value": round(n * per_launch / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"{n} whole layer-side fetches of this workload ({el:.1f} s)"}
+    return {
+        "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
+        "dtype": "int4 codes + fp16 scale/bias -> fp32",
+        "config": {"workload": f"V-store fetch, mlx4g32 records -> fp32, {L} layers x K,V, "
+                               f"H={H} N={N} D={D} (kv={kv}, {rb} B/token)",
+                   "bytes_per_step": nbytes,
+                   "memory_side_cache": f"cold: steps rotate over {NCOPY} copies of the records"},
+        "roofline": {"bound": "hbm", "achieved": per_launch / (launch_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "avg_launch_us": launch_us},
+        "warm": {"value": round(nbytes / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
+                 "note": "one copy of the records every step (memory-side cache warm)"},
+        "warm_call": {"value": round(warm_us, 1), "unit": "us per layer",
+                      "note": "pion_prefix_warm, K and V of one layer, mlx4g32 records -> fp16 "
+                              "slot replacing the live one (allocation and free included)"},
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -545,7 +636,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse,
-              6: run_query_sparse}[args.config]
+              6: run_query_sparse, 7: run_vstore}[args.config]
     r = runner(args, torch, kp, synth, dev, stream)
     roof = r["roofline"]
     if roof is not None:
@@ -570,7 +661,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    for extra in ("warm", "single_query"):
+    for extra in ("warm", "single_query", "warm_call"):
         if extra in r:
             line[extra] = r[extra]
     print(json.dumps(line), flush=True)

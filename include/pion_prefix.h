@@ -216,8 +216,8 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
  * concatenated dequantized fp32 values of tokens start .. end - 1.
  *   rows  device, n_rows V-store rows in format fmt (see above).
  *   out   device fp32 [end - start, kv_dim], 16-byte aligned.
- * Errors: INVALID (pointers, fmt, kv_dim <= 0 or not a multiple of 8 (fp16) / 32
- * (mlx4g32), range outside [0, n_rows], alignment), HIP. An empty range is a no-op
+ * Errors: INVALID (pointers, fmt, kv_dim <= 0 or not a multiple of 32, range outside
+ * [0, n_rows], alignment), HIP. An empty range is a no-op
  * (rows and out may then be NULL). */
 int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim,
                           int64_t start, int64_t end, float *out, void *stream);

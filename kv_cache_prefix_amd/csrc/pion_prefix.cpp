@@ -737,7 +737,7 @@ int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim,
                           int64_t end, float *out, void *stream) {
   if (n_rows < 0 || kv_dim <= 0) return PION_ERR_INVALID;
   if (fmt != PION_KV_FP16 && fmt != PION_KV_MLX4G32) return PION_ERR_INVALID;
-  if (kv_dim % (fmt == PION_KV_FP16 ? 8 : 32)) return PION_ERR_INVALID;
+  if (kv_dim % 32) return PION_ERR_INVALID;  // whole groups of 32 values
   if (start < 0 || end < start || end > n_rows) return PION_ERR_INVALID;
   if (end == start) return PION_OK;  // nothing read or written
   if (!rows || !out) return PION_ERR_INVALID;

@@ -164,7 +164,7 @@ def test_vstore_argument_validation(lib):
     assert f(None, 0, 10, 64, 0, 1, FAKE, None) == kp.PION_ERR_INVALID
     assert f(FAKE, 7, 10, 64, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # format
     assert f(FAKE, 1, 10, 48, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # mlx4g32: kv % 32
-    assert f(FAKE, 0, 10, 12, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # fp16: kv % 8
+    assert f(FAKE, 0, 10, 48, 0, 1, FAKE, None) == kp.PION_ERR_INVALID        # fp16: kv % 32
     assert f(FAKE, 0, 10, 64, 5, 11, FAKE, None) == kp.PION_ERR_INVALID       # past n_rows
     assert f(FAKE, 0, 10, 64, 5, 4, FAKE, None) == kp.PION_ERR_INVALID        # end < start
     assert f(FAKE, 0, 10, 64, 3, 3, FAKE, None) == kp.PION_OK                 # empty range
