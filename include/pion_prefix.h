@@ -26,7 +26,7 @@
  *   - Supported head dims: D in {32, 64, 96, 128, 160, 192, 256, 512} (the native SDPA
  *     head-dim set of the "Shared KV Cache Serving" page); other values ->
  *     PION_ERR_UNSUPPORTED. Batched-Q (M >= 32) fp16 queries run on matrix cores for
- *     D in {64, 128, 256} and on the vector split kernel otherwise (same results).
+ *     every D but 512, which runs on the vector split kernel (same results).
  *   - Calls are thread-safe (one library-wide lock guards the slot table).
  */
 #ifndef PION_PREFIX_H

@@ -102,9 +102,11 @@ bool sid_ok(const char *sid) {
 }
 
 bool d_supported(int D) { return head_dim_supported(D); }
-// Head dims of the MFMA kernels (batched-Q prefill and grouped-query decode); a query
-// at another head dim runs on the split kernels.
-bool mfma_dim(int D) { return D == 64 || D == 128 || D == 256; }
+// Head dims of the MFMA kernels; a query at another head dim runs on the split kernels.
+// Batched-Q prefill: every served D but 512 (its accumulators exceed the registers).
+// Grouped-query decode: the power-of-two dims its LDS layout is written for.
+bool prefill_dim(int D) { return D != 512; }
+bool gqa_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
 // Capacity (env PION_MAX_SLOTS, PION_MAX_BYTES, PION_COLD_SLOTS at load; then
 // pion_prefix_set_capacity) and the cold-tier counters; all under g_mu.
@@ -371,7 +373,7 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   if (tiles > kMaxCounters / 2) return PION_ERR_UNSUPPORTED;  // ticket and done counters
   const long long total = (long long)sl.N + c.S_suf;
   // splits: up to about 1.5 workgroups per CU over the row blocks (two fit on a CU for
-  // D <= 128, one for D = 256); each split adds a partial round trip and merge work.
+  // D <= 128, one above); each split adds a partial round trip and merge work.
   // env PION_PREFILL_SPLITS overrides
   const long long slots = c.D <= 128 ? 384 : 256;
   long long ns = std::max<long long>(1, (slots + tiles / 2) / tiles);
@@ -414,7 +416,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   // (the MFMA kernel addresses a kv-head's K, V and suffix through 32-bit buffer ranges)
   const long long row_bytes = 2LL * c.D;
   if (slots.size() == 1 && slots[0]->fmt == PION_KV_FP16 && !c.blocks && c.M >= kMfmaMinRows &&
-      mfma_dim(c.D) &&
+      prefill_dim(c.D) &&
       slots[0]->N * row_bytes < (1LL << 31) && c.S_suf * row_bytes < (1LL << 31) &&
       !getenv_flag("PION_NO_MFMA"))
     return run_prefill(*slots[0], c, st);
@@ -507,7 +509,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     // PION_NO_GQA_MFMA turns it off. It addresses a kv-head's K, V and suffix through
     // 32-bit buffer ranges.
     const long long row_bytes = 2LL * c.D;
-    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && mfma_dim(c.D) &&
+    const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && gqa_dim(c.D) &&
                         N_max * row_bytes < (1LL << 31) &&
                         (long long)c.S_suf * row_bytes < (1LL << 31) &&
                         !getenv_flag("PION_NO_GQA_MFMA");

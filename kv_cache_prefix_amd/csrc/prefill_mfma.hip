@@ -21,7 +21,10 @@
 // (no register staging), NSTAGE tiles deep: the loads of tile j + NSTAGE - 1 are issued
 // when tile j starts. Both tiles are stored row-major with the 16-byte chunks of a row
 // XOR-swizzled by a function of the row (swz), which makes the K operand reads and the
-// transposed V reads bank-conflict free. V^T operands come from row-major V through the
+// transposed V reads bank-conflict free. An LDS row holds DP = D rounded up to a power of
+// two (at least 64) dims, the layout the swizzle was searched for: for D = 32, 96, 160,
+// 192 the chunks past D are padding (their loads fetch a chunk of the same row again,
+// already in flight, and nothing reads them). V^T operands come from row-major V through the
 // LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i receives
 // element i % 4 of the 8-byte pieces addressed by lanes 4j + i/4 (j = 0..3), so lanes
 // addressing (row kbase + q/4, dims dbase + 4(q%4)) receive 4 consecutive keys of dim
@@ -57,9 +60,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int NSTAGE = 2;  // LDS tile stages (loads run NSTAGE - 1 tiles ahead)
 
+// LDS dims per key row: D rounded up to a power of two, at least 64
+template <int D>
+constexpr int lds_dims() {
+  int p = 64;
+  while (p < D) p *= 2;
+  return p;
+}
+
 template <int D>
 struct PrefillSmem {
-  static constexpr int TB = BK * 2 * D;  // bytes of one K or V tile
+  static constexpr int TB = BK * 2 * lds_dims<D>();  // bytes of one K or V tile
   union {
     alignas(16) char kv[NSTAGE][2][TB];  // [stage][0: K, 1: V]
     struct {                             // split merge: per (row, split) m then weight, and l
@@ -84,7 +95,10 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
   constexpr int NDS = D / 16;                 // 16-dim k-steps of S^T
   constexpr int CH = D / 8;                   // 16-byte chunks per key row
-  constexpr uint32_t ROWB = D * 2;            // bytes per key row
+  constexpr int DP = lds_dims<D>();           // dims per LDS row (swizzle layout)
+  constexpr int CHP = DP / 8;                 // 16-byte chunks per LDS row
+  constexpr uint32_t ROWG = D * 2;            // bytes per key row in HBM
+  constexpr uint32_t ROWB = DP * 2;           // bytes per key row in LDS
   constexpr int TB = PrefillSmem<D>::TB;
   constexpr int NLD = TB / 1024 / 4;          // 1 KB LDS loads per wave, tile and side
   __shared__ PrefillSmem<D> sm;
@@ -117,13 +131,13 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const int lim_first = p.S_suf > 0 ? p.N + p.S_suf - p.M + i0 + 1 : p.N;
   const int full_end = min(k_end, lim_first);
 
-  const i32x4 rK = rsrc_words(p.K + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
-  const i32x4 rV = rsrc_words(p.V + (size_t)g * p.N * D, (uint32_t)p.N * ROWB);
+  const i32x4 rK = rsrc_words(p.K + (size_t)g * p.N * D, (uint32_t)p.N * ROWG);
+  const i32x4 rV = rsrc_words(p.V + (size_t)g * p.N * D, (uint32_t)p.N * ROWG);
   const bool has_suf = p.S_suf > 0;  // a null suffix gets an empty range
   const i32x4 rKs =
-      rsrc_words(has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : p.K, (uint32_t)p.S_suf * ROWB);
+      rsrc_words(has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : p.K, (uint32_t)p.S_suf * ROWG);
   const i32x4 rVs =
-      rsrc_words(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWB);
+      rsrc_words(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWG);
 
   // Tiles never straddle the prefix / suffix boundary: the split's prefix part
   // [k_begin, pre_end) is tiled from k_begin, its suffix part [suf_beg, k_stop) from
@@ -135,16 +149,17 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const int n_tiles = n_pre + n_suf;
 
   // LDS loads of a tile: wave w's load t fills tile bytes [1 KB (NLD w + t), +1 KB),
-  // lane l the 16 bytes at 16 l there: tile row r, physical chunk l % CH, which holds
-  // logical chunk (l % CH) ^ swz(r) of source row r0 + r.
+  // lane l the 16 bytes at 16 l there: tile row r, physical chunk l % CHP, which holds
+  // logical chunk (l % CHP) ^ swz(r) of source row r0 + r (a padding chunk, logical
+  // chunk >= CH, loads chunk 0 of the row again).
   const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, &sm.kv[0][0][0]);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t voff[NLD];
 #pragma unroll
   for (int t = 0; t < NLD; ++t) {
     const int r = (1024 * (NLD * wave_u + t) + 16 * lane) / (int)ROWB;
-    const int pc = lane % CH;
-    voff[t] = (uint32_t)r * ROWB + (uint32_t)((pc ^ swz<D>(r)) * 16);
+    const int lc = (lane % CHP) ^ swz<DP>(r);
+    voff[t] = (uint32_t)r * ROWG + (uint32_t)((lc < CH ? lc : 0) * 16);
   }
   auto issue = [&](int j) {
     const bool suf = j >= n_pre;  // workgroup-uniform
@@ -153,8 +168,8 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     const uint32_t st = lds0 + (uint32_t)((j % NSTAGE) * 2 * TB + 1024 * NLD * wave_u);
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
-      load_lds16(rk, (uint32_t)r0 * ROWB + voff[t], st + 1024 * t);
-      load_lds16(rv, (uint32_t)r0 * ROWB + voff[t], st + TB + 1024 * t);
+      load_lds16(rk, (uint32_t)r0 * ROWG + voff[t], st + 1024 * t);
+      load_lds16(rv, (uint32_t)r0 * ROWG + voff[t], st + TB + 1024 * t);
     }
   };
 
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const char *smb = &sm.kv[0][0][0];
   uint32_t koff[NDS];
   {
-    const int swk = swz<D>(col);
+    const int swk = swz<DP>(col);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
       koff[ds] = (uint32_t)col * ROWB + (uint32_t)(((2 * ds + hl) ^ swk) << 4);
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int r = 4 * hl + 8 * c + (q16 >> 2);  // row modulo 16
-      const int vsw = swz<D>(r);
+      const int vsw = swz<DP>(r);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         voffs[c][db] = (uint32_t)r * ROWB + (uint32_t)(q16 & 1) * 8 +
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       for (int e = 0; e < 16; ++e) o[db][e] = REG ? o[db][e] * ws : 0.f;
   }
   // one round: DBC 32-dim blocks of CB splits (register budget)
-  constexpr int CB = D <= 64 ? 2 : 1, DBC = D <= 128 ? NDB : 2;
+  constexpr int CB = D <= 64 ? 2 : 1, DBC = D <= 128 ? NDB : NDB % 2 ? 1 : 2;
   for (int c0 = 0; c0 < S; c0 += CB) {
 #pragma unroll
     for (int d0 = 0; d0 < NDB; d0 += DBC) {
@@ -491,8 +506,12 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s) {
   const int W = p.H_q * p.n_iblk * p.n_splits;
   dim3 grid(8 * ((W + 7) / 8));
   switch (p.D) {
+    case 32: hipLaunchKernelGGL(prefill_kernel<32>, grid, dim3(256), 0, s, p); break;
     case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(prefill_kernel<96>, grid, dim3(256), 0, s, p); break;
     case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, p); break;
+    case 160: hipLaunchKernelGGL(prefill_kernel<160>, grid, dim3(256), 0, s, p); break;
+    case 192: hipLaunchKernelGGL(prefill_kernel<192>, grid, dim3(256), 0, s, p); break;
     case 256: hipLaunchKernelGGL(prefill_kernel<256>, grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }

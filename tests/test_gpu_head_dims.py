@@ -47,7 +47,7 @@ def test_decode_fp16_arbitrary_head_map(kp, D):
 @pytest.mark.parametrize("D", NEW_D)
 @pytest.mark.parametrize("M,S_suf", [(1, 40), (5, 70), (40, 40), (70, 100)])
 def test_fused_suffix(kp, D, M, S_suf):
-    # M >= 32 at these head dims runs the vector split kernel with M query indices
+    # M >= 32 runs the MFMA kernel (D = 512: the vector split kernel with M query indices)
     inp = synth.generate(synth.PREFILL, 22, N=300, M=M, S_suf=S_suf, D=D, H_q=6, H_kv=2)
     kp.pion_prefix_store("t", 702, dev(inp.K), dev(inp.V))
     out, lse = empty((6, M, D)), empty((6, M))
@@ -133,3 +133,39 @@ def test_unsupported_head_dim(kp):
     with pytest.raises(k.PionError) as e:
         kp.pion_prefix_store("t", 720, x, x)
     assert e.value.status == k.PION_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("D", [32, 96, 160, 192])
+@pytest.mark.parametrize("N,M,S_suf", [(1000, 130, 200), (777, 257, 0), (64, 32, 0), (300, 40, 40)])
+def test_mfma_prefill(kp, D, N, M, S_suf):
+    # M >= 32 runs the MFMA kernel with rows padded in LDS to a power-of-two layout
+    inp = synth.generate(synth.PREFILL, 29, N=N, M=M, S_suf=S_suf, D=D, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 730, dev(inp.K), dev(inp.V))
+    out, lse = empty((6, M, D)), empty((6, M))
+    if S_suf:
+        kp.pion_prefix_query_fused("t", 730, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    else:
+        kp.pion_prefix_query("t", 730, dev(inp.Q), out, lse)
+    out, lse = host(out), host(lse)
+    rng = np.random.default_rng(N + M + D)
+    rows = [(h, i) for h in range(6) for i in (0, M - 1)] + \
+        [(int(h), int(i)) for h, i in zip(rng.integers(0, 6, 30), rng.integers(0, M, 30))]
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
+    check(out, lse, ref, ref_lse, rows=rows)
+    assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("D", [32, 96, 160, 192, 512])
+def test_mfma_and_valu_prefill_agree(kp, monkeypatch, D):
+    inp = synth.generate(synth.PREFILL, 30, N=500, M=64, S_suf=64, D=D, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 731, dev(inp.K), dev(inp.V))
+    outs = []
+    for flag in ("0", "1"):
+        monkeypatch.setenv("PION_NO_MFMA", flag)
+        out, lse = empty((6, 64, D)), empty((6, 64))
+        kp.pion_prefix_query_fused("t", 731, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+        outs.append((host(out), host(lse)))
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+    for o, l in outs:
+        check(o, l, ref, ref_lse)
+    assert np.max(np.abs(outs[0][0] - outs[1][0])) <= 2 * OUT_TOL
