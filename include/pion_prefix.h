@@ -70,11 +70,17 @@ enum {
 
 /* Resident formats. FP16 keeps K and V as given. MLX4G32 is the int4 group-32 affine
  * tier ("Shared KV Cache Serving", Quantized tier - mlx4g32; V-store page, The
- * mlx4g32 tier), quantized on the device at store time with pion_kv_quantize_mlx4g32. */
-enum { PION_KV_FP16 = 0, PION_KV_MLX4G32 = 1 };
+ * mlx4g32 tier), quantized on the device at store time with pion_kv_quantize_mlx4g32.
+ * FP32 keeps fp32 K and V (the sdpa_*_fp32 kernels of the native SDPA paragraph).
+ *
+ * Precision of the arrays a call passes: on an FP32 slot, K and V of the store, Q of
+ * every query form and the suffix K_suf, V_suf are fp32; on FP16 and MLX4G32 slots they
+ * are fp16. out and lse are fp32 always. An FP32 slot runs every query form on the
+ * vector split kernel (no fp16 matrix-core rounding of its values). */
+enum { PION_KV_FP16 = 0, PION_KV_MLX4G32 = 1, PION_KV_FP32 = 2 };
 
 /* ATTEND.PREFIX.STORE <sid> <layer> <H> <N> <D> <K_blob> <V_blob>.
- * Copies K and V, fp16 [H, N, D] each, into a library-owned slot keyed (sid, layer)
+ * Copies K and V, [H, N, D] each (fp16, or fp32 for PION_KV_FP32), into a library-owned slot keyed (sid, layer)
  * and keeps them resident until pion_prefix_drop, demotion (see Capacity above) or
  * library unload (the command table: "resident until DROP"). Storing a live key
  * replaces its slot and drops any cached block means; storing a cold key rehydrates it. The library owns the slot memory; K and V may be freed once
@@ -225,7 +231,8 @@ int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim,
 /* KV.PREFIX.WARM, one layer ("Shared KV Cache Serving"): rehydrate the slot (sid, layer)
  * from the layer's V-store rows of K and of V (N tokens each, src_format, kv_dim = H * D),
  * transposed from the V-store layout [N, H * D] into the STORE layout [H, N, D]:
- *   kv_format FP16     the dequantized values (fp16 rows: the values themselves);
+ *   kv_format FP16     the dequantized values rounded to fp16 (fp16 rows: the values);
+ *   kv_format FP32     the dequantized fp32 values (the pages' own rehydrate);
  *   kv_format MLX4G32  from mlx4g32 rows: the codes, scales and biases unchanged (the same
  *                      slot a STORE of the original fp16 K/V with MLX4G32 makes); from
  *                      fp16 rows: encoded as pion_prefix_store does.

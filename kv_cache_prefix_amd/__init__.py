@@ -22,6 +22,7 @@ PION_ERR_HIP = -5
 PION_ERR_COLDMISS = -6
 PION_KV_FP16 = 0
 PION_KV_MLX4G32 = 1
+PION_KV_FP32 = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpion_prefix.so")
 
@@ -118,14 +119,28 @@ def _head_map(head_map, H_q):
     return arr, arr.ctypes.data
 
 
-def pion_prefix_store(sid, layer: int, K, V, kv_format: int = PION_KV_FP16, stream=None) -> int:
-    """ATTEND.PREFIX.STORE: K, V fp16 [H, N, D] device tensors -> resident slot."""
+def _fmt_dtype(kv_format: int):
+    """Element type of the arrays a call passes for a slot of this format."""
     import torch
+    return torch.float32 if kv_format == PION_KV_FP32 else torch.float16
+
+
+def _slot_dtype(sid, layer: int):
+    """Element type of Q and the suffix for the slot (sid, layer); fp16 if it has no warm
+    slot (the call itself then reports the status)."""
+    fmt = ctypes.c_int(PION_KV_FP16)
+    lib().pion_prefix_info(_sid(sid), layer, None, None, None, ctypes.byref(fmt))
+    return _fmt_dtype(fmt.value)
+
+
+def pion_prefix_store(sid, layer: int, K, V, kv_format: int = PION_KV_FP16, stream=None) -> int:
+    """ATTEND.PREFIX.STORE: K, V [H, N, D] device tensors (fp16; fp32 for PION_KV_FP32)
+    -> resident slot."""
     if K.dim() != 3 or V.shape != K.shape:
         raise ValueError("K and V must both be [H, N, D]")
     H, N, D = K.shape
-    rc = lib().pion_prefix_store(_sid(sid), layer, H, N, D,
-                                 _dev(K, torch.float16, "K"), _dev(V, torch.float16, "V"),
+    dt = _fmt_dtype(kv_format)
+    rc = lib().pion_prefix_store(_sid(sid), layer, H, N, D, _dev(K, dt, "K"), _dev(V, dt, "V"),
                                  kv_format, _stream(stream))
     return _check(rc, "pion_prefix_store")
 
@@ -201,12 +216,14 @@ def pion_prefix_warm(sid, layer: int, H: int, D: int, K_rows, V_rows, src_format
 
 
 def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=None) -> int:
-    """ATTEND.PREFIX.QUERY (M >= 1): Q fp16 [H_q, M, D] -> out fp32 [H_q, M, D], lse [H_q, M]."""
+    """ATTEND.PREFIX.QUERY (M >= 1): Q [H_q, M, D] (fp16; fp32 on an fp32 slot) ->
+    out fp32 [H_q, M, D], lse [H_q, M]."""
     import torch
     H_q, M, D = Q.shape
+    qt = _slot_dtype(sid, layer)
     hm, hm_ptr = _head_map(head_map, H_q)
     rc = lib().pion_prefix_query(
-        _sid(sid), layer, H_q, D, M, _dev(Q, torch.float16, "Q"), hm_ptr,
+        _sid(sid), layer, H_q, D, M, _dev(Q, qt, "Q"), hm_ptr,
         _dev(out, torch.float32, "out", (H_q, M, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (H_q, M)), _stream(stream))
     return _check(rc, "pion_prefix_query")
@@ -214,13 +231,14 @@ def pion_prefix_query(sid, layer: int, Q, out, lse=None, head_map=None, stream=N
 
 def pion_prefix_query_layers(sid, layer0: int, Q, out, lse=None, head_map=None,
                              stream=None) -> int:
-    """Layers layer0 .. layer0 + n - 1 in one launch: Q fp16 [n, H_q, M, D] ->
-    out fp32 [n, H_q, M, D], lse fp32 [n, H_q, M]."""
+    """Layers layer0 .. layer0 + n - 1 in one launch: Q [n, H_q, M, D] (the slots'
+    precision) -> out fp32 [n, H_q, M, D], lse fp32 [n, H_q, M]."""
     import torch
     n, H_q, M, D = Q.shape
+    qt = _slot_dtype(sid, layer0)
     hm, hm_ptr = _head_map(head_map, H_q)
     rc = lib().pion_prefix_query_layers(
-        _sid(sid), layer0, n, H_q, D, M, _dev(Q, torch.float16, "Q"), hm_ptr,
+        _sid(sid), layer0, n, H_q, D, M, _dev(Q, qt, "Q"), hm_ptr,
         _dev(out, torch.float32, "out", (n, H_q, M, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (n, H_q, M)), _stream(stream))
     return _check(rc, "pion_prefix_query_layers")
@@ -228,21 +246,23 @@ def pion_prefix_query_layers(sid, layer0: int, Q, out, lse=None, head_map=None,
 
 def pion_prefix_query_fused(sid, layer: int, Q, K_suf, V_suf, out, lse=None, head_map=None,
                             H_kv: Optional[int] = None, stream=None) -> int:
-    """ATTEND.PREFIX.QUERY_FUSED: Q [H_q, M, D], K_suf/V_suf fp16 [H_kv, S_suf, D]."""
+    """ATTEND.PREFIX.QUERY_FUSED: Q [H_q, M, D], K_suf/V_suf [H_kv, S_suf, D] (fp16; fp32
+    on an fp32 slot)."""
     import torch
     H_q, M, D = Q.shape
+    qt = _slot_dtype(sid, layer)
     if K_suf is not None:
         H_kv_s, S_suf, _ = K_suf.shape
         H_kv = H_kv_s if H_kv is None else H_kv
-        ks = _dev(K_suf, torch.float16, "K_suf", (H_kv, S_suf, D))
-        vs = _dev(V_suf, torch.float16, "V_suf", (H_kv, S_suf, D))
+        ks = _dev(K_suf, qt, "K_suf", (H_kv, S_suf, D))
+        vs = _dev(V_suf, qt, "V_suf", (H_kv, S_suf, D))
     else:
         if H_kv is None:
             raise ValueError("H_kv is required without a suffix")
         S_suf, ks, vs = 0, None, None
     hm, hm_ptr = _head_map(head_map, H_q)
     rc = lib().pion_prefix_query_fused(
-        _sid(sid), layer, H_q, D, M, S_suf, H_kv, _dev(Q, torch.float16, "Q"), ks, vs, hm_ptr,
+        _sid(sid), layer, H_q, D, M, S_suf, H_kv, _dev(Q, qt, "Q"), ks, vs, hm_ptr,
         _dev(out, torch.float32, "out", (H_q, M, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (H_q, M)), _stream(stream))
     return _check(rc, "pion_prefix_query_fused")
@@ -251,23 +271,25 @@ def pion_prefix_query_fused(sid, layer: int, Q, K_suf, V_suf, out, lse=None, hea
 def pion_prefix_query_sparse_auto(sid, layer: int, Q, B: int, K_top: int, out, lse=None,
                                   blocks_out=None, K_suf=None, V_suf=None, head_map=None,
                                   H_kv: Optional[int] = None, stream=None) -> int:
-    """ATTEND.PREFIX.QUERY_SPARSE_AUTO(_FUSED): Q fp16 [H_q, 1, D] -> out fp32 [H_q, D]."""
+    """ATTEND.PREFIX.QUERY_SPARSE_AUTO(_FUSED): Q [H_q, 1, D] (fp16; fp32 on an fp32 slot)
+    -> out fp32 [H_q, D]."""
     import torch
     H_q, M, D = Q.shape
+    qt = _slot_dtype(sid, layer)
     if M != 1:
         raise ValueError("sparse-auto takes one query row per head")
     if K_suf is not None:
         H_kv_s, S_suf, _ = K_suf.shape
         H_kv = H_kv_s if H_kv is None else H_kv
-        ks = _dev(K_suf, torch.float16, "K_suf", (H_kv, S_suf, D))
-        vs = _dev(V_suf, torch.float16, "V_suf", (H_kv, S_suf, D))
+        ks = _dev(K_suf, qt, "K_suf", (H_kv, S_suf, D))
+        vs = _dev(V_suf, qt, "V_suf", (H_kv, S_suf, D))
     else:
         if H_kv is None:
             raise ValueError("H_kv is required without a suffix")
         S_suf, ks, vs = 0, None, None
     hm, hm_ptr = _head_map(head_map, H_q)
     rc = lib().pion_prefix_query_sparse_auto(
-        _sid(sid), layer, H_q, D, B, K_top, H_kv, S_suf, _dev(Q, torch.float16, "Q"), ks, vs,
+        _sid(sid), layer, H_q, D, B, K_top, H_kv, S_suf, _dev(Q, qt, "Q"), ks, vs,
         hm_ptr, _dev(out, torch.float32, "out", (H_q, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (H_q,)),
         None if blocks_out is None else _dev(blocks_out, torch.int32, "blocks_out", (H_kv, K_top)),
@@ -277,15 +299,16 @@ def pion_prefix_query_sparse_auto(sid, layer: int, Q, B: int, K_top: int, out, l
 
 def pion_prefix_query_sparse(sid, layer: int, Q, indices, counts, out, lse=None,
                              stream=None) -> int:
-    """ATTEND.PREFIX.QUERY_SPARSE: Q fp16 [H, 1, D], indices int32 [H, K_sparse_max],
-    counts int32 [H] -> out fp32 [H, D], lse fp32 [H]."""
+    """ATTEND.PREFIX.QUERY_SPARSE: Q [H, 1, D] (fp16; fp32 on an fp32 slot), indices int32
+    [H, K_sparse_max], counts int32 [H] -> out fp32 [H, D], lse fp32 [H]."""
     import torch
     H, M, D = Q.shape
+    qt = _slot_dtype(sid, layer)
     if M != 1:
         raise ValueError("QUERY_SPARSE takes one query row per head")
     K_sparse_max = indices.shape[1]
     rc = lib().pion_prefix_query_sparse(
-        _sid(sid), layer, H, D, K_sparse_max, _dev(Q, torch.float16, "Q"),
+        _sid(sid), layer, H, D, K_sparse_max, _dev(Q, qt, "Q"),
         _dev(indices, torch.int32, "indices", (H, K_sparse_max)),
         _dev(counts, torch.int32, "counts", (H,)), _dev(out, torch.float32, "out", (H, D)),
         None if lse is None else _dev(lse, torch.float32, "lse", (H,)), _stream(stream))

@@ -83,10 +83,11 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
   const int n_sub = sm.seg_cum[nseg];
 
   const KVView kv = make_view(p.kv_base[z], 0, p.H_kv, b.N, D);
-  const uint16_t *Kp = kv.K + (size_t)g * b.N * D, *Vp = kv.V + (size_t)g * b.N * D;
+  const uint16_t *Kp = (const uint16_t *)kv.K + (size_t)g * b.N * D;
+  const uint16_t *Vp = (const uint16_t *)kv.V + (size_t)g * b.N * D;
   const bool has_suf = p.S_suf > 0;
-  const uint16_t *Ks = has_suf ? p.Ksuf + (size_t)g * p.S_suf * D : Kp;
-  const uint16_t *Vs = has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : Vp;
+  const uint16_t *Ks = has_suf ? (const uint16_t *)p.Ksuf + (size_t)g * p.S_suf * D : Kp;
+  const uint16_t *Vs = has_suf ? (const uint16_t *)p.Vsuf + (size_t)g * p.S_suf * D : Vp;
   const i32x4 wKp = rsrc_words(Kp, (uint32_t)b.N * ROWB), wVp = rsrc_words(Vp, (uint32_t)b.N * ROWB);
   const uint32_t suf_bytes = (uint32_t)(has_suf ? p.S_suf : 0) * ROWB;
   const i32x4 wKs = rsrc_words(Ks, suf_bytes), wVs = rsrc_words(Vs, suf_bytes);
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
   half8 qb[NDS];
   {
     const bool live = col < cnt;
-    const uint16_t *qrow = b.Q + ((size_t)heads[live ? col : 0] * p.M + qi) * D;
+    const uint16_t *qrow = (const uint16_t *)b.Q + ((size_t)heads[live ? col : 0] * p.M + qi) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       const half8 v = *(const half8 *)(qrow + 16 * ds + 8 * hl);

@@ -173,7 +173,8 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = heads[r < cnt ? r : 0];
-    const uint4 *qp = (const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + 32 * (grp ? g : 0));
+    const uint4 *qp =
+        (const uint4 *)((const uint16_t *)b.Q + ((size_t)h * p.M + qi) * D + 32 * (grp ? g : 0));
     float qs = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {

@@ -1,6 +1,7 @@
-// Split-over-keys attention over fp16 keys and values (VALU path), with the split
-// merge done in-kernel. Serves an fp16 prefix and the fp16 causal suffix of a fused
-// query (the mlx4g32 prefix has its own kernel).
+// Split-over-keys attention over fp16 (or fp32) keys and values (VALU path), with the
+// split merge done in-kernel. Serves an fp16 or fp32 prefix and the causal suffix of a
+// fused query in the same precision (the mlx4g32 prefix has its own kernel; its suffix
+// is fp16 and runs here).
 //
 // What is computed: for each query row (q-head h, query index i) and each key span of
 // a workgroup, the online-softmax partial
@@ -8,8 +9,8 @@
 // with s_j = log2(e)/sqrt(D) * (q . k_j), the scaled logit in log2 units. The spans of
 // a row are merged by the LSE rule (split_common.h).
 //
-// Layout and schedule. A key row of D halves is read by LPR consecutive lanes, 16 bytes
-// each, LPR = D/8 rounded up to a power of two (for D = 96, 160, 192 the lanes past D/8
+// Layout and schedule. A key row of D values is read by LPR consecutive lanes, 8 values
+// (16 bytes of fp16, 32 of fp32) each, LPR = D/8 rounded up to a power of two (for D = 96, 160, 192 the lanes past D/8
 // hold no dims and load nothing); one wave-wide load covers 64/LPR whole rows, fully
 // coalesced. Each group of LPR lanes is a "slot" that runs its own online softmax over
 // the keys it sees, so the inner loop needs no cross-lane max: only the LPR-lane
@@ -147,15 +148,29 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
 }
 
 // One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.
-template <int U>
+// One tile: U keys per lane (keys base + u*KPI + kk), NV 16-byte pieces per key and side.
+template <int U, int NV>
 struct Tile {
-  uint4 k[U], v[U];
+  uint4 k[U][NV], v[U][NV];
   bool ok[U];
 };
 
-template <int D, int R, int U, bool GATHER>
+// A lane's 8 q values of each row: fp16 pairs, or fp32.
+template <bool F32, int R>
+struct QRegs {
+  h2_t q[R][4];
+};
+template <int R>
+struct QRegs<true, R> {
+  float q[R][8];
+};
+
+__device__ __forceinline__ float f32_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+template <int D, int R, int U, bool GATHER, bool F32>
 __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   constexpr int LPR = fp16_row_lanes(D), KPI = 64 / LPR, STEP = KPI * U;
+  constexpr int ESZ = F32 ? 4 : 2, NV = F32 ? 2 : 1;  // bytes per value, pieces per 8 values
   __shared__ Scratch<D, R> sm;
   __shared__ int gsp[GATHER ? kGatherChunk : 1];  // the span's token indices
   const int lane = threadIdx.x & 63;
@@ -169,17 +184,28 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   const int hg = y / p.M, qi = y - hg * p.M;
   const int g = p.rg.g[hg], cnt = p.rg.cnt[hg];
   const uint8_t *heads = p.rg.heads[hg];
-  // q of each row: this lane's 8 halves
-  h2_t q[R][4];
+  // q of each row: this lane's 8 values
+  QRegs<F32, R> qr;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int h = heads[r < cnt ? r : 0];
-    const uint4 qq = dims ? *(const uint4 *)(b.Q + ((size_t)h * p.M + qi) * D + sub * 8)
-                          : make_uint4(0, 0, 0, 0);
-    q[r][0] = as_h2(qq.x);
-    q[r][1] = as_h2(qq.y);
-    q[r][2] = as_h2(qq.z);
-    q[r][3] = as_h2(qq.w);
+    const uint4 *qp =
+        (const uint4 *)((const char *)b.Q + (((size_t)h * p.M + qi) * D + sub * 8) * ESZ);
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const uint4 qq = dims ? qp[t] : make_uint4(0, 0, 0, 0);
+      if constexpr (F32) {
+        qr.q[r][4 * t] = f32_bits(qq.x);
+        qr.q[r][4 * t + 1] = f32_bits(qq.y);
+        qr.q[r][4 * t + 2] = f32_bits(qq.z);
+        qr.q[r][4 * t + 3] = f32_bits(qq.w);
+      } else {
+        qr.q[r][0] = as_h2(qq.x);
+        qr.q[r][1] = as_h2(qq.y);
+        qr.q[r][2] = as_h2(qq.z);
+        qr.q[r][3] = as_h2(qq.w);
+      }
+    }
   }
 
   float m[R], l[R], acc[R][8];
@@ -195,7 +221,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   const int seg0 = x * p.seg_per_span, seg1 = min(seg0 + p.seg_per_span, b.n_seg);
   for (int sgi = seg0; sgi < seg1; ++sgi) {
     Span sp = get_segment(p, sgi, b.pre_splits, b.N, g, qi);
-    if (!sp.suffix && p.fmt != 0) continue;  // an mlx4g32 prefix has its own kernel
+    if (!sp.suffix && p.fmt == 1) continue;  // an mlx4g32 prefix has its own kernel
     if constexpr (GATHER) {  // list positions [j0, j1) of q-head heads[0]'s token list
       const int h = heads[0];
       sp.j1 = min(sp.j1, max(sp.j0, min(p.gcount[h], p.gmax)));
@@ -204,17 +230,17 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
         gsp[t] = p.gidx[(size_t)h * p.gmax + sp.j0 + t];
       __syncthreads();
     }
-    const uint16_t *Kf, *Vf;
+    const char *Kf, *Vf;  // kv-head g's rows of this segment's keys
     if (sp.suffix) {
-      Kf = p.Ksuf + (size_t)g * p.S_suf * D;
-      Vf = p.Vsuf + (size_t)g * p.S_suf * D;
+      Kf = (const char *)p.Ksuf + (size_t)g * p.S_suf * D * ESZ;
+      Vf = (const char *)p.Vsuf + (size_t)g * p.S_suf * D * ESZ;
     } else {
       const KVView kv = make_view(p.kv_base[z], p.fmt, p.H_kv, b.N, D);
-      Kf = kv.K + (size_t)g * b.N * D;
-      Vf = kv.V + (size_t)g * b.N * D;
+      Kf = (const char *)kv.K + (size_t)g * b.N * D * ESZ;
+      Vf = (const char *)kv.V + (size_t)g * b.N * D * ESZ;
     }
 
-    auto load = [&](Tile<U> &t, int base) {
+    auto load = [&](Tile<U, NV> &t, int base) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         int j = base + u * KPI + kk;
@@ -224,25 +250,39 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
           t.ok[u] = t.ok[u] && tok >= 0 && tok < b.N;
           j = tok;
         }
-        if (t.ok[u] && dims) {
-          t.k[u] = ld_stream16(Kf + (size_t)j * D + sub * 8);
-          t.v[u] = ld_stream16(Vf + (size_t)j * D + sub * 8);
-        } else {
-          t.k[u] = make_uint4(0, 0, 0, 0);
-          t.v[u] = make_uint4(0, 0, 0, 0);
+        const size_t off = ((size_t)j * D + sub * 8) * ESZ;
+#pragma unroll
+        for (int w = 0; w < NV; ++w) {
+          if (t.ok[u] && dims) {
+            t.k[u][w] = ld_stream16(Kf + off + 16 * w);
+            t.v[u][w] = ld_stream16(Vf + off + 16 * w);
+          } else {
+            t.k[u][w] = make_uint4(0, 0, 0, 0);
+            t.v[u][w] = make_uint4(0, 0, 0, 0);
+          }
         }
       }
     };
 
-    auto consume = [&](const Tile<U> &t) {
+    auto consume = [&](const Tile<U, NV> &t) {
       float vals[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t w4[4] = {t.v[u].x, t.v[u].y, t.v[u].z, t.v[u].w};
+        if constexpr (F32) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          vals[u][2 * c] = h2f((uint16_t)(w4[c] & 0xffffu));
-          vals[u][2 * c + 1] = h2f((uint16_t)(w4[c] >> 16));
+          for (int w = 0; w < 2; ++w) {
+            vals[u][4 * w] = f32_bits(t.v[u][w].x);
+            vals[u][4 * w + 1] = f32_bits(t.v[u][w].y);
+            vals[u][4 * w + 2] = f32_bits(t.v[u][w].z);
+            vals[u][4 * w + 3] = f32_bits(t.v[u][w].w);
+          }
+        } else {
+          const uint32_t w4[4] = {t.v[u][0].x, t.v[u][0].y, t.v[u][0].z, t.v[u][0].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            vals[u][2 * c] = h2f((uint16_t)(w4[c] & 0xffffu));
+            vals[u][2 * c + 1] = h2f((uint16_t)(w4[c] >> 16));
+          }
         }
       }
 #pragma unroll
@@ -250,10 +290,22 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
         float s[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          float dsum = __builtin_amdgcn_fdot2(q[r][0], as_h2(t.k[u].x), 0.f, false);
-          dsum = __builtin_amdgcn_fdot2(q[r][1], as_h2(t.k[u].y), dsum, false);
-          dsum = __builtin_amdgcn_fdot2(q[r][2], as_h2(t.k[u].z), dsum, false);
-          dsum = __builtin_amdgcn_fdot2(q[r][3], as_h2(t.k[u].w), dsum, false);
+          float dsum;
+          if constexpr (F32) {
+            dsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              dsum = __builtin_fmaf(qr.q[r][4 * w], f32_bits(t.k[u][w].x), dsum);
+              dsum = __builtin_fmaf(qr.q[r][4 * w + 1], f32_bits(t.k[u][w].y), dsum);
+              dsum = __builtin_fmaf(qr.q[r][4 * w + 2], f32_bits(t.k[u][w].z), dsum);
+              dsum = __builtin_fmaf(qr.q[r][4 * w + 3], f32_bits(t.k[u][w].w), dsum);
+            }
+          } else {
+            dsum = __builtin_amdgcn_fdot2(qr.q[r][0], as_h2(t.k[u][0].x), 0.f, false);
+            dsum = __builtin_amdgcn_fdot2(qr.q[r][1], as_h2(t.k[u][0].y), dsum, false);
+            dsum = __builtin_amdgcn_fdot2(qr.q[r][2], as_h2(t.k[u][0].z), dsum, false);
+            dsum = __builtin_amdgcn_fdot2(qr.q[r][3], as_h2(t.k[u][0].w), dsum, false);
+          }
           dsum = group_sum<LPR>(dsum);
           s[u] = t.ok[u] ? dsum * p.qscale : -INFINITY;
         }
@@ -276,11 +328,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
     };
 
     int base = sp.j0 + wave * STEP;
-    Tile<U> cur;
+    Tile<U, NV> cur;
     if (base < sp.j1) load(cur, base);
     while (base < sp.j1) {
       const int next = base + 4 * STEP;
-      Tile<U> nxt;
+      Tile<U, NV> nxt;
       if (next < sp.j1) load(nxt, next);
       consume(cur);
       cur = nxt;
@@ -290,13 +342,19 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
   finish<D, R, LPR>(p, b, sm, m, l, acc, heads, cnt, qi, x);
 }
 
+// fp32 (slot format 2) tiles hold twice the bytes per key, so half the keys per lane
 template <int D, int R>
 hipError_t launch_partial_d(const PartialParams &p, int x_count, hipStream_t s) {
   dim3 grid(x_count, p.y_groups, p.n_prob);
-  if (p.gidx)
-    hipLaunchKernelGGL((attn_split_kernel<D, 1, 4, true>), grid, dim3(256), 0, s, p);
+  const bool f32 = p.fmt == 2;
+  if (p.gidx && f32)
+    hipLaunchKernelGGL((attn_split_kernel<D, 1, 2, true, true>), grid, dim3(256), 0, s, p);
+  else if (p.gidx)
+    hipLaunchKernelGGL((attn_split_kernel<D, 1, 4, true, false>), grid, dim3(256), 0, s, p);
+  else if (f32)
+    hipLaunchKernelGGL((attn_split_kernel<D, R, 2, false, true>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_split_kernel<D, R, 4, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<D, R, 4, false, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -329,8 +387,9 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
   if (p.S_max > kMaxSplits || p.n_prob > kMaxBatch) return hipErrorInvalidValue;
   // a token list: one q-head per row group, one segment per span of at most kGatherChunk
   if (p.gidx && (rows_per_group != 1 || p.seg_per_span != 1 || p.pre_chunk > kGatherChunk ||
-                 p.n_prob != 1 || p.fmt != 0))
+                 p.n_prob != 1 || p.fmt == 1))
     return hipErrorInvalidValue;
+  if (p.esz != (p.fmt == 2 ? 4 : 2)) return hipErrorInvalidValue;
   switch (p.D) {
     case 32: return launch_partial_r<32>(p, rows_per_group, x_count, s);
     case 64: return launch_partial_r<64>(p, rows_per_group, x_count, s);

@@ -41,7 +41,8 @@ constexpr int kGatherChunk = 2048;  // token-list positions per span
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Byte offsets of the arrays inside one slot allocation; host (store) and device
-// (query) both derive pointers from this. fp16: K, V [H, N, D]. mlx4g32: K codes
+// (query) both derive pointers from this. fmt 0 fp16 / fmt 2 fp32: K, V [H, N, D]. fmt 1
+// mlx4g32: K codes
 // [H, N, D/8] u32, K scale/bias pairs [H, N, D/32] u32 (fp16 scale in the low half,
 // fp16 bias in the high half), then the same two for V. A lane that owns one group of
 // one token reads its 16 code bytes and its 4-byte pair with two loads.
@@ -53,8 +54,8 @@ struct SlotLayout {
 __host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int N, int D) {
   SlotLayout L;
   const size_t elems = (size_t)H * N * D;
-  if (fmt == 0) {
-    const size_t b = (elems * 2 + 255) & ~(size_t)255;
+  if (fmt != 1) {
+    const size_t b = (elems * (fmt == 2 ? 4 : 2) + 255) & ~(size_t)255;
     L.off[0] = 0;
     L.off[1] = b;
     L.off[2] = L.off[3] = 0;
@@ -73,9 +74,9 @@ __host__ __device__ inline SlotLayout slot_layout(int fmt, int H, int N, int D) 
 
 // One resident prefix as the kernels see it.
 struct KVView {
-  int fmt;              // 0 fp16, 1 mlx4g32
+  int fmt;              // 0 fp16, 1 mlx4g32, 2 fp32
   int H, N, D;
-  const uint16_t *K, *V;                 // fp16 [H, N, D]
+  const void *K, *V;                     // fp16 or fp32 [H, N, D]
   const uint32_t *Kc, *Vc;               // mlx4g32 codes [H, N, D/8]
   const uint32_t *Ksb, *Vsb;             // mlx4g32 (scale | bias << 16) [H, N, D/32]
 };
@@ -91,9 +92,9 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
   v.K = v.V = nullptr;
   v.Kc = v.Vc = nullptr;
   v.Ksb = v.Vsb = nullptr;
-  if (fmt == 0) {
-    v.K = (const uint16_t *)(b + L.off[0]);
-    v.V = (const uint16_t *)(b + L.off[1]);
+  if (fmt != 1) {
+    v.K = b + L.off[0];
+    v.V = b + L.off[1];
   } else {
     v.Kc = (const uint32_t *)(b + L.off[0]);
     v.Ksb = (const uint32_t *)(b + L.off[1]);
@@ -120,11 +121,12 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
 // out and lse.
 struct PartialParams {
   int H_q, M, D, H_kv, fmt;
+  int esz;                // bytes per element of Q and the suffix: 4 for an fp32 slot, else 2
   float qscale;           // log2(e) / sqrt(D)
   int n_prob;
   const void *kv_base[kMaxBatch];
   int N[kMaxBatch];
-  const uint16_t *Q;      // fp16 [n_prob][H_q, M, D]
+  const void *Q;          // fp16 (fp32 for an fp32 slot) [n_prob][H_q, M, D]
   size_t q_stride;
   float *out;             // [n_prob][H_q, M, D]
   size_t out_stride;
@@ -138,7 +140,7 @@ struct PartialParams {
   // [0, N) are skipped. The prefix segments then chunk the list positions [0, gmax).
   const int32_t *gidx, *gcount;  // [H, gmax], [H] or null
   int gmax;
-  const uint16_t *Ksuf, *Vsuf;  // fp16 [H_kv, S_suf, D] (single problem only)
+  const void *Ksuf, *Vsuf;  // fp16 (fp32) [H_kv, S_suf, D] (single problem only)
   int S_suf, suf_chunk, suf_splits;
   int seg_per_span;       // segments per span (>= 1)
   int S_max;              // span stride of the partial layout
@@ -193,12 +195,14 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s);
 // V-store rows of one layer (kv = H * D values per token): fmt 0 = fp16 [N, kv], fmt 1 =
 // mlx4g32 records of 5 * kv / 8 bytes. Fetch: fp32 [count, kv] of tokens start ..
 // start + count - 1. Relayout into a slot: fp16 [H, N, D] (dequantized and rounded for
-// fmt 1), or, from fmt 1, mlx4g32 codes [H, N, D/8] and (scale | bias << 16) pairs
-// [H, N, D/32].
+// fmt 1), fp32 [H, N, D] (dequantized), or, from fmt 1, mlx4g32 codes [H, N, D/8] and
+// (scale | bias << 16) pairs [H, N, D/32].
 hipError_t launch_vstore_fetch(const void *rows, int fmt, int kv, int64_t start, int64_t count,
                                float *out, hipStream_t s);
 hipError_t launch_rows_to_fp16_slot(const void *rows, int fmt, int64_t N, int H, int D,
                                     uint16_t *dst, hipStream_t s);
+hipError_t launch_rows_to_fp32_slot(const void *rows, int fmt, int64_t N, int H, int D,
+                                    float *dst, hipStream_t s);
 hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, uint32_t *codes,
                                     uint32_t *pairs, hipStream_t s);
 

@@ -333,12 +333,12 @@ int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4) {
 }
 
 struct AttnCall {
-  const uint16_t *Q;
+  const void *Q;          // fp16, or fp32 for an fp32 slot
   size_t q_stride;        // elements between problems
   int H_q, M, D;
   const std::vector<int> *hm;
   int H_kv;
-  const uint16_t *Ksuf, *Vsuf;
+  const void *Ksuf, *Vsuf;  // the slot's precision (fp16 for an mlx4g32 slot)
   int S_suf;
   const int32_t *blocks;  // device [H_kv, K_top] or null
   int n_sel, K_top, B;
@@ -356,11 +356,11 @@ constexpr int kMfmaMinRows = 32;
 int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   PrefillParams p;
   memset(&p, 0, sizeof(p));
-  p.Q = c.Q;
-  p.K = sl.view.K;
-  p.V = sl.view.V;
-  p.Ksuf = c.S_suf > 0 ? c.Ksuf : nullptr;
-  p.Vsuf = c.S_suf > 0 ? c.Vsuf : nullptr;
+  p.Q = (const uint16_t *)c.Q;
+  p.K = (const uint16_t *)sl.view.K;
+  p.V = (const uint16_t *)sl.view.V;
+  p.Ksuf = c.S_suf > 0 ? (const uint16_t *)c.Ksuf : nullptr;
+  p.Vsuf = c.S_suf > 0 ? (const uint16_t *)c.Vsuf : nullptr;
   p.H_q = c.H_q;
   p.M = c.M;
   p.D = c.D;
@@ -435,6 +435,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   p.D = c.D;
   p.H_kv = s0.H;
   p.fmt = s0.fmt;
+  p.esz = s0.fmt == PION_KV_FP32 ? 4 : 2;
   p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
   p.n_prob = n_prob;
   int N_max = 0;
@@ -510,6 +511,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     // 32-bit buffer ranges.
     const long long row_bytes = 2LL * c.D;
     const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && gqa_dim(c.D) &&
+                        s0.fmt == PION_KV_FP16 &&
                         N_max * row_bytes < (1LL << 31) &&
                         (long long)c.S_suf * row_bytes < (1LL << 31) &&
                         !getenv_flag("PION_NO_GQA_MFMA");
@@ -536,7 +538,8 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
 // Shape checks shared by STORE and WARM.
 int check_slot_shape(const char *sid, int H, int N, int D, int kv_format) {
   if (!sid_ok(sid) || H < 1 || H > 255 || N < 1 || D <= 0) return PION_ERR_INVALID;
-  if (kv_format != PION_KV_FP16 && kv_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
+  if (kv_format != PION_KV_FP16 && kv_format != PION_KV_MLX4G32 && kv_format != PION_KV_FP32)
+    return PION_ERR_INVALID;
   if (kv_format == PION_KV_MLX4G32 && D % 32) return PION_ERR_INVALID;
   if (!d_supported(D)) return PION_ERR_UNSUPPORTED;
   if ((size_t)N * D > ((size_t)1 << 40)) return PION_ERR_INVALID;
@@ -546,14 +549,15 @@ int check_slot_shape(const char *sid, int H, int N, int D, int kv_format) {
   return PION_OK;
 }
 
-// Write a slot's arrays from fp16 K, V [H, N, D]: copies, or the mlx4g32 encoder with
-// scale and bias interleaved as (scale | bias << 16) words.
+// Write a slot's arrays from K, V [H, N, D] (fp32 for an fp32 slot, else fp16): copies,
+// or the mlx4g32 encoder with scale and bias interleaved as (scale | bias << 16) words.
 hipError_t fill_from_fp16(char *base, const SlotLayout &L, int kv_format, const void *K,
                           const void *V, size_t elems, int D, hipStream_t st) {
-  if (kv_format == PION_KV_FP16) {
-    hipError_t e = hipMemcpyAsync(base + L.off[0], K, elems * 2, hipMemcpyDeviceToDevice, st);
+  if (kv_format != PION_KV_MLX4G32) {
+    const size_t bytes = elems * (kv_format == PION_KV_FP32 ? 4 : 2);
+    hipError_t e = hipMemcpyAsync(base + L.off[0], K, bytes, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return e;
-    return hipMemcpyAsync(base + L.off[1], V, elems * 2, hipMemcpyDeviceToDevice, st);
+    return hipMemcpyAsync(base + L.off[1], V, bytes, hipMemcpyDeviceToDevice, st);
   }
   const int64_t rows = (int64_t)(elems / D);
   uint16_t *ksb = (uint16_t *)(base + L.off[1]), *vsb = (uint16_t *)(base + L.off[3]);
@@ -712,6 +716,13 @@ int pion_prefix_warm(const char *sid, int layer, int H, int N, int D, int src_fo
           return launch_rows_to_fp16_slot(V_rows, src_format, N, H, D,
                                           (uint16_t *)(base + L.off[1]), st);
         }
+        if (kv_format == PION_KV_FP32) {  // dequantized to fp32 and transposed
+          hipError_t e = launch_rows_to_fp32_slot(K_rows, src_format, N, H, D,
+                                                  (float *)(base + L.off[0]), st);
+          if (e != hipSuccess) return e;
+          return launch_rows_to_fp32_slot(V_rows, src_format, N, H, D,
+                                          (float *)(base + L.off[1]), st);
+        }
         if (src_format == PION_KV_MLX4G32) {  // codes, scales and biases move unchanged
           hipError_t e = launch_rows_to_mlx4_slot(K_rows, N, H, D, (uint32_t *)(base + L.off[0]),
                                                   (uint32_t *)(base + L.off[1]), st);
@@ -856,7 +867,7 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const v
   hipStream_t st = (hipStream_t)stream;
   if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
   AttnCall c{};
-  c.Q = (const uint16_t *)Q;
+  c.Q = Q;
   c.H_q = H_q;
   c.M = M;
   c.D = D;
@@ -895,7 +906,7 @@ int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q,
     if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
   }
   AttnCall c{};
-  c.Q = (const uint16_t *)Q;
+  c.Q = Q;
   c.q_stride = (size_t)H_q * M * D;
   c.H_q = H_q;
   c.M = M;
@@ -932,14 +943,14 @@ int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, i
   hipStream_t st = (hipStream_t)stream;
   if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
   AttnCall c{};
-  c.Q = (const uint16_t *)Q;
+  c.Q = Q;
   c.H_q = H_q;
   c.M = M;
   c.D = D;
   c.hm = &hm;
   c.H_kv = H_kv;
-  c.Ksuf = (const uint16_t *)K_suf;
-  c.Vsuf = (const uint16_t *)V_suf;
+  c.Ksuf = K_suf;
+  c.Vsuf = V_suf;
   c.S_suf = S_suf;
   c.out = out;
   c.lse = lse;
@@ -1030,19 +1041,19 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
   // the selection's tickets use the stream's split counters (zero between launches)
   int *counters;
   if (get_counters(st, &counters) != hipSuccess) return PION_ERR_NOMEM;
-  if (launch_block_select((const uint16_t *)Q, hmap, it->second.ptr, H_kv, nb, D, K_top,
+  if (launch_block_select(Q, sl->fmt == PION_KV_FP32, hmap, it->second.ptr, H_kv, nb, D, K_top,
                           keys, cand, counters, blocks, st) != hipSuccess)
     return PION_ERR_HIP;
 
   AttnCall c{};
-  c.Q = (const uint16_t *)Q;
+  c.Q = Q;
   c.H_q = H_q;
   c.M = 1;
   c.D = D;
   c.hm = &hm;
   c.H_kv = H_kv;
-  c.Ksuf = (const uint16_t *)K_suf;
-  c.Vsuf = (const uint16_t *)V_suf;
+  c.Ksuf = K_suf;
+  c.Vsuf = V_suf;
   c.S_suf = S_suf;
   c.blocks = blocks;
   c.n_sel = n_sel;
@@ -1067,7 +1078,7 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
   Slot *sl = find_slot(sid, layer);
   if (!sl) return absent_status(sid, layer);
   if (sl->D != D || sl->H != H) return PION_ERR_INVALID;
-  if (sl->fmt != PION_KV_FP16) return PION_ERR_UNSUPPORTED;
+  if (sl->fmt == PION_KV_MLX4G32) return PION_ERR_UNSUPPORTED;
   if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse)) || !on_device(indices) ||
       !on_device(counts))
     return PION_ERR_INVALID;
@@ -1076,7 +1087,7 @@ int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_spa
   std::vector<int> hm(H);
   for (int h = 0; h < H; ++h) hm[h] = h;
   AttnCall c{};
-  c.Q = (const uint16_t *)Q;
+  c.Q = Q;
   c.H_q = H;
   c.M = 1;
   c.D = D;

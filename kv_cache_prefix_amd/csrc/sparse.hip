@@ -33,7 +33,9 @@ __global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int n
       const size_t tok = (size_t)g * kv.N + j;
       float x;
       if (FMT == 0) {
-        x = h2f(kv.K[tok * D + d]);
+        x = h2f(((const uint16_t *)kv.K)[tok * D + d]);
+      } else if (FMT == 2) {
+        x = ((const float *)kv.K)[tok * D + d];
       } else {
         const uint32_t w = kv.Kc[tok * (D / 8) + d / 8];
         const float c = (float)((w >> (4 * (d % 8))) & 0xFu);
@@ -101,8 +103,8 @@ constexpr int kSelCand = 512;   // candidate merge: at most this many candidates
 //   then one scan in block order places each chosen block at
 //     (blocks with key > T before it) + min(blocks with key T before it, need),
 //   which is ascending index order with ties going to the lower index.
-template <int D>
-__global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__restrict__ Q,
+template <int D, bool Q32>
+__global__ __launch_bounds__(256) void block_select_kernel(const void *__restrict__ Q,
                                                            HeadMap hm,
                                                            const float *__restrict__ kmean,
                                                            int nb, int K_top, uint32_t *keys,
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(const uint16_t *__res
     float a = 0.f;
 #pragma unroll 8
     for (int h = 0; h < hm.H_q; ++h) {
-      const float v = h2f(Q[(size_t)h * D + d]);
+      const float v = Q32 ? ((const float *)Q)[(size_t)h * D + d]
+                          : h2f(((const uint16_t *)Q)[(size_t)h * D + d]);
       if (hm.m[h] == g) a += v;
     }
     qsum[d] = a;
@@ -352,20 +355,26 @@ hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t 
   const int threads = kv.D < 256 ? kv.D : 256;
   if (kv.fmt == 0)
     hipLaunchKernelGGL(block_mean_kernel<0>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
+  else if (kv.fmt == 2)
+    hipLaunchKernelGGL(block_mean_kernel<2>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
   else
     hipLaunchKernelGGL(block_mean_kernel<1>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
   return hipGetLastError();
 }
 
-hipError_t launch_block_select(const uint16_t *Q, const HeadMap &hm, const float *kmean,
+hipError_t launch_block_select(const void *Q, bool q32, const HeadMap &hm, const float *kmean,
                                int H_kv, int nb, int D, int K_top, uint32_t *keys,
                                uint64_t *cand, int *counters, int32_t *blocks, hipStream_t s) {
   if (K_top < 1 || nb < 1 || H_kv < 1) return hipErrorInvalidValue;
   dim3 grid((nb + kSelBlocks - 1) / kSelBlocks, H_kv);
-#define PION_SELECT_D(DD)                                                                    \
-  case DD:                                                                                 \
-    hipLaunchKernelGGL(block_select_kernel<DD>, grid, dim3(256), 0, s, Q, hm, kmean, nb, K_top, \
-                       keys, cand, counters, blocks);                                      \
+#define PION_SELECT_D(DD)                                                                  \
+  case DD:                                                                               \
+    if (q32)                                                                             \
+      hipLaunchKernelGGL((block_select_kernel<DD, true>), grid, dim3(256), 0, s, Q, hm, kmean, \
+                         nb, K_top, keys, cand, counters, blocks);                       \
+    else                                                                                 \
+      hipLaunchKernelGGL((block_select_kernel<DD, false>), grid, dim3(256), 0, s, Q, hm,     \
+                         kmean, nb, K_top, keys, cand, counters, blocks);                \
     break;
   switch (D) {
     PION_SELECT_D(32)

@@ -93,7 +93,7 @@ __device__ __forceinline__ Span get_segment(const PartialParams &p, int x, int p
 // Per-problem pointers of this workgroup.
 struct Prob {
   int N, pre_splits, n_seg, S_total;  // pre_splits: prefix segments
-  const uint16_t *Q;
+  const void *Q;
   float *out, *lse, *part_acc, *part_m, *part_l;
   int *counter;
 };
@@ -104,7 +104,7 @@ __device__ __forceinline__ Prob get_prob(const PartialParams &p, int z, int y) {
   b.pre_splits = p.blocks ? p.n_sel : ((p.gidx ? p.gmax : b.N) + p.pre_chunk - 1) / p.pre_chunk;
   b.n_seg = b.pre_splits + p.suf_splits;
   b.S_total = (b.n_seg + p.seg_per_span - 1) / p.seg_per_span;
-  b.Q = p.Q + z * p.q_stride;
+  b.Q = (const char *)p.Q + z * p.q_stride * p.esz;
   b.out = p.out + z * p.out_stride;
   b.lse = p.lse ? p.lse + z * p.lse_stride : nullptr;
   b.part_acc = p.part_acc + z * p.part_stride;

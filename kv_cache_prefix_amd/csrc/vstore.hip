@@ -144,6 +144,33 @@ __global__ __launch_bounds__(256) void rows_to_fp16_slot_kernel(const uint8_t *_
   }
 }
 
+// KV.PREFIX.WARM into an fp32 slot: rows [N, H*D] -> dst [H, N, D], 4 values per item
+// (the fetch's values, transposed).
+template <int FMT, bool WIDE>
+__global__ __launch_bounds__(256) void rows_to_fp32_slot_kernel(const uint8_t *__restrict__ rows,
+                                                                int64_t N, int H, int D,
+                                                                float *__restrict__ dst) {
+  const int kv = H * D, qpr = kv / 4, dq4 = D / 4;
+  const int64_t total = N * qpr, stride = (int64_t)gridDim.x * 256;
+  const int64_t rb = FMT == 0 ? 2LL * kv : (int64_t)kv * 5 / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const Item c = item_of<WIDE>(i, qpr);
+    const uint8_t *row = rows + c.n * rb;
+    const int h = c.k / dq4, d4 = c.k - h * dq4;
+    f32x4_nt v;
+    if (FMT == 0) {
+      const u32x2_nt x = __builtin_nontemporal_load((const u32x2_nt *)(row + 8 * c.k));
+      v = f32x4_nt{half_bits(x.x & 0xffffu), half_bits(x.x >> 16), half_bits(x.y & 0xffffu),
+                   half_bits(x.y >> 16)};
+    } else {
+      Word r = read_word(row, kv, c.k >> 1);
+      r.w >>= 16 * (c.k & 1);
+      v = f32x4_nt{dq(r, 0), dq(r, 1), dq(r, 2), dq(r, 3)};
+    }
+    *(f32x4_nt *)(dst + ((int64_t)h * N + c.n) * D + 4 * d4) = v;
+  }
+}
+
 // KV.PREFIX.WARM into an mlx4g32 slot from mlx4g32 rows: the codes and the (scale |
 // bias << 16) pairs move to the slot layout unchanged, one code word per item.
 template <bool WIDE>
@@ -215,6 +242,21 @@ hipError_t launch_rows_to_fp16_slot(const void *rows, int fmt, int64_t N, int H,
   } else {
     if (narrow(total)) hipLaunchKernelGGL((rows_to_fp16_slot_kernel<1, false>), g, b, 0, s, r, N, H, D, dst);
     else hipLaunchKernelGGL((rows_to_fp16_slot_kernel<1, true>), g, b, 0, s, r, N, H, D, dst);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_to_fp32_slot(const void *rows, int fmt, int64_t N, int H, int D,
+                                    float *dst, hipStream_t s) {
+  const int64_t total = N * (H * D / 4);
+  const dim3 g(grid_for(total)), b(256);
+  const uint8_t *r = (const uint8_t *)rows;
+  if (fmt == 0) {
+    if (narrow(total)) hipLaunchKernelGGL((rows_to_fp32_slot_kernel<0, false>), g, b, 0, s, r, N, H, D, dst);
+    else hipLaunchKernelGGL((rows_to_fp32_slot_kernel<0, true>), g, b, 0, s, r, N, H, D, dst);
+  } else {
+    if (narrow(total)) hipLaunchKernelGGL((rows_to_fp32_slot_kernel<1, false>), g, b, 0, s, r, N, H, D, dst);
+    else hipLaunchKernelGGL((rows_to_fp32_slot_kernel<1, true>), g, b, 0, s, r, N, H, D, dst);
   }
   return hipGetLastError();
 }

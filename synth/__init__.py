@@ -6,7 +6,8 @@ bench) take their inputs from here, so both sides see the same fp16 bits.
 
 Recipe (numpy PCG64 via ``default_rng``):
   * every tensor is drawn as ``standard_normal`` in fp64 and cast to fp16 with
-    round-to-nearest-even (numpy's cast);
+    round-to-nearest-even (numpy's cast), or to fp32 (``dtype="float32"``, for
+    fp32-resident slots: same draws, more mantissa bits kept);
   * draw order per (config, layer): Q, K, V, suffix K, suffix V, then extras
     (per-channel K scales, needle block choice);
   * the tiny dense case uses seed 0; every other case uses seed ``[case, layer]``;
@@ -84,17 +85,19 @@ def rng_for(case: Case, layer: int = 0) -> np.random.Generator:
     return np.random.default_rng([case.case_id, layer])
 
 
-def _normal16(rng: np.random.Generator, shape) -> np.ndarray:
-    return rng.standard_normal(shape).astype(np.float16)
+def _normal(rng: np.random.Generator, shape, dtype) -> np.ndarray:
+    return rng.standard_normal(shape).astype(dtype)
 
 
 def generate(case: Case, layer: int = 0, *, N: Optional[int] = None,
              M: Optional[int] = None, S_suf: Optional[int] = None,
              H_q: Optional[int] = None, H_kv: Optional[int] = None,
              D: Optional[int] = None, n_needles: Optional[int] = None,
-             seed=None) -> Inputs:
+             seed=None, dtype: str = "float16") -> Inputs:
     """Draw the inputs of ``case`` for ``layer``; keyword overrides shrink a shape
-    (same recipe, same draw order) for tests that need a smaller instance."""
+    (same recipe, same draw order) for tests that need a smaller instance. ``dtype``
+    is the element type of every returned tensor (float16, or float32)."""
+    dt = np.dtype(dtype)
     H_q = case.H_q if H_q is None else H_q
     H_kv = case.H_kv if H_kv is None else H_kv
     N = case.N if N is None else N
@@ -108,12 +111,12 @@ def generate(case: Case, layer: int = 0, *, N: Optional[int] = None,
     Vd = rng.standard_normal((H_kv, N, D))
     Ks = Vs = None
     if S_suf > 0:
-        Ks = _normal16(rng, (H_kv, S_suf, D))
-        Vs = _normal16(rng, (H_kv, S_suf, D))
+        Ks = _normal(rng, (H_kv, S_suf, D), dt)
+        Vs = _normal(rng, (H_kv, S_suf, D), dt)
     if case.k_channel_scale:
         c = rng.lognormal(0.0, 0.5, size=(H_kv, D))
         Kd = Kd * c[:, None, :]
-    Q = Qd.astype(np.float16)
+    Q = Qd.astype(dt)
     r = max(1, H_q // H_kv)
     head_map = (np.arange(H_q) // r).astype(np.int32)
     needles = None
@@ -129,8 +132,8 @@ def generate(case: Case, layer: int = 0, *, N: Optional[int] = None,
             for b in blocks:
                 Kd[g, b * case.B:min((b + 1) * case.B, N), :] += 3.0 * u
         needles = np.stack(picks)
-    K = Kd.astype(np.float16)
-    V = Vd.astype(np.float16)
+    K = Kd.astype(dt)
+    V = Vd.astype(dt)
     return Inputs(Q=Q, K=K, V=V, K_suf=Ks, V_suf=Vs, head_map=head_map, needles=needles)
 
 
