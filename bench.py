@@ -54,8 +54,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "3d36951da55e6491dfffb84580033b52718e1226371c4e3d189ceeb45ee57826",
-                  "bytes_per_launch": 269455604}
+DECODE_TRAFFIC = {"sources_sha256": "2283c20789d44568b40c1aeccf07ca7362bfc9d294d97f8f2db416bd6dd76d72",
+                  "bytes_per_launch": 269472883}
 
 
 def kernel_sources_sha256():

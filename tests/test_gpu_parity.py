@@ -659,3 +659,32 @@ def test_mfma_and_valu_paths_agree(kp, monkeypatch):
     ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
     for o, l in outs:
         check(o, l, ref, ref_lse)
+
+
+# ------------------------------------------------------------------ bench shapes of the NEXT rows
+def test_query_sparse_bench_shape(kp):
+    # the QUERY_SPARSE bench workload: H = 8, N = 65536, D = 128, 2048 random indices per head
+    import torch
+    H, N, D, KS = 8, 65536, 128, 2048
+    inp = synth.generate(synth.DECODE, 21, N=N, H_q=H, H_kv=H, D=D)
+    rng = np.random.default_rng(21)
+    idx = rng.integers(0, N, size=(H, KS)).astype(np.int32)
+    counts = np.full(H, KS, np.int32)
+    kp.pion_prefix_store("t", 900, dev(inp.K), dev(inp.V))
+    out, lse = empty((H, D)), empty((H,))
+    kp.pion_prefix_query_sparse("t", 900, dev(inp.Q), dev(idx), dev(counts), out, lse)
+    check(host(out), host(lse), *oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts))
+    kp.pion_prefix_drop("t", 900)
+
+
+def test_vstore_fetch_bench_shape(kp):
+    # one layer-side of the V-store bench workload: N = 2048 tokens, kv = 8 x 128, records
+    from oracle import vstore as ovs
+    inp = synth.generate(synth.DECODE, 31, N=2048, D=128, H_q=8, H_kv=8)
+    rows = np.ascontiguousarray(inp.V.transpose(1, 0, 2).reshape(2048, 1024))
+    rec = ovs.pack_records(*oracle.quantize(rows))
+    assert rec.shape == (2048, 640)
+    out = empty((2048, 1024))
+    kp.pion_vstore_fetch_f32(dev(rec), ovs.MLX4G32, 1024, 0, 2048, out)
+    want = ovs.fetch_f32(rec, ovs.MLX4G32, 1024, 0, 2048)
+    np.testing.assert_array_equal(host(out).view(np.uint32), want.view(np.uint32))
