@@ -29,10 +29,10 @@
 // when a tile's max exceeds it by more than kSlack (log2 units), so p <= 2^kSlack and
 // p * s stays within fp16 range for any fp16 scale (s <= 131008 / 15).
 //
-// End of span: the slots of a wave merge without LDS (DPP row rotations within each
-// 16-lane row, then the lane swaps across rows), the wave partials merge through LDS,
-// and the workgroup stores its partial, takes its ticket, and the last one merges the
-// row group.
+// End of span: the slots of each 16-lane row merge with DPP row rotations (for D = 512
+// also the 4 rows of a wave, by the lane swaps, so that the LDS partials fit), the row
+// (or wave) partials of the workgroup merge through LDS, and the workgroup stores its
+// partial, takes its ticket, and the last one merges the row group.
 #include "split_common.h"
 
 namespace pion {
@@ -68,29 +68,33 @@ __device__ __forceinline__ float swap_sum(float v, bool by32) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Combine the lanes of a wave that are NGP apart (the slots holding the same group):
-// row rotations by NGP, 2 NGP, ..., 8 inside each 16-lane row, then the two row swaps.
-template <int NGP>
-__device__ __forceinline__ float wave_slots_max(float v) {
+// Combine the lanes that are NGP apart (the slots holding the same group): row
+// rotations by NGP, 2 NGP, ..., 8 inside each 16-lane row; with WAVE also the two row
+// swaps, so that every lane of the wave holds the wave's result.
+template <int NGP, bool WAVE>
+__device__ __forceinline__ float slots_max(float v) {
   if constexpr (NGP <= 1) v = fmaxf(v, dpp<0x121>(v));
   if constexpr (NGP <= 2) v = fmaxf(v, dpp<0x122>(v));
   if constexpr (NGP <= 4) v = fmaxf(v, dpp<0x124>(v));
   if constexpr (NGP <= 8) v = fmaxf(v, dpp<0x128>(v));
-  return swap_max(swap_max(v, false), true);
+  if constexpr (WAVE) v = swap_max(swap_max(v, false), true);
+  return v;
 }
-template <int NGP>
-__device__ __forceinline__ float wave_slots_sum(float v) {
+template <int NGP, bool WAVE>
+__device__ __forceinline__ float slots_sum(float v) {
   if constexpr (NGP <= 1) v += dpp<0x121>(v);
   if constexpr (NGP <= 2) v += dpp<0x122>(v);
   if constexpr (NGP <= 4) v += dpp<0x124>(v);
   if constexpr (NGP <= 8) v += dpp<0x128>(v);
-  return swap_sum(swap_sum(v, false), true);
+  if constexpr (WAVE) v = swap_sum(swap_sum(v, false), true);
+  return v;
 }
 
-// Wave partials of a workgroup of NW waves.
+// Row (16-lane) partials of a workgroup of NW waves, or wave partials for D = 512.
 template <int D, int R, int NW>
 struct Mlx4Scratch {
-  static constexpr int kParts = NW;
+  static constexpr bool kWave = D >= 512;
+  static constexpr int kParts = kWave ? NW : 4 * NW;
   float m[kParts][R], l[kParts][R];
   union {
     alignas(16) float acc[kParts][R][D];
@@ -324,21 +328,22 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     base = next;
   }
 
-  // back to value units, bias added; slots of the wave merged
+  // back to value units, bias added; slots of the row (D = 512: of the wave) merged
+  constexpr bool WAVE = Mlx4Scratch<D, R, NW>::kWave;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float M = wave_slots_max<NGP>(m[r]);
+    const float M = slots_max<NGP, WAVE>(m[r]);
     const float f = fast_exp2(m[r] - M);
-    l[r] = wave_slots_sum<NGP>(l[r] * f);
+    l[r] = slots_sum<NGP, WAVE>(l[r] * f);
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const float v = __builtin_fmaf(acc[r][e], (e & 1) ? 1048576.0f : 16777216.0f, bs[r]);
-      acc[r][e] = wave_slots_sum<NGP>(v * f);
+      acc[r][e] = slots_sum<NGP, WAVE>(v * f);
     }
     m[r] = M;
   }
-  const int part = wave;
-  if (lane < NG) {  // slot 0's groups (lane = g)
+  const int part = WAVE ? wave : wave * 4 + (lane >> 4);
+  if ((WAVE ? lane : (lane & 15)) < NG) {  // slot 0's groups of the row (lane % 16 = g)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float4 *dst = (float4 *)&sm.acc[part][r][32 * g];

@@ -16,6 +16,14 @@ from test_gpu_parity import sparse_indices
 pytestmark = pytest.mark.gpu
 
 F32_OUT, F32_LSE = 1e-4, 2e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _drop_sessions(kp):
+    yield
+    kp.pion_prefix_drop("f32", -1)
+
+
 ALL_D = [32, 64, 96, 128, 160, 192, 256, 512]
 
 

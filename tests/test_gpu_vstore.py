@@ -14,6 +14,12 @@ from test_gpu_parity import check, dev, empty, host, kp, query  # noqa: F401
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(scope="module", autouse=True)
+def _drop_sessions(kp):
+    yield
+    kp.pion_prefix_drop("vs", -1)
+
+
 def records(x16):
     """fp16 [N, kv] -> mlx4g32 records uint8 [N, 5 kv / 8] (oracle encoder and layout)."""
     return ovs.pack_records(*oracle.quantize(x16))
@@ -80,8 +86,9 @@ def test_warm_into_mlx4g32_slot(kp, H, N, D, src):
 
 def test_warm_rehydrates_a_cold_key(kp):
     saved = kp.pion_prefix_stats()
+    assert saved["warm_slots"] == 0, "the slot table must start empty"
     try:
-        kp.pion_prefix_set_capacity(saved["warm_slots"] + 1, 0, 16)
+        kp.pion_prefix_set_capacity(1, 0, 16)
         a = synth.generate(synth.DECODE, 52, N=200, D=64, H_q=2, H_kv=2)
         b = synth.generate(synth.DECODE, 53, N=100, D=64, H_q=2, H_kv=2)
         kp.pion_prefix_store("vs", 0, dev(a.K), dev(a.V))
