@@ -27,6 +27,10 @@
  *     head-dim set of the "Shared KV Cache Serving" page); other values ->
  *     PION_ERR_UNSUPPORTED. Batched-Q (M >= 32) fp16 queries run on matrix cores for
  *     every D but 512, which runs on the vector split kernel (same results).
+ *   - Launch-plan limits: a query row is cut into at most 8192 key spans, and one query
+ *     index's partials (H_q x spans x D fp32) must stay under 2^31 bytes; a query whose
+ *     plan exceeds either returns PION_ERR_UNSUPPORTED before any launch (this happens
+ *     only for token lists near 2^24 positions at H = 128, D = 512).
  *   - Calls are thread-safe (one library-wide lock guards the slot table).
  */
 #ifndef PION_PREFIX_H

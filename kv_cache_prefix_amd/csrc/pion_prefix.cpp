@@ -45,7 +45,8 @@ namespace {
 
 using namespace pion;
 
-constexpr int kMaxSplitsTotal = 1024;  // spans per row: the in-kernel merge limit
+constexpr int kMaxSplitsTotal = 8192;  // spans per row: the in-kernel merge limit
+constexpr int kDenseSpans = 512;        // a dense key range is cut into at most this many
 constexpr int kMaxKTop = 1024;
 
 struct KMean {
@@ -327,8 +328,8 @@ int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4) {
   long long c = (keys * work_rows + target - 1) / target;
   c = std::max<long long>(c, granule);
   c = (c + granule - 1) / granule * granule;
-  // keep the span count within the in-kernel merge limit (1024 spans)
-  while ((keys + c - 1) / c > kMaxSplitsTotal / 2) c *= 2;
+  // keep the span count of a dense range at most kDenseSpans
+  while ((keys + c - 1) / c > kDenseSpans) c *= 2;
   return (int)std::min<long long>(c, 1LL << 30);
 }
 
@@ -477,6 +478,9 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   }
   p.S_max = pre_max + p.suf_splits;
   if (p.S_max > kMaxSplitsTotal) return PION_ERR_UNSUPPORTED;
+  // the kernels address one query index's partials (H_q x S_max x D fp32) with 32-bit
+  // byte offsets
+  if ((long long)c.H_q * p.S_max * c.D * 4 > 0x7fffffffLL) return PION_ERR_UNSUPPORTED;
   p.y_groups = Y;
 
   const size_t rows = (size_t)c.H_q * c.M;

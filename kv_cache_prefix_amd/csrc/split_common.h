@@ -23,7 +23,7 @@ namespace {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: 2^(kNegBig - kNegBig) = 1
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = 8192;  // spans of a row (partials per row in the workspace)
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ float h2f(uint16_t u) {
