@@ -176,3 +176,30 @@ def test_vstore_argument_validation(lib):
     assert w(b"s", 0, 2, 8, 64, 0, None, FAKE, 0, None) == kp.PION_ERR_INVALID
     assert w(b"s", 0, 2, 8, 64, 0, FAKE, FAKE, 0, None) == kp.PION_ERR_INVALID  # not device memory
     assert lib.pion_prefix_lookup(b"s", 0) == 0
+
+
+def test_binding_rejects_bad_tensors_before_calling_the_library(lib):
+    # the Python binding checks device, dtype, contiguity and shapes itself; on a CPU
+    # tensor it raises before any library call
+    import torch
+    cpu = torch.zeros((2, 8, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kp.pion_prefix_store("s", 0, cpu, cpu)
+    with pytest.raises(ValueError, match=r"\[H, N, D\]"):
+        kp.pion_prefix_store("s", 0, cpu, cpu[:1])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kp.pion_prefix_query("s", 0, torch.zeros((2, 1, 64), dtype=torch.float16),
+                             torch.zeros((2, 1, 64)))
+    with pytest.raises(ValueError, match="one query row"):
+        kp.pion_prefix_query_sparse("s", 0, torch.zeros((2, 3, 64), dtype=torch.float16),
+                                    torch.zeros((2, 4), dtype=torch.int32),
+                                    torch.zeros(2, dtype=torch.int32), torch.zeros((2, 64)))
+    with pytest.raises(ValueError, match="H_kv is required"):
+        kp.pion_prefix_query_fused("s", 0, torch.zeros((2, 1, 64), dtype=torch.float16), None, None,
+                                   torch.zeros((2, 1, 64)))
+    rec = torch.zeros((10, 39), dtype=torch.uint8)  # not 5 * 64 / 8 = 40 bytes a row
+    with pytest.raises(ValueError, match=r"\[n, 40\]"):
+        kp.pion_vstore_fetch_f32(rec, kp.PION_KV_MLX4G32, 64, 0, 10, torch.zeros((10, 64)))
+    with pytest.raises(ValueError, match="one int32 per q-head"):
+        kp._head_map([0, 1, 2], 2)
+    assert lib.pion_prefix_lookup(b"s", 0) == 0
