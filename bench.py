@@ -54,8 +54,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "218cd7f4191827bc70164805018d999920aadaebe2d7a4b213fed5bf99bc56b1",
-                  "bytes_per_launch": 269472944}
+DECODE_TRAFFIC = {"sources_sha256": "406a3ec9dbedee232f3e23695ae1b34de6312fb3cbb87d0c7b2a3532f5f42df9",
+                  "bytes_per_launch": 268750056}
 
 
 def kernel_sources_sha256():
@@ -240,7 +240,7 @@ def run_decode(args, torch, kp, synth, dev, stream):
                                  if args.mode == "layers"
                                  and kernel_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]
                                  else None),
-                     "kernel": "attn_split_kernel<128,1,4,false,false>",
+                     "kernel": "attn_split_kernel<128,1,4,false,false,8>",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
         "warm": {"value": round(bytes_step / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
                  "avg_launch_us": round(wlaunch_us, 3),

@@ -78,31 +78,31 @@ __device__ __forceinline__ float slots_sum(float v) {
   return v;
 }
 
-template <int D, int R>
+template <int D, int R, int NW>
 struct WaveState {
-  float m[4][R];
-  float l[4][R];
-  alignas(16) float acc[4][R][D];
+  float m[NW][R];
+  float l[NW][R];
+  alignas(16) float acc[NW][R][D];
 };
 
-template <int D, int R>
+template <int D, int R, int NW>
 struct Scratch {
   union {
-    WaveState<D, R> ws;
-    MergeScratch<256> ms;
+    WaveState<D, R, NW> ws;
+    MergeScratch<64 * NW> ms;
   };
   int last;
 };
 
 // Wave-level slot merge, workgroup merge, partial store, ticket, and (last) merge.
-template <int D, int R, int LPR>
-__device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Scratch<D, R> &sm,
+template <int D, int R, int LPR, int NW>
+__device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Scratch<D, R, NW> &sm,
                                        float (&m)[R], float (&l)[R], float (&acc)[R][8],
                                        const uint8_t *heads, int cnt, int qi, int x) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
-  WaveState<D, R> &ws = sm.ws;
+  WaveState<D, R, NW> &ws = sm.ws;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float M = slots_max<LPR>(m[r]);
@@ -122,13 +122,15 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
   __syncthreads();
   const PartRsrc pr = part_rsrc(p, b, qi);
   constexpr int DQ = D / 4;
-  for (int t = threadIdx.x; t < cnt * DQ; t += 256) {
+  for (int t = threadIdx.x; t < cnt * DQ; t += 64 * NW) {
     const int r = t / DQ, dq = t - r * DQ;
-    const float mm = fmaxf(fmaxf(ws.m[0][r], ws.m[1][r]), fmaxf(ws.m[2][r], ws.m[3][r]));
+    float mm = ws.m[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, ws.m[w][r]);
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float lw = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = fast_exp2(ws.m[w][r] - mm);
       a += f * *(const f32x4 *)&ws.acc[w][r][4 * dq];
       lw = __builtin_fmaf(f, ws.l[w][r], lw);
@@ -144,7 +146,7 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
       if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, 256>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
 }
 
 // One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.
@@ -167,11 +169,11 @@ struct QRegs<true, R> {
 
 __device__ __forceinline__ float f32_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-template <int D, int R, int U, bool GATHER, bool F32>
-__global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
+template <int D, int R, int U, bool GATHER, bool F32, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void attn_split_kernel(PartialParams p) {
   constexpr int LPR = fp16_row_lanes(D), KPI = 64 / LPR, STEP = KPI * U;
   constexpr int ESZ = F32 ? 4 : 2, NV = F32 ? 2 : 1;  // bytes per value, pieces per 8 values
-  __shared__ Scratch<D, R> sm;
+  __shared__ Scratch<D, R, NW> sm;
   __shared__ int gsp[GATHER ? kGatherChunk : 1];  // the span's token indices
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
       const int h = heads[0];
       sp.j1 = min(sp.j1, max(sp.j0, min(p.gcount[h], p.gmax)));
       __syncthreads();  // the previous segment is done with gsp
-      for (int t = threadIdx.x; t < sp.j1 - sp.j0; t += 256)
+      for (int t = threadIdx.x; t < sp.j1 - sp.j0; t += 64 * NW)
         gsp[t] = p.gidx[(size_t)h * p.gmax + sp.j0 + t];
       __syncthreads();
     }
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
     Tile<U, NV> cur;
     if (base < sp.j1) load(cur, base);
     while (base < sp.j1) {
-      const int next = base + 4 * STEP;
+      const int next = base + NW * STEP;
       Tile<U, NV> nxt;
       if (next < sp.j1) load(nxt, next);
       consume(cur);
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(PartialParams p) {
       base = next;
     }
   }
-  finish<D, R, LPR>(p, b, sm, m, l, acc, heads, cnt, qi, x);
+  finish<D, R, LPR, NW>(p, b, sm, m, l, acc, heads, cnt, qi, x);
 }
 
 // fp32 (slot format 2) tiles hold twice the bytes per key, so half the keys per lane
@@ -353,6 +355,9 @@ hipError_t launch_partial_d(const PartialParams &p, int x_count, hipStream_t s) 
     hipLaunchKernelGGL((attn_split_kernel<D, 1, 4, true, false>), grid, dim3(256), 0, s, p);
   else if (f32)
     hipLaunchKernelGGL((attn_split_kernel<D, R, 2, false, true>), grid, dim3(256), 0, s, p);
+  else if (p.waves == 8 && R <= 2)  // 8-wave workgroups (twice the keys per workgroup)
+    hipLaunchKernelGGL((attn_split_kernel<D, R <= 2 ? R : 1, 4, false, false, 8>), grid, dim3(512),
+                       0, s, p);
   else
     hipLaunchKernelGGL((attn_split_kernel<D, R, 4, false, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -390,6 +395,8 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
                  p.n_prob != 1 || p.fmt == 1))
     return hipErrorInvalidValue;
   if (p.esz != (p.fmt == 2 ? 4 : 2)) return hipErrorInvalidValue;
+  if (p.waves != 4 && !(p.waves == 8 && !p.gidx && p.fmt == 0 && rows_per_group <= 2))
+    return hipErrorInvalidValue;
   switch (p.D) {
     case 32: return launch_partial_r<32>(p, rows_per_group, x_count, s);
     case 64: return launch_partial_r<64>(p, rows_per_group, x_count, s);

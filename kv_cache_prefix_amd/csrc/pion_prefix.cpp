@@ -322,9 +322,9 @@ int pow2_at_least(int n) {
   return R;
 }
 
-int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4) {
+int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4, int waves = 4) {
   if (keys <= 0) return granule;
-  const long long target = split_target(mlx4);
+  const long long target = split_target(mlx4) * 4 / waves;  // the same waves in total
   long long c = (keys * work_rows + target - 1) / target;
   c = std::max<long long>(c, granule);
   c = (c + granule - 1) / granule * granule;
@@ -445,6 +445,23 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.N[z] = slots[z]->N;
     N_max = std::max(N_max, slots[z]->N);
   }
+  // 8-wave workgroups (fp16 prefix, groups of at most 2 rows, dense keys): the same
+  // waves in half as many workgroups. Taken when that leaves every row group one span,
+  // so no split merge runs at all, and there are at least 256 of them to fill the chip
+  // (measured +5% on the 32-layer decode launch; single layers keep 4-wave splits).
+  // PION_SPLIT_WAVES=4 or 8 forces the choice where 8 is allowed.
+  static const int waves_env = [] {
+    const char *e = getenv("PION_SPLIT_WAVES");
+    return e ? atoi(e) : 0;
+  }();
+  {
+    const bool can8 = s0.fmt == PION_KV_FP16 && !c.gidx && !c.blocks && R <= 2;
+    const long long units = (long long)Y * n_prob;
+    bool use8 = can8 && units >= 256 &&
+                pick_chunk(N_max, units, 64, false, 8) >= N_max;  // one span per row group
+    if (waves_env == 4 || waves_env == 8) use8 = can8 && waves_env == 8;
+    p.waves = use8 ? 8 : 4;
+  }
   p.Q = c.Q;
   p.q_stride = c.q_stride;
   p.out = c.out;
@@ -466,7 +483,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.pre_chunk = c.B;
     pre_max = c.n_sel;
   } else {
-    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64, mlx4);
+    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64, mlx4, p.waves);
     pre_max = (N_max + p.pre_chunk - 1) / p.pre_chunk;
   }
   if (c.S_suf > 0) {
