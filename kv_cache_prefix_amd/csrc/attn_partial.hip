@@ -355,8 +355,8 @@ hipError_t launch_partial_d(const PartialParams &p, int x_count, hipStream_t s) 
     hipLaunchKernelGGL((attn_split_kernel<D, 1, 4, true, false>), grid, dim3(256), 0, s, p);
   else if (f32)
     hipLaunchKernelGGL((attn_split_kernel<D, R, 2, false, true>), grid, dim3(256), 0, s, p);
-  else if (p.waves == 8 && R <= 2)  // 8-wave workgroups (twice the keys per workgroup)
-    hipLaunchKernelGGL((attn_split_kernel<D, R <= 2 ? R : 1, 4, false, false, 8>), grid, dim3(512),
+  else if (p.waves == 8 && R <= 4)  // 8-wave workgroups (twice the keys per workgroup)
+    hipLaunchKernelGGL((attn_split_kernel<D, R <= 4 ? R : 1, 4, false, false, 8>), grid, dim3(512),
                        0, s, p);
   else
     hipLaunchKernelGGL((attn_split_kernel<D, R, 4, false, false>), grid, dim3(256), 0, s, p);
@@ -395,7 +395,7 @@ hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_coun
                  p.n_prob != 1 || p.fmt == 1))
     return hipErrorInvalidValue;
   if (p.esz != (p.fmt == 2 ? 4 : 2)) return hipErrorInvalidValue;
-  if (p.waves != 4 && !(p.waves == 8 && !p.gidx && p.fmt == 0 && rows_per_group <= 2))
+  if (p.waves != 4 && !(p.waves == 8 && !p.gidx && p.fmt == 0 && rows_per_group <= 4))
     return hipErrorInvalidValue;
   switch (p.D) {
     case 32: return launch_partial_r<32>(p, rows_per_group, x_count, s);

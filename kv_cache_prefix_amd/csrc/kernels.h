@@ -122,7 +122,7 @@ __host__ __device__ inline KVView make_view(const void *base, int fmt, int H, in
 struct PartialParams {
   int H_q, M, D, H_kv, fmt;
   int esz;                // bytes per element of Q and the suffix: 4 for an fp32 slot, else 2
-  int waves;              // waves per workgroup of the fp16 kernel: 4, or 8 (rows <= 2)
+  int waves;              // waves per workgroup of the fp16 kernel: 4, or 8 (rows <= 4)
   float qscale;           // log2(e) / sqrt(D)
   int n_prob;
   const void *kv_base[kMaxBatch];

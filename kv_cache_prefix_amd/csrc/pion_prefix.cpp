@@ -445,7 +445,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.N[z] = slots[z]->N;
     N_max = std::max(N_max, slots[z]->N);
   }
-  // 8-wave workgroups (fp16 prefix, groups of at most 2 rows, dense keys): the same
+  // 8-wave workgroups (fp16 prefix, groups of at most 4 rows, dense keys): the same
   // waves in half as many workgroups. Taken when that leaves every row group one span,
   // so no split merge runs at all, and there are at least 256 of them to fill the chip
   // (measured +5% on the 32-layer decode launch; single layers keep 4-wave splits).
@@ -455,7 +455,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     return e ? atoi(e) : 0;
   }();
   {
-    const bool can8 = s0.fmt == PION_KV_FP16 && !c.gidx && !c.blocks && R <= 2;
+    const bool can8 = s0.fmt == PION_KV_FP16 && !c.gidx && !c.blocks && R <= 4;
     const long long units = (long long)Y * n_prob;
     bool use8 = can8 && units >= 256 &&
                 pick_chunk(N_max, units, 64, false, 8) >= N_max;  // one span per row group
