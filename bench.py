@@ -54,7 +54,7 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "406a3ec9dbedee232f3e23695ae1b34de6312fb3cbb87d0c7b2a3532f5f42df9",
+DECODE_TRAFFIC = {"sources_sha256": "bb7278c872d2591ec8031c2505613465862335f5e6147502d4388530d3379710",
                   "bytes_per_launch": 268750056}
 
 

@@ -322,6 +322,20 @@ int pow2_at_least(int n) {
   return R;
 }
 
+// Whether a decode over row groups of `grp_rows` q-heads (4 to 8) runs faster on the MFMA
+// kernel than on the vector split kernel, from timings of single-layer and 32-layer
+// launches at N = 2048 to 8192 and D = 64, 128 and 256. Groups of 5 or more rows, which
+// the vector kernel pads to 8: at D = 64 always, else for 64 or more row groups (+25-45%)
+// or prefixes of at most 2048 keys. Groups of 4 rows: at D = 64 unless long prefixes
+// fill the chip (N > 4096 over 64 or more row groups), at D = 128 for prefixes of at
+// most 2048 keys, never at D = 256. The 8-wave split kernel is ahead elsewhere, by up
+// to 30% (4 rows at D = 256, N = 4096).
+bool prefer_gqa(int grp_rows, int D, int N_max, long long units) {
+  if (grp_rows >= 5) return D == 64 || units >= 64 || N_max <= 2048;
+  if (grp_rows == 4) return D == 64 ? !(units >= 64 && N_max > 4096) : D == 128 && N_max <= 2048;
+  return false;
+}
+
 int pick_chunk(long long keys, long long work_rows, int granule, bool mlx4, int waves = 4) {
   if (keys <= 0) return granule;
   const long long target = split_target(mlx4) * 4 / waves;  // the same waves in total
@@ -525,18 +539,18 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.x_begin = 0;
     const long long keys =
         (c.gidx ? (long long)c.gmax : c.blocks ? (long long)c.n_sel * c.B : N_max) + c.S_suf;
-    // row groups of 6 to 8 q-heads at M = 1 and D <= 128 run on the MFMA kernel, whose
-    // key work does not grow with the rows (measured 11-15% faster there; slower for
-    // 4 rows or D = 256). PION_GQA_MFMA forces it for any group of 4 or more rows,
-    // PION_NO_GQA_MFMA turns it off. It addresses a kv-head's K, V and suffix through
-    // 32-bit buffer ranges.
+    // Row groups of 4 to 8 q-heads at M = 1 may run on the MFMA kernel, whose key work
+    // does not grow with the rows; the vector kernel pads a group of 5 to 8 rows to 8.
+    // PION_GQA_MFMA forces it for any group of 4 or more rows, PION_NO_GQA_MFMA turns
+    // it off. It addresses a kv-head's K, V and suffix through 32-bit buffer ranges.
     const long long row_bytes = 2LL * c.D;
     const bool gqa_ok = c.M == 1 && grp_rows >= 4 && !c.gidx && gqa_dim(c.D) &&
                         s0.fmt == PION_KV_FP16 &&
                         N_max * row_bytes < (1LL << 31) &&
                         (long long)c.S_suf * row_bytes < (1LL << 31) &&
                         !getenv_flag("PION_NO_GQA_MFMA");
-    const bool gqa = gqa_ok && ((grp_rows >= 6 && c.D <= 128) || getenv_flag("PION_GQA_MFMA"));
+    const bool gqa = gqa_ok && (getenv_flag("PION_GQA_MFMA") ||
+                                prefer_gqa(grp_rows, c.D, N_max, (long long)Y * n_prob));
     if (gqa) {
       // one span when each wave gets at most PION_GQA_ONE_SPAN (default 2) sub-tiles of
       // 32 keys: a wave keeps one sub-tile in flight ahead, which does not cover the load

@@ -208,6 +208,27 @@ def test_decode_gqa_mfma_agrees_with_valu_path(kp, monkeypatch):
     assert np.max(np.abs(a - b)) <= 2 * OUT_TOL
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("H_q,H_kv", [(16, 4), (20, 4), (24, 4), (32, 4)])
+@pytest.mark.parametrize("force", ["PION_GQA_MFMA", "PION_NO_GQA_MFMA", None])
+def test_decode_layers_gqa_groups(kp, monkeypatch, D, H_q, H_kv, force):
+    # batched layers of 4 to 8 rows per kv-head (padded groups of 5 to 7 included) on
+    # each kernel and on the default choice, with ragged prefix lengths per layer
+    if force:
+        monkeypatch.setenv(force, "1")
+    Ns = [1, 33, 700, 2049, 3000, 64, 129, 1500]
+    inputs = [synth.generate(synth.DECODE, 40 + l, N=N, D=D, H_q=H_q, H_kv=H_kv) for l, N in enumerate(Ns)]
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store("t", 740 + l, dev(inp.K), dev(inp.V))
+    out, lse = empty((len(Ns), H_q, 1, D)), empty((len(Ns), H_q, 1))
+    kp.pion_prefix_query_layers("t", 740, dev(np.stack([i.Q for i in inputs])), out, lse)
+    out, lse = host(out), host(lse)
+    for l, inp in enumerate(inputs):
+        check(out[l], lse[l], *oracle.prefix_query(inp.Q, inp.K, inp.V))
+    for l in range(len(Ns)):
+        kp.pion_prefix_drop("t", 740 + l)
+
+
 def test_restore_replaces_and_unknown_session(kp):
     import kv_cache_prefix_amd as k
     a = synth.generate(synth.DECODE, 1, N=100, H_q=2, H_kv=2)
