@@ -185,8 +185,7 @@ struct PrefillParams {
   int n_iblk;                     // ceil(M / 128)
   int n_splits, split_keys;       // split_keys a multiple of 64
   float *out, *lse;
-  float *part_acc, *part_m, *part_l;
-  int *counters, *done;           // per tile
+  float *part_acc, *part_m, *part_l;  // split partials (n_splits > 1)
   HeadMap hm;
   uint8_t order[kMaxHeads];       // q-heads sorted by kv-head
 };

@@ -385,13 +385,13 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   p.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.D));
   p.n_iblk = (c.M + 127) / 128;
   const long long tiles = (long long)c.H_q * p.n_iblk;
-  if (tiles > kMaxCounters / 2) return PION_ERR_UNSUPPORTED;  // ticket and done counters
+  if (tiles * (c.D / 32) > 0x7fffffffLL) return PION_ERR_UNSUPPORTED;  // merge grid
   const long long total = (long long)sl.N + c.S_suf;
-  // splits: up to about 1.5 workgroups per CU over the row blocks (two fit on a CU for
-  // D <= 128, one above); each split adds a partial round trip and merge work.
-  // env PION_PREFILL_SPLITS overrides
-  const long long slots = c.D <= 128 ? 384 : 256;
-  long long ns = std::max<long long>(1, (slots + tiles / 2) / tiles);
+  // splits: as many as keep every workgroup resident at once (two fit on a CU for
+  // D <= 128, one above: 512 or 256 on 256 CUs), at most 16; a second kernel merges
+  // them. env PION_PREFILL_SPLITS overrides
+  const long long slots = c.D <= 128 ? 512 : 256;
+  long long ns = std::max<long long>(1, slots / tiles);
   if (const char *e = getenv("PION_PREFILL_SPLITS")) ns = std::max(1, atoi(e));
   ns = std::min<long long>(ns, std::min<long long>(16, (total + 63) / 64));
   long long sk = (total + ns - 1) / ns;
@@ -419,8 +419,6 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
     p.part_acc = (float *)ws;
     p.part_m = (float *)((char *)ws + acc_bytes);
     p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
-    p.counters = g_ws[st].counters;
-    p.done = g_ws[st].counters + kMaxCounters / 2;
   }
   return launch_prefill(p, st) == hipSuccess ? PION_OK : PION_ERR_HIP;
 }

@@ -33,9 +33,9 @@
 // would wait for every outstanding one before any LDS read; the loads are issued
 // through inline assembly instead and the kernel waits for them itself (s_waitcnt
 // vmcnt, then a barrier) before a stage is read.
-// Splits of the key range run in different workgroups; the one that draws the last
-// ticket of a row block merges the others' (acc, m, l) partials into its own with the
-// LSE rule.
+// Splits of the key range run in different workgroups, which store their (acc, m, l)
+// partials; a second kernel merges them with the LSE rule (no workgroup waits on
+// another).
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -54,6 +54,14 @@ constexpr float kNegBig = -1.0e30f;
 constexpr int BQ = 128;   // query rows per workgroup
 constexpr int BK = 64;    // keys per tile
 constexpr int kMaxPrefillSplits = 16;
+constexpr int kMergeChunk = 8;  // splits whose partials the merge loads per round
+
+// Byte offset of the 16-byte piece (split c, wave w, 32-dim block db, quad i, lane) in a
+// row block's partials
+template <int NDB>
+__device__ __forceinline__ uint32_t part_off(int c, int w, int db, int i, int lane) {
+  return (uint32_t)(((((c * 4 + w) * NDB + db) * 4 + i) * 64 + lane) * 16);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -71,15 +79,7 @@ constexpr int lds_dims() {
 template <int D>
 struct PrefillSmem {
   static constexpr int TB = BK * 2 * lds_dims<D>();  // bytes of one K or V tile
-  union {
-    alignas(16) char kv[NSTAGE][2][TB];  // [stage][0: K, 1: V]
-    struct {                             // split merge: per (row, split) m then weight, and l
-      float w[BQ * 16];
-      float l[BQ * 16];
-      float inv[BQ];
-    } mg;
-  };
-  int last;
+  alignas(16) char kv[NSTAGE][2][TB];  // [stage][0: K, 1: V]
 };
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return zero, which
@@ -249,6 +249,16 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     // ... and every wave's; every wave is also done reading the stage loaded next
     __syncthreads();
     if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
+    // Two workgroups on a CU share its SIMDs; the arbiter favours the older waves, so one
+    // would run ahead and the other finish alone at the end. Priority falls with the tiles
+    // left, so the one behind catches up and both end together.
+    {
+      const int rem = n_tiles - j;
+      if (rem > 8) __builtin_amdgcn_s_setprio(3);
+      else if (rem > 4) __builtin_amdgcn_s_setprio(2);
+      else if (rem > 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     constexpr int KB = STG * 2 * TB, VB = KB + TB;  // stage offsets of K and V
 
     // two 32-key sub-tiles: S^T, softmax, PV
@@ -339,163 +349,94 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
 
   // Split partial: acc unnormalized against m_run, in the register layout of o (tile,
   // split, wave, 32-dim block db, quad i, lane: one 16-byte piece per lane, so every
-  // store and load instruction moves 1 KB of consecutive bytes); m and l (log2 units)
-  // per [row][split]. Written and read with agent-coherent (sc1) accesses.
-  //
-  // Order: every workgroup of the tile first takes a ticket; the one that draws the
-  // last ticket merges, all others store their partial and then count it in done[tile].
-  // The merging workgroup keeps its own partial in registers and waits (bounded) until
-  // the other n_splits - 1 are counted; those workgroups are already past their loops,
-  // so the wait only covers their stores.
+  // store instruction moves 1 KB of consecutive bytes); m and l (log2 units) per
+  // [row][split]. prefill_merge_kernel, next on the stream, combines the splits.
   const int S = p.n_splits;
   const int rows_valid = min(BQ, p.M - i0);
   const size_t row0 = (size_t)h * p.M + i0;
   const __amdgpu_buffer_rsrc_t rA =
       make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
-  // byte offset of (split c, 32-dim block db, quad i) for this lane
-  auto aoff = [&](int c, int db, int i) { return ((((c * 4 + wave) * NDB + db) * 4 + i) * 64 + lane) * 16; };
   const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
-  constexpr int SC1 = 16;  // cache policy: device coherent
   const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
-  // (for D > 128 the registers cannot hold o through the merge: the merging workgroup
-  // stores its partial too and merges all splits from memory)
-  constexpr bool REG = D <= 128;
-  __syncthreads();
-  if (tid == 0)
-    sm.last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == S - 1;
-  __syncthreads();
-  const bool last = sm.last;
-  if (!last || !REG) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
-                                               aoff(split, db, i), 0, SC1);
-      }
-    if (hl == 0) {
-      const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM,
-                                            (r * S + split) * 4, 0, SC1);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL,
-                                            (r * S + split) * 4, 0, SC1);
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
+                                             part_off<NDB>(split, wave, db, i, lane), 0, 0);
     }
-    // this wave's stores have completed before the barrier and the count
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (!last) {
-      if (tid == 0)
-        __hip_atomic_fetch_add(p.done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
+  if (hl == 0) {
+    const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM, (r * S + split) * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL, (r * S + split) * 4, 0, 0);
   }
-  if (tid == 0) {
-    // bounded: ends after about a second even if a count never arrives
-    for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (__hip_atomic_load(p.done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S - 1)
-        break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
+}
 
-  // Merge. (1) m and l of every (row, split) into LDS, this split's from registers;
-  // (2) per row the weights 2^(m_c - m*), 1 / sum_c w_c l_c and lse; (3) in the MFMA
-  // layout of o: out = (w_self o + sum over the other splits of w_c acc_c) / L.
-  constexpr int OWN_REG = REG ? 1 : 0;  // this split's m, l and acc come from registers
-  if (REG && hl == 0 && r < rows_valid) {
-    sm.mg.w[r * S + split] = l_run > 0.f ? m_run : -INFINITY;
-    sm.mg.l[r * S + split] = l_run;
+// Combine the split partials of prefill_kernel. One workgroup per (row block, 32-dim
+// block db): thread (wave w, lane l) takes the place of the split kernel's lane, row
+// 32 w + l % 32 and dims 32 db + 8 i + 4 (l / 32) + 0..3, and reads that piece of every
+// split (up to kMergeChunk splits per round of loads) with the row's m and l, then
+// applies the LSE rule: out = sum_c 2^(m_c - m*) acc_c / sum_c 2^(m_c - m*) l_c.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+  constexpr int NDB = D / 32, CH = kMergeChunk;
+  const int S = p.n_splits;
+  const int tile = blockIdx.x / NDB, db = blockIdx.x - tile * NDB;
+  const int h = tile / p.n_iblk, ib = tile - h * p.n_iblk;
+  const int i0 = ib * BQ, rows_valid = min(BQ, p.M - i0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int r = wave * 32 + (lane & 31);
+  const int rr = min(r, rows_valid - 1);  // rows past the end repeat the last row, unstored
+  const size_t row0 = (size_t)h * p.M + i0;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
+  float mv[kMaxPrefillSplits], lv[kMaxPrefillSplits];
+#pragma unroll
+  for (int c = 0; c < kMaxPrefillSplits; ++c) {
+    mv[c] = c < S ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, (rr * S + c) * 4, 0, 0))
+                  : -INFINITY;
+    lv[c] = c < S ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (rr * S + c) * 4, 0, 0))
+                  : 0.f;
   }
-  for (int x0 = 0; x0 < rows_valid * S; x0 += (D <= 128 ? 4 : 1) * 256) {
-    constexpr int ML = D <= 128 ? 4 : 1;
-    float mv[ML], lv[ML];
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float M = -INFINITY, L = 0.f;
+  for (int c0 = 0; c0 < S; c0 += CH) {
+    f32x4 v[CH][4];
 #pragma unroll
-    for (int k = 0; k < ML; ++k) {
-      const int x = x0 + tid + 256 * k;
-      const bool in = x < rows_valid * S && !(OWN_REG && x % S == split);
-      mv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, x * 4, 0, SC1)) : 0.f;
-      lv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, x * 4, 0, SC1)) : 0.f;
-    }
+    for (int cc = 0; cc < CH; ++cc)
 #pragma unroll
-    for (int k = 0; k < ML; ++k) {
-      const int x = x0 + tid + 256 * k;
-      if (x < rows_valid * S && !(OWN_REG && x % S == split)) {
-        sm.mg.w[x] = mv[k];
-        sm.mg.l[x] = lv[k];
+      for (int i = 0; i < 4; ++i)
+        v[cc][i] = c0 + cc < S ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                     rA, part_off<NDB>(c0 + cc, wave, db, i, lane), 0, 0))
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c0 == 0) {
+#pragma unroll
+      for (int c = 0; c < kMaxPrefillSplits; ++c) M = fmaxf(M, mv[c]);
+#pragma unroll
+      for (int c = 0; c < kMaxPrefillSplits; ++c) {
+        mv[c] = fast_exp2(mv[c] - M);  // the split's weight; -inf (empty or absent) -> 0
+        L = __builtin_fmaf(mv[c], lv[c], L);
       }
     }
-  }
-  __syncthreads();
-  if (tid < rows_valid) {
-    float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, sm.mg.w[tid * S + c]);
-    float L = 0.f;
-    for (int c = 0; c < S; ++c) {
-      const float w = fast_exp2(sm.mg.w[tid * S + c] - M);  // -inf -> 0
-      sm.mg.w[tid * S + c] = w;
-      L = __builtin_fmaf(w, sm.mg.l[tid * S + c], L);
-    }
-    sm.mg.inv[tid] = 1.f / L;
-    if (p.lse) p.lse[row0 + tid] = (M + __log2f(L)) * 0.69314718055994530942f;
-  }
-  __syncthreads();
-  const int rr = r < rows_valid ? r : 0;  // rows past the end read row 0's weights
-  {
-    const float ws = REG ? sm.mg.w[rr * S + split] : 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int cc = 0; cc < CH; ++cc) {
+      float w = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] = REG ? o[db][e] * ws : 0.f;
-  }
-  // one round: DBC 32-dim blocks of CB splits (register budget)
-  constexpr int CB = D <= 64 ? 2 : 1, DBC = D <= 128 ? NDB : NDB % 2 ? 1 : 2;
-  for (int c0 = 0; c0 < S; c0 += CB) {
+      for (int c = 0; c < kMaxPrefillSplits; ++c) w = c == c0 + cc ? mv[c] : w;
 #pragma unroll
-    for (int d0 = 0; d0 < NDB; d0 += DBC) {
-      f32x4 v[CB][DBC][4];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = c0 + cb;
-        const bool skip = (REG && c == split) || c >= S;  // nothing to add
-#pragma unroll
-        for (int db = 0; db < DBC; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v[cb][db][i] = skip ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                      rA, aoff(c, d0 + db, i), 0, SC1));
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = c0 + cb;
-        const float w = ((REG && c == split) || c >= S) ? 0.f : sm.mg.w[rr * S + c];
-#pragma unroll
-        for (int db = 0; db < DBC; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              o[d0 + db][4 * i + jj] = __builtin_fmaf(w, v[cb][db][i][jj], o[d0 + db][4 * i + jj]);
-      }
+      for (int i = 0; i < 4; ++i) acc[i] += w * v[cc][i];
     }
   }
   if (r < rows_valid) {
-    const float inv = sm.mg.inv[r];
+    const float inv = 1.f / L;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(float4 *)(p.out + (row0 + r) * D + 32 * db + 8 * i + 4 * hl) =
-            make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
-                        o[db][4 * i + 3] * inv);
-  }
-  if (tid == 0) {
-    __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p.done + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 4; ++i)
+      *(f32x4 *)(p.out + (row0 + r) * D + 32 * db + 8 * i + 4 * hl) = acc[i] * inv;
+    if (db == 0 && hl == 0 && p.lse) p.lse[row0 + r] = (M + __log2f(L)) * 0.69314718055994530942f;
   }
 }
 
@@ -503,18 +444,25 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s) {
   if (p.n_splits < 1 || p.n_splits > kMaxPrefillSplits || p.split_keys % BK) return hipErrorInvalidValue;
-  const int W = p.H_q * p.n_iblk * p.n_splits;
-  dim3 grid(8 * ((W + 7) / 8));
+  const int tiles = p.H_q * p.n_iblk, W = tiles * p.n_splits;
+  const dim3 grid(8 * ((W + 7) / 8)), mgrid(tiles * (p.D / 32));
+  const bool merge = p.n_splits > 1;
+#define PION_PREFILL_D(DD)                                                              \
+  case DD:                                                                              \
+    hipLaunchKernelGGL(prefill_kernel<DD>, grid, dim3(256), 0, s, p);                   \
+    if (merge) hipLaunchKernelGGL(prefill_merge_kernel<DD>, mgrid, dim3(256), 0, s, p); \
+    break;
   switch (p.D) {
-    case 32: hipLaunchKernelGGL(prefill_kernel<32>, grid, dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(prefill_kernel<96>, grid, dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, p); break;
-    case 160: hipLaunchKernelGGL(prefill_kernel<160>, grid, dim3(256), 0, s, p); break;
-    case 192: hipLaunchKernelGGL(prefill_kernel<192>, grid, dim3(256), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(prefill_kernel<256>, grid, dim3(256), 0, s, p); break;
+    PION_PREFILL_D(32)
+    PION_PREFILL_D(64)
+    PION_PREFILL_D(96)
+    PION_PREFILL_D(128)
+    PION_PREFILL_D(160)
+    PION_PREFILL_D(192)
+    PION_PREFILL_D(256)
     default: return hipErrorInvalidValue;
   }
+#undef PION_PREFILL_D
   return hipGetLastError();
 }
 
