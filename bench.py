@@ -297,6 +297,7 @@ def run_prefill(args, torch, kp, synth, dev, stream):
                                "M=S_suf=512 causal suffix", "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": flops / (launch_us * 1e-6) / 1e12,
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None,
+                     "kernel": "prefill_kernel<128> then prefill_merge_kernel<128> (one call)",
                      "avg_launch_us": launch_us},
         "cpu_baseline": cpu,
     }
