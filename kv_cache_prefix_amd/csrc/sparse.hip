@@ -3,7 +3,8 @@
 // K_top blocks; ATTEND.* page, QUERY_SPARSE_AUTO rows: K_mean cached per slot).
 //
 //   block_mean : K_mean[g, b, d] = (sum of K[g, j, d] over the tokens j of block b) / n_b,
-//                summed in token order in fp32; one thread per (g, b, d), coalesced over d.
+//                summed in fp32; threads read 16-byte chunks of the key rows (coalesced
+//                rows), partial sums of row slots added through LDS.
 //   block_select: score[g, b] = sum over q-heads h with head_map[h] == g of q_h . K_mean[g, b],
 //                computed as (sum of those q_h) . K_mean[g, b] (equal in exact arithmetic),
 //                then per kv-head the min(K_top, nb) best blocks by (score desc, index asc),
@@ -20,30 +21,58 @@ __device__ __forceinline__ float h2f(uint16_t u) {
   return (float)__builtin_bit_cast(_Float16, u);
 }
 
+// Block means, workgroup (block b, kv-head g): thread t owns 16-byte chunk c = t % TPR of
+// the key rows (E dims: 8 fp16, 4 fp32, or one 32-dim mlx4g32 group, dequantized as
+// s * code + b) and rows j0 + t / TPR + k RP of the block (RP = 256 / TPR row slots);
+// threads past the row's chunks idle. Each thread sums its rows in fp32 in row order, the
+// row slots' sums are added in slot order through LDS, and the total is divided by the
+// block's row count. The order depends only on the block's own rows.
 template <int FMT>
-__global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int nb,
+__global__ __launch_bounds__(256) void block_mean_kernel(KVView kv, int B, int nb, int tpr,
                                                          float *__restrict__ kmean) {
-  const int b = blockIdx.x, g = blockIdx.y;
-  const int D = kv.D;
+  constexpr int E = FMT == 0 ? 8 : FMT == 2 ? 4 : 32;  // dims per chunk
+  __shared__ float part[256 * E];
+  const int b = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int D = kv.D, CH = D / E, RP = 256 / tpr;
   const int j0 = b * B, j1 = min(j0 + B, kv.N);
-  const float n = (float)(j1 - j0);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float sum = 0.f;
-    for (int j = j0; j < j1; ++j) {
-      const size_t tok = (size_t)g * kv.N + j;
-      float x;
-      if (FMT == 0) {
-        x = h2f(((const uint16_t *)kv.K)[tok * D + d]);
-      } else if (FMT == 2) {
-        x = ((const float *)kv.K)[tok * D + d];
+  const int c = t % tpr;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (c < CH) {
+    const size_t row0 = (size_t)g * kv.N;
+#pragma unroll 4
+    for (int j = j0 + t / tpr; j < j1; j += RP) {
+      if constexpr (FMT == 0) {
+        const uint4 w = *((const uint4 *)((const uint16_t *)kv.K + (row0 + j) * D) + c);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += h2f((uint16_t)(u[e / 2] >> (16 * (e % 2))));
+      } else if constexpr (FMT == 2) {
+        const float4 w = *((const float4 *)((const float *)kv.K + (row0 + j) * D) + c);
+        acc[0] += w.x;
+        acc[1] += w.y;
+        acc[2] += w.z;
+        acc[3] += w.w;
       } else {
-        const uint32_t w = kv.Kc[tok * (D / 8) + d / 8];
-        const float c = (float)((w >> (4 * (d % 8))) & 0xFu);
-        const uint32_t sb = kv.Ksb[tok * (D / 32) + d / 32];
-        x = __builtin_fmaf(h2f((uint16_t)(sb & 0xffffu)), c, h2f((uint16_t)(sb >> 16)));
+        const uint4 w = *((const uint4 *)(kv.Kc + (row0 + j) * (D / 8)) + c);
+        const uint32_t sb = kv.Ksb[(row0 + j) * (D / 32) + c];
+        const float sc = h2f((uint16_t)(sb & 0xffffu)), bi = h2f((uint16_t)(sb >> 16));
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          acc[e] += __builtin_fmaf(sc, (float)((u[e / 8] >> (4 * (e % 8))) & 0xFu), bi);
       }
-      sum += x;
     }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) part[t * E + e] = acc[e];
+  __syncthreads();
+  const float n = (float)(j1 - j0);
+  for (int d = t; d < D; d += 256) {
+    const int cd = d / E, e = d - cd * E;
+    float sum = 0.f;
+    for (int r = 0; r < RP; ++r) sum += part[(r * tpr + cd) * E + e];
     kmean[((size_t)g * nb + b) * D + d] = __fdiv_rn(sum, n);
   }
 }
@@ -351,14 +380,19 @@ __global__ __launch_bounds__(256) void block_select_kernel(const void *__restric
 
 hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t s) {
   const int nb = (kv.N + B - 1) / B;
-  dim3 grid(nb, kv.H);
-  const int threads = kv.D < 256 ? kv.D : 256;
+  const dim3 grid(nb, kv.H);
+  // 16-byte chunks per key row, each handled by one thread of a power-of-two row group
+  const int E = kv.fmt == 0 ? 8 : kv.fmt == 2 ? 4 : 32;
+  if (B < 1 || kv.D % E) return hipErrorInvalidValue;
+  int tpr = 1;
+  while (tpr < kv.D / E) tpr <<= 1;
+  if (tpr > 256) return hipErrorInvalidValue;
   if (kv.fmt == 0)
-    hipLaunchKernelGGL(block_mean_kernel<0>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
+    hipLaunchKernelGGL(block_mean_kernel<0>, grid, dim3(256), 0, s, kv, B, nb, tpr, kmean);
   else if (kv.fmt == 2)
-    hipLaunchKernelGGL(block_mean_kernel<2>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
+    hipLaunchKernelGGL(block_mean_kernel<2>, grid, dim3(256), 0, s, kv, B, nb, tpr, kmean);
   else
-    hipLaunchKernelGGL(block_mean_kernel<1>, grid, dim3(threads), 0, s, kv, B, nb, kmean);
+    hipLaunchKernelGGL(block_mean_kernel<1>, grid, dim3(256), 0, s, kv, B, nb, tpr, kmean);
   return hipGetLastError();
 }
 
