@@ -315,7 +315,6 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
     K16, V16 = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
     for k in range(NSET * LAYERS):   # the same quantized prefix in every layer slot
         kp.pion_prefix_store(sid, k, K16, V16, kp.PION_KV_MLX4G32)
-    del K16, V16
     Q1 = torch.from_numpy(inp.Q).to(dev)
     Q = Q1.unsqueeze(0).expand(LAYERS, -1, -1, -1).contiguous()
     out = torch.empty((LAYERS, case.H_q, 1, case.D), dtype=torch.float32, device=dev)
@@ -347,6 +346,49 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
         return step
     one_ms, one_us = Timed(torch, stream, [make_one(k) for k in range(NSET * LAYERS)], 1,
                            False).measure(args.steps, args.warmup)
+
+    # the store-side encoder over this shape's K and V (two launches per step)
+    rows = case.H_kv * case.N
+    codes = torch.empty((rows, case.D // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((rows, case.D // 32), dtype=torch.float16, device=dev)
+    biases = torch.empty((rows, case.D // 32), dtype=torch.float16, device=dev)
+    xk, xv = K16.reshape(rows, case.D), V16.reshape(rows, case.D)
+
+    def quant():
+        for x in (xk, xv):
+            rc = lib.pion_kv_quantize_mlx4g32(x.data_ptr(), rows, case.D, codes.data_ptr(),
+                                              scales.data_ptr(), biases.data_ptr(),
+                                              torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_kv_quantize_mlx4g32")
+    q_ms, _ = Timed(torch, stream, quant, 2, False).measure(args.steps // 4 + 1, args.warmup)
+    q_read, q_written = 2 * rows * case.D * 2, 2 * rows * (case.D // 2 + case.D // 32 * 4)
+    del codes, scales, biases
+
+    # the same shape resident in fp16 (16 layers per launch, two sets alternating)
+    sid16 = "bench-mlx4-fp16"
+    for k in range(NSET * LAYERS):
+        kp.pion_prefix_store(sid16, k, K16, V16)
+    del K16, V16, xk, xv
+    sid16b = sid16.encode()
+    out16, lse16 = torch.empty_like(out), torch.empty_like(lse)   # out keeps the mlx4g32 result
+
+    def make_step16(k):
+        a = (sid16b, LAYERS * k, LAYERS, case.H_q, case.D, 1, Q.data_ptr(), None,
+             out16.data_ptr(), lse16.data_ptr())
+
+        def step():
+            rc = lib.pion_prefix_query_layers(*a, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise kp.PionError(rc, "pion_prefix_query_layers")
+        return step
+    (ms16, _), _ = warm_cold(torch, stream, [make_step16(k) for k in range(NSET)], 1, False,
+                             args)
+    ref16, _ = oracle.prefix_query(inp.Q, inp.K, inp.V)
+    check_close(out16[LAYERS - 1].cpu().numpy(), ref16, 2e-3, "out")
+    kp.pion_prefix_drop(sid16, -1)
+    del out16, lse16
+    nbytes16 = LAYERS * case.H_kv * case.N * case.D * 4
 
     Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
     Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
@@ -383,6 +425,15 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
         "warm": {"value": round(nbytes / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
                  "avg_launch_us": round(wlaunch_us, 3),
                  "note": "one set every step (memory-side cache warm)"},
+        "quantize": {"GB/s": round((q_read + q_written) / (q_ms * 1e-3) / 1e9, 1),
+                     "us_per_step": round(q_ms * 1e3, 3),
+                     "note": f"pion_kv_quantize_mlx4g32 of this shape's K and V ({q_read} B read, "
+                             f"{q_written} B written per step, two launches)"},
+        "fp16_resident": {"GB/s": round(nbytes16 / (ms16 * 1e-3) / 1e9, 1),
+                          "us_per_layer": round(ms16 * 1e3 / LAYERS, 3),
+                          "mlx4g32_us_per_layer": round(ms * 1e3 / LAYERS, 3),
+                          "note": "the same shape and launch with fp16 K/V "
+                                  f"({nbytes16} B per {LAYERS}-layer launch, cold)"},
         "single_query": {"us_per_query": round(one_ms * 1e3, 3),
                          "GB/s": round(nbytes_layer / (one_ms * 1e-3) / 1e9, 3),
                          "note": "one M=1 pion_prefix_query per launch over one 41.9 MB "
@@ -673,7 +724,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    for extra in ("warm", "single_query", "warm_call"):
+    for extra in ("warm", "single_query", "warm_call", "quantize", "fp16_resident"):
         if extra in r:
             line[extra] = r[extra]
     print(json.dumps(line), flush=True)
