@@ -9,9 +9,11 @@
 //
 // Layout: one lane per uint32 code word (8 elements, 16 input bytes), so four
 // consecutive lanes hold one group; min/max combine across those four lanes. Loads are
-// 16 B per lane and stores 4 B per lane, contiguous across the wave. Division is the
-// correctly rounded fp32 divide and there is no contraction, so the codes are bit-exact
-// with any IEEE fp32 evaluation of the steps above.
+// 16 B per lane and stores 4 B per lane, contiguous across the wave. The scale uses the
+// correctly rounded fp32 divide; the codes round the correctly rounded quotient (a
+// product with the reciprocal where that provably rounds the same, else the divide), and
+// there is no contraction, so the codes are bit-exact with any IEEE fp32 evaluation of
+// the steps above.
 #include "kernels.h"
 
 #include <hip/hip_fp16.h>
@@ -19,17 +21,20 @@
 namespace pion {
 namespace {
 
-__global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *__restrict__ x,
-                                                               int64_t nwords,
-                                                               uint32_t *__restrict__ codes,
-                                                               uint16_t *__restrict__ scales,
-                                                               uint16_t *__restrict__ biases,
-                                                               int sb_stride) {
+// v from the lane given by a quad_perm DPP control (all rows and banks)
+template <int CTRL>
+__device__ __forceinline__ float quad_xor(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Encode code word t (elements 8t .. 8t+7) from its 16 loaded bytes; the four words of
+// a group are in one lane quad.
+__device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
+                                            uint32_t *__restrict__ codes,
+                                            uint16_t *__restrict__ scales,
+                                            uint16_t *__restrict__ biases, int sb_stride) {
 #pragma clang fp contract(off)
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < nwords;
-  uint4 raw = make_uint4(0, 0, 0, 0);
-  if (valid) raw = *(const uint4 *)(x + t * 8);
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   float v[8];
 #pragma unroll
@@ -43,11 +48,11 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
     mn = fminf(mn, v[e]);
     mx = fmaxf(mx, v[e]);
   }
-  // the four lanes of a group are lanes 4k..4k+3 of the same wave
-  mn = fminf(mn, __shfl_xor(mn, 1));
-  mn = fminf(mn, __shfl_xor(mn, 2));
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  // the four lanes of a group are a lane quad (4k..4k+3): quad_perm moves
+  mn = fminf(mn, quad_xor<0xB1>(mn));  // lane ^ 1
+  mn = fminf(mn, quad_xor<0x4E>(mn));  // lane ^ 2
+  mx = fmaxf(mx, quad_xor<0xB1>(mx));
+  mx = fmaxf(mx, quad_xor<0x4E>(mx));
 
   const float range = mx - mn;
   const float s32 = __fdiv_rn(range, 15.0f);
@@ -57,11 +62,31 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
   const float b = __half2float(b16);
   uint32_t word = 0;
   if (s != 0.0f) {
+    // rint of the correctly rounded quotient diff / s, without a divide per element:
+    // with r = fl(1 / s), fl(diff * r) is within 3 * 2^-24 * |diff / s| of fl(diff / s)
+    // (three roundings of relative size <= 2^-24), so the two round to the same integer
+    // unless a half-integer lies that close; such elements (and non-finite ones) take the
+    // correctly rounded divide.
+    const float r = __fdiv_rn(1.0f, s);
+    float diff[8], tq[8];
+    bool near = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float diff = v[e] - b;
-      const float tq = __fdiv_rn(diff, s);
-      const float q = fminf(fmaxf(rintf(tq), 0.0f), 15.0f);
+      diff[e] = v[e] - b;
+      tq[e] = diff[e] * r;
+      const float gap = fabsf(tq[e] - (floorf(tq[e]) + 0.5f));  // to the nearest half-integer
+      near |= !(gap > fabsf(tq[e]) * 0x1p-20f);                 // NaN counts as near
+    }
+    // rare: a wave-uniform branch, so the divides run only for waves that need them
+    if (__builtin_amdgcn_ballot_w64(near)) {
+      if (near) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tq[e] = __fdiv_rn(diff[e], s);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = fminf(fmaxf(rintf(tq[e]), 0.0f), 15.0f);
       word |= (uint32_t)q << (4 * e);
     }
   }
@@ -72,6 +97,19 @@ __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *_
       biases[(t >> 2) * sb_stride] = __builtin_bit_cast(uint16_t, b16);
     }
   }
+}
+
+// One code word per lane: lane t of the grid encodes word t.
+__global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *__restrict__ x,
+                                                               int64_t nwords,
+                                                               uint32_t *__restrict__ codes,
+                                                               uint16_t *__restrict__ scales,
+                                                               uint16_t *__restrict__ biases,
+                                                               int sb_stride) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < nwords;
+  const uint4 raw = valid ? *(const uint4 *)(x + t * 8) : make_uint4(0, 0, 0, 0);
+  encode_word(raw, t, valid, codes, scales, biases, sb_stride);
 }
 
 }  // namespace

@@ -132,6 +132,27 @@ def test_quantize_ragged_shapes(kp, rows, D):
     _assert_same_encoding(_quantize_gpu(kp, x), oracle.quantize(x))
 
 
+def test_quantize_half_integer_quotients(kp):
+    # Groups whose elements sit on, and one fp16 step either side of, (k + 0.5) * s for
+    # random fp16 scales s: the quotients (x - b) / s land on or next to the rint ties,
+    # where rounding the quotient any other way than the correctly rounded fp32 divide
+    # would change a code.
+    rng = np.random.default_rng(11)
+    rows, D = 512, 256
+    x = np.zeros((rows * D // 32, 32), np.float32)
+    s = (2.0 ** rng.integers(-12, 6, len(x))) * rng.choice([1.0, 1.5, 1.25, 1.75, 1.375, 3.0 / 7], len(x))
+    k = rng.integers(0, 15, (len(x), 30)) + 0.5
+    x[:, 0] = 0.0
+    x[:, 1] = 15.0 * s
+    x[:, 2:] = k * s[:, None]
+    x16 = x.astype(np.float16)
+    step = rng.integers(-1, 2, x16[:, 2:].shape)          # one fp16 step down, none, up
+    x16[:, 2:] = np.where(step < 0, np.nextafter(x16[:, 2:], np.float16(-np.inf)),
+                          np.where(step > 0, np.nextafter(x16[:, 2:], np.float16(np.inf)), x16[:, 2:]))
+    x16 = np.ascontiguousarray(x16.reshape(rows, D))
+    _assert_same_encoding(_quantize_gpu(kp, x16), oracle.quantize(x16))
+
+
 def test_quantize_full_mlx4g32_decode_shape(kp):
     inp = synth.generate(synth.MLX4_DECODE)
     for x in (inp.K, inp.V):
