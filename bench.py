@@ -17,8 +17,9 @@ above): --config 1 tiny dense query; --config 3 fused batched-Q prefill (TFLOP/s
 plus the single-query latency); --config 5 sparse-auto
 fused query (us/query); --config 6 QUERY_SPARSE over caller-supplied indices (us/query,
 GB/s of gathered rows); --config 7 V-store fetch of whole layers from mlx4g32 records to
-fp32 (GB/s read + written), with the whole-call time of a WARM rehydrate beside it
-(configs 6 and 7 are not headline workloads).
+fp32 (GB/s read + written), with the whole-call time of a WARM rehydrate beside it;
+--config 8 the decode step at every supported head dim and with fp32-resident slots
+(configs 6, 7 and 8 are not headline workloads).
 
 Timing: wall clock over K steps between device synchronizations; a HIP event pair on
 the launch stream brackets the same timed region, and its elapsed time over the number
@@ -74,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kmean-builds", type=int, default=0,
@@ -588,6 +589,70 @@ def run_query_sparse(args, torch, kp, synth, dev, stream):
     }
 
 
+def run_sweep(args, torch, kp, synth, dev, stream):
+    """The decode step (H_q = H_kv = 8, N = 2048, 32 layers per launch, cold over two sets)
+    at every supported head dim with fp16 slots, and with fp32-resident slots at D = 64,
+    128 and 256. One seeded layer per case is stored in all 64 slots."""
+    import numpy as np
+    import oracle
+    LAYERS, NSET, H, N = 32, 2, 8, 2048
+    cases = [(D, kp.PION_KV_FP16) for D in (32, 64, 96, 128, 160, 192, 256, 512)]
+    cases += [(D, kp.PION_KV_FP32) for D in (64, 128, 256)]
+    lib = kp.lib()
+    rows, head = [], None
+    for D, fmt in cases:
+        f32 = fmt == kp.PION_KV_FP32
+        inp = synth.generate(synth.DECODE, 0, D=D, dtype="float32" if f32 else "float16")
+        sid = f"bench-sweep-{D}-{fmt}"
+        K, V = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
+        for k in range(NSET * LAYERS):
+            kp.pion_prefix_store(sid, k, K, V, fmt)
+        del K, V
+        Q = torch.from_numpy(np.stack([inp.Q] * LAYERS)).to(dev)
+        out = torch.empty((LAYERS, H, 1, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((LAYERS, H, 1), dtype=torch.float32, device=dev)
+        sidb = sid.encode()
+
+        def make_step(k):
+            a = (sidb, LAYERS * k, LAYERS, H, D, 1, Q.data_ptr(), None, out.data_ptr(),
+                 lse.data_ptr())
+
+            def step():
+                rc = lib.pion_prefix_query_layers(*a, torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise kp.PionError(rc, "pion_prefix_query_layers")
+            return step
+        ms, launch_us = Timed(torch, stream, [make_step(k) for k in range(NSET)], 1,
+                              False).measure(args.steps, args.warmup)
+        ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+        check_close(out[LAYERS - 1].cpu().numpy(), ref, 1e-4 if f32 else 2e-3, "out")
+        check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 2e-5 if f32 else 1e-4, "lse")
+        kp.pion_prefix_drop(sid, -1)
+        nbytes = LAYERS * H * N * D * 2 * (4 if f32 else 2)
+        row = {"D": D, "resident": "fp32" if f32 else "fp16", "bytes_per_launch": nbytes,
+               "avg_launch_us": round(launch_us, 3),
+               "GB/s": round(nbytes / (launch_us * 1e-6) / 1e9, 1),
+               "frac": round(nbytes / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        rows.append(row)
+        if D == 128 and not f32:
+            head = (ms, launch_us, nbytes)
+    ms, launch_us, nbytes = head
+    return {
+        "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
+        "dtype": "fp16 or fp32 K/V, fp32 accumulate",
+        "config": {"workload": "M=1 decode H_q=H_kv=8 N=2048, 32 layers per launch, at every "
+                               "supported head dim (fp16) and D=64/128/256 fp32-resident; value: "
+                               "the D=128 fp16 case",
+                   "entry": "pion_prefix_query_layers", "launches_per_step": 1,
+                   "memory_side_cache": f"cold: steps alternate over {NSET} sets of {LAYERS} slots"},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "bytes_per_launch": nbytes, "avg_launch_us": launch_us},
+        "sweep": rows,
+        "cpu_baseline": None,
+    }
+
+
 def run_vstore(args, torch, kp, synth, dev, stream):
     """V-store side of the decode shape: 32 layers, K and V, H = 8, N = 2048, D = 128
     (kv = 1024, the 640 B/token mlx4g32 record). A step fetches every layer-side's whole
@@ -699,7 +764,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse,
-              6: run_query_sparse, 7: run_vstore}[args.config]
+              6: run_query_sparse, 7: run_vstore, 8: run_sweep}[args.config]
     r = runner(args, torch, kp, synth, dev, stream)
     roof = r["roofline"]
     if roof is not None:
@@ -724,7 +789,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    for extra in ("warm", "single_query", "warm_call", "quantize", "fp16_resident"):
+    for extra in ("warm", "single_query", "warm_call", "quantize", "fp16_resident", "sweep"):
         if extra in r:
             line[extra] = r[extra]
     print(json.dumps(line), flush=True)
