@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
 # taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
 # reports null.
-DECODE_TRAFFIC = {"sources_sha256": "bb7278c872d2591ec8031c2505613465862335f5e6147502d4388530d3379710",
+DECODE_TRAFFIC = {"sources_sha256": "2984738fdfb1f2ddb279d617edc89f7e2947f0cbace84f37ebe2209c31823c5c",
                   "bytes_per_launch": 268750056}
 
 
