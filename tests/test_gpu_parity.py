@@ -250,6 +250,19 @@ def test_decode_layers_gqa_groups(kp, monkeypatch, D, H_q, H_kv, force):
         kp.pion_prefix_drop("t", 740 + l)
 
 
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+def test_prefill_splits_without_keys(kp, D):
+    # a short prefix under a long causal suffix: the key range is cut into 64-key splits,
+    # and the first row blocks see no key in the later splits (their partials carry
+    # weight 0 in the merge); the last row block is ragged
+    inp = synth.generate(synth.PREFILL, 14, N=64, M=300, S_suf=300, D=D, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 8, dev(inp.K), dev(inp.V))
+    out, lse = empty((6, 300, D)), empty((6, 300))
+    kp.pion_prefix_query_fused("t", 8, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf))
+    kp.pion_prefix_drop("t", 8)
+
+
 def test_restore_replaces_and_unknown_session(kp):
     import kv_cache_prefix_amd as k
     a = synth.generate(synth.DECODE, 1, N=100, H_q=2, H_kv=2)
