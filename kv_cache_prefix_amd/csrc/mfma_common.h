@@ -53,6 +53,10 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // past the buffer's end the bytes are zero. One wait state separates the M0 write from
 // the load that reads it. The compiler cannot tell which LDS bytes such a load writes,
 // so it is issued here, and the caller waits for it (s_waitcnt vmcnt) before reading.
+// The compiler treats M0 as reserved and may ignore its clobber (it warns so); that is
+// safe only because nothing else in the kernels that call this reads or writes M0 — in
+// their ISA every M0 write is this statement's own, right before its load. A kernel that
+// adds a use of M0 (LDS DMA builtins, movrel indexing, s_sendmsg) must not call this.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                    :
