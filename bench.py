@@ -50,22 +50,36 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the decode kernel in --mode layers, from rocprofv3 FETCH_SIZE /
-# WRITE_SIZE counter passes scaled by the same counters on a plain 256 MiB copy
-# (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0). Valid only for the kernel sources they were
-# taken on (sha256 of attn_partial.hip + split_common.h + kernels.h); any other source
-# reports null.
-DECODE_TRAFFIC = {"sources_sha256": "2984738fdfb1f2ddb279d617edc89f7e2947f0cbace84f37ebe2209c31823c5c",
+# HBM bytes per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE counter passes scaled by
+# the same counters on a plain 256 MiB copy (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0).
+# Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
+# files, in order); any other source reports null.
+DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
+                  "sources_sha256": "2984738fdfb1f2ddb279d617edc89f7e2947f0cbace84f37ebe2209c31823c5c",
                   "bytes_per_launch": 268750056}
+# One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
+# 22,199,533 B and writes 32,275,046 B (the five splits' partials), prefill_merge_kernel<128>
+# reads 33,518,721 B and writes 6,340,608 B (out and lse).
+PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
+                   "sources_sha256": "ae6dc00513bcaeed0ec1cbc86366c2db992cab0a6778b4d0cb039b5e02687fa0",
+                   "bytes_per_launch": 94333909}
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(files=DECODE_TRAFFIC["sources"]):
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn_partial.hip", "split_common.h", "kernels.h"):
+    for f in files:
         with open(os.path.join(ROOT, "kv_cache_prefix_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def measured_traffic(entry):
+    """The counted bytes per launch while the sources match the ones counted, else None."""
+    ok = kernel_sources_sha256(entry["sources"]) == entry["sources_sha256"]
+    return entry["bytes_per_launch"] if ok else None
+
+
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "prefix-attn K/V GB/s (M=1) & TFLOP/s (batched-Q), % of MI355X roofline"
 
@@ -240,10 +254,8 @@ def run_decode(args, torch, kp, synth, dev, stream):
                                         f"layers ({NSET * bytes_step / 1e6:.0f} MB)"},
         "roofline": {"bound": "hbm", "achieved": bytes_launch / (launch_us * 1e-6) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "traffic": (DECODE_TRAFFIC["bytes_per_launch"]
-                                 if args.mode == "layers"
-                                 and kernel_sources_sha256() == DECODE_TRAFFIC["sources_sha256"]
-                                 else None),
+                     "traffic": (measured_traffic(DECODE_TRAFFIC)
+                                 if args.mode == "layers" else None),
                      "kernel": "attn_split_kernel<128,1,4,false,false,8>",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
         "warm": {"value": round(bytes_step / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
@@ -300,7 +312,8 @@ def run_prefill(args, torch, kp, synth, dev, stream):
         "config": {"workload": "fused batched-Q prefill H_q=24 H_kv=8 (h//3) D=128 N=4096 "
                                "M=S_suf=512 causal suffix", "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": flops / (launch_us * 1e-6) / 1e12,
-                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None,
+                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "traffic": measured_traffic(PREFILL_TRAFFIC),
                      "kernel": "prefill_kernel<128> then prefill_merge_kernel<128> (one call)",
                      "avg_launch_us": launch_us},
         "cpu_baseline": cpu,
