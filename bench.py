@@ -58,11 +58,16 @@ DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h")
                   "sources_sha256": "2984738fdfb1f2ddb279d617edc89f7e2947f0cbace84f37ebe2209c31823c5c",
                   "bytes_per_launch": 268750056}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
-# 22,199,533 B and writes 32,275,046 B (the five splits' partials), prefill_merge_kernel<128>
+# 22,198,510 B and writes 32,232,960 B (the five splits' partials), prefill_merge_kernel<128>
 # reads 33,518,721 B and writes 6,340,608 B (out and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "ae6dc00513bcaeed0ec1cbc86366c2db992cab0a6778b4d0cb039b5e02687fa0",
-                   "bytes_per_launch": 94333909}
+                   "sources_sha256": "434ed7b4ba112d6e3a480a1e927f5fb2700b284e57ddf3cb9c7e96b1a374bb46",
+                   "bytes_per_launch": 94290799}
+# The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_split_kernel<128,3,2,8>
+# reads 671,977,647 B (671,088,640 algorithmic) and writes 644,096 B.
+MLX4_TRAFFIC = {"sources": ("attn_mlx4.hip", "split_common.h", "kernels.h"),
+                "sources_sha256": "08e023b91efc5ce7880d0ee9844ad20e5bd076a324445f69abbcd3764f5199dd",
+                "bytes_per_launch": 672621743}
 
 
 def kernel_sources_sha256(files=DECODE_TRAFFIC["sources"]):
@@ -433,7 +438,8 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
                    "memory_side_cache": f"cold: steps alternate over {NSET} sets of {LAYERS} "
                                         f"slots ({NSET * nbytes / 1e6:.0f} MB)"},
         "roofline": {"bound": "hbm", "achieved": nbytes / (launch_us * 1e-6) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "traffic": measured_traffic(MLX4_TRAFFIC),
                      "kernel": "mlx4_split_kernel<128,3,2,8>",
                      "bytes_per_launch": nbytes, "avg_launch_us": launch_us},
         "warm": {"value": round(nbytes / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",

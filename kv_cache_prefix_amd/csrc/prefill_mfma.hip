@@ -277,10 +277,15 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds % KR], qb[ds], s, 0, 0, 0);
         if (ds + KR < NDS) kf[ds % KR] = kfrag(KB + 32 * kb * (int)ROWB, ds + KR);
       }
-      // the first k-step's V^T fragments load while the softmax runs
-      half8 vf[NDB];
+      // the V^T fragments of both 16-key k-steps load while the softmax runs; the
+      // scheduling barrier keeps the compiler from sinking the loads to their products,
+      // where the wait for LDS would stall the wave
+      half8 vf[NDB], vf2[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vf[db] = vfrag(VB + 32 * kb * (int)ROWB, db);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf2[db] = vfrag(VB + (32 * kb + 16) * (int)ROWB, db);
+      __builtin_amdgcn_sched_barrier(0);
       if (kt0 + 32 > clean_end) {  // boundary sub-tile: mask keys past this row's limit
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -311,13 +316,11 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pb[0], o[db], 0, 0, 0);
-        vf[db] = vfrag(VB + (32 * kb + 16) * (int)ROWB, db);
-      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pb[1], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf2[db], pb[1], o[db], 0, 0, 0);
     }
   };
 
