@@ -34,8 +34,16 @@ config 4: two sets of 16 layers, 1.34 GB; config 5: 4 slots), so each step reads
 steps have evicted; `value` is that cold figure. `warm` repeats one set every step and
 is reported beside it, labelled.
 
-cpu_baseline: the fp64 numpy oracle as it stands, one thread, on a bounded sample of the
-same workload (about 10 s), scaled to the metric's unit.
+The default run reports both halves of the metric in one JSON line: `value` is the M=1
+decode figure above (GB/s), and `batched_q` the fused batched-Q prefill (--config 3's
+workload, TFLOP/s) with its own roofline and CPU baseline; `stream_ceiling` is a plain
+streaming read of 1 GiB timed in the same run (the achievable HBM read rate).
+
+cpu_baseline (default run and --config 3): the fp64 numpy oracle as it stands, timed on
+the host before the GPU is touched: worker processes (one BLAS thread each) over all
+usable host cores (at most 16) on a fixed sample of the workload - whole 32-layer decode
+passes, or every row of one prefill step - median of 3 runs, with the 1-thread figure of
+a smaller sample beside it (`single_thread`). Other configs: one thread, about 10 s.
 """
 from __future__ import annotations
 
@@ -182,6 +190,117 @@ def cpu_time(fn, seconds):
                 return n, el
 
 
+# ----------------------------------------------------------------- host CPU baseline
+# Work shared with forked worker processes (set before the pool is created).
+_CPU_WORK = {}
+_PREFILL_ROWS = 64   # query rows per oracle work unit of the prefill baseline
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    global _TPL
+    _TPL = threadpool_limits(1)   # one BLAS thread per worker process
+
+
+def _oracle_unit(unit):
+    """One work unit of the oracle: a whole decode layer, or a block of prefill rows."""
+    import oracle
+    kind, a = unit
+    if kind == "decode":
+        inp = _CPU_WORK["decode"][a]
+        oracle.prefix_query(inp.Q, inp.K, inp.V)
+    else:
+        inp = _CPU_WORK["prefill"]
+        h, i0 = a
+        M = inp.Q.shape[1]
+        oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf,
+                                  rows=[(h, i) for i in range(i0, min(i0 + _PREFILL_ROWS, M))])
+    return 0
+
+
+def host_cores():
+    """Host cores the oracle may use: this process's CPU affinity, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _median_time(fn, runs=3):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def cpu_baselines(decode_inputs=None, prefill_input=None):
+    """Time the oracle on the host: all usable cores (worker processes forked before any
+    GPU use, one BLAS thread each) over a fixed sample, and one thread on a smaller one;
+    median of 3 runs each. Returns {"decode": ..., "prefill": ...} cpu_baseline objects."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    _CPU_WORK["decode"] = decode_inputs
+    _CPU_WORK["prefill"] = prefill_input
+    W = host_cores()
+    res = {}
+    with mp.get_context("fork").Pool(W, initializer=_worker_init) as pool:
+        pool.map(_oracle_unit, [("decode", 0)] * W if decode_inputs else
+                 [("prefill", (0, 0))] * W)   # warm the workers (imports)
+
+        def measure(units_all, units_one):
+            t_all = _median_time(lambda: pool.map(_oracle_unit, units_all, chunksize=1))
+            with threadpool_limits(1):
+                _oracle_unit(units_one[0])
+                t_one = _median_time(lambda: [_oracle_unit(u) for u in units_one])
+            return t_all, t_one
+
+        if decode_inputs:
+            L = len(decode_inputs)
+            inp = decode_inputs[0]
+            per_layer = inp.K.shape[0] * inp.K.shape[1] * inp.K.shape[2] * 2 * 2
+            all_u = [("decode", l) for _ in range(6 * W) for l in range(L)]
+            one_u = [("decode", l) for _ in range(6) for l in range(L)]
+            t_all, t_one = measure(all_u, one_u)
+            res["decode"] = {
+                "value": round(len(all_u) * per_layer / t_all / 1e9, 4), "unit": "GB/s",
+                "cores": W, "kind": "oracle",
+                "sample": f"{6 * W} whole {L}-layer passes of this workload over {W} worker processes "
+                          f"(fp64 numpy, one BLAS thread each), median of 3 runs "
+                          f"({t_all:.2f} s)",
+                "single_thread": {"value": round(len(one_u) * per_layer / t_one / 1e9, 4),
+                                  "sample": f"6 whole passes, 1 thread, median of 3 ({t_one:.2f} s)"},
+                "host_cpus": os.cpu_count()}
+        if prefill_input is not None:
+            H_q, M, D = prefill_input.Q.shape
+            N = prefill_input.K.shape[1]
+            S = 0 if prefill_input.K_suf is None else prefill_input.K_suf.shape[1]
+
+            def flops(unit):
+                h, i0 = unit[1]
+                return sum(4 * D * (N + (S - M + i + 1 if S else 0))
+                           for i in range(i0, min(i0 + _PREFILL_ROWS, M)))
+            step_u = [("prefill", (h, i0)) for h in range(H_q) for i0 in range(0, M, _PREFILL_ROWS)]
+            reps = max(1, W // 2)
+            all_u = step_u * reps
+            one_u = step_u[::2]
+            t_all, t_one = measure(all_u, one_u)
+            res["prefill"] = {
+                "value": round(sum(map(flops, all_u)) / t_all / 1e12, 6), "unit": "TFLOP/s",
+                "cores": W, "kind": "oracle",
+                "sample": f"every row of {reps} steps ({H_q * M} rows each, in blocks of {_PREFILL_ROWS}) "
+                          f"over {W} worker processes (fp64 numpy, one BLAS thread each), "
+                          f"median of 3 runs ({t_all:.2f} s)",
+                "single_thread": {"value": round(sum(map(flops, one_u)) / t_one / 1e12, 6),
+                                  "sample": f"{len(one_u) * _PREFILL_ROWS} rows (every 2nd block), "
+                                            f"1 thread, median of 3 ({t_one:.2f} s)"},
+                "host_cpus": os.cpu_count()}
+    _CPU_WORK.clear()
+    return res
+
+
 def check_close(got, ref, tol, what):
     import numpy as np
     err = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
@@ -190,11 +309,12 @@ def check_close(got, ref, tol, what):
 
 
 # ----------------------------------------------------------------------------- configs
-def run_decode(args, torch, kp, synth, dev, stream):
+def run_decode(args, torch, kp, synth, dev, stream, inputs=None, cpu=None):
     import numpy as np
     import oracle
     case = synth.DECODE
-    inputs = [synth.generate(case, l) for l in range(case.layers)]
+    if inputs is None:
+        inputs = [synth.generate(case, l) for l in range(case.layers)]
     sid = "bench-decode"
     NSET = 2   # layers [32 k, 32 k + 32) hold set k (the same data)
     for k in range(NSET):
@@ -227,8 +347,11 @@ def run_decode(args, torch, kp, synth, dev, stream):
 
     graph = args.mode == "calls" and not args.eager
     lps = len(calls[0])
-    (ms, launch_us), (wms, wlaunch_us) = warm_cold(torch, stream, [make_step(c) for c in calls],
-                                                   lps, graph, args)
+    steps = [make_step(c) for c in calls]
+    with torch.cuda.stream(stream):
+        steps[0]()
+    plan = kp.pion_prefix_last_plan()   # the kernel(s) of one launch of the step
+    (ms, launch_us), (wms, wlaunch_us) = warm_cold(torch, stream, steps, lps, graph, args)
     for l in (0, case.layers - 1):
         ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
         check_close(out[l].cpu().numpy(), ref, 2e-3, "out")
@@ -236,16 +359,6 @@ def run_decode(args, torch, kp, synth, dev, stream):
     bytes_layer = case.H_kv * case.N * case.D * 2 * 2
     bytes_step = bytes_layer * case.layers
     bytes_launch = bytes_step // lps
-    cpu = None
-    if not args.no_cpu_baseline:
-        def one_pass():
-            for inp in inputs:
-                oracle.prefix_query(inp.Q, inp.K, inp.V)
-        n, el = cpu_time(one_pass, args.cpu_seconds)
-        cpu = {"value": round(bytes_step * n / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{n} whole 32-layer passes of this workload "
-                         f"({el:.1f} s, fp64 numpy, 1 thread)"}
     kp.pion_prefix_drop(sid, -1)
     return {
         "value": bytes_step / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms,
@@ -261,7 +374,7 @@ def run_decode(args, torch, kp, synth, dev, stream):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "traffic": (measured_traffic(DECODE_TRAFFIC)
                                  if args.mode == "layers" else None),
-                     "kernel": "attn_split_kernel<128,1,4,false,false,8>",
+                     "kernel": plan,
                      "bytes_per_launch": bytes_launch, "avg_launch_us": launch_us},
         "warm": {"value": round(bytes_step / (wms * 1e-3) / 1e9, 3), "unit": "GB/s",
                  "avg_launch_us": round(wlaunch_us, 3),
@@ -270,10 +383,14 @@ def run_decode(args, torch, kp, synth, dev, stream):
     }
 
 
-def run_prefill(args, torch, kp, synth, dev, stream):
+def run_prefill(args, torch, kp, synth, dev, stream, inp=None, cpu=None, calls=None):
+    """The fused batched-Q prefill: `calls` timed back-to-back calls (default: --steps),
+    each bracketed by HIP events on the launch stream; the mean of those durations is the
+    roofline's launch time, their median is reported beside it."""
     import oracle
     case = synth.PREFILL
-    inp = synth.generate(case)
+    if inp is None:
+        inp = synth.generate(case)
     sid = "bench-prefill"
     kp.pion_prefix_store(sid, 0, torch.from_numpy(inp.K).to(dev),
                          torch.from_numpy(inp.V).to(dev))
@@ -289,40 +406,74 @@ def run_prefill(args, torch, kp, synth, dev, stream):
         if rc != 0:
             raise kp.PionError(rc, "pion_prefix_query_fused")
 
-    t = Timed(torch, stream, step, 1, False)
-    ms, launch_us = t.measure(args.steps, args.warmup)
-    rows = [(0, 0), (5, 511), (23, 300), (12, 100)]
-    ref, _ = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
-    o = out.cpu().numpy()
-    for h, i in rows:
-        check_close(o[h, i], ref[h, i], 2e-3, "out")
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            step()
+    plan = kp.pion_prefix_last_plan()
+    n = calls or args.steps
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(n):
+            step()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
+    launch_us = evs[0].elapsed_time(evs[n]) * 1e3 / n
+    median_us = per_call[n // 2]
+    # every row checked against the oracle (the timed calls all wrote the same output)
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    check_close(o, ref, 2e-3, "out")
+    check_close(l, ref_lse, 1e-4, "lse")
     flops = 4 * case.H_q * case.D * (case.M * case.N + case.M * (case.M + 1) // 2)
-    cpu = None
-    if not args.no_cpu_baseline:
-        rows_all = [(h, i) for h in range(case.H_q) for i in range(0, case.M, 64)]
-        k = [0]
-
-        def one_row():
-            h, i = rows_all[k[0] % len(rows_all)]
-            k[0] += 1
-            oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=[(h, i)])
-        n, el = cpu_time(one_row, args.cpu_seconds)
-        per_row = 4 * case.D * (case.N + case.S_suf / 2)
-        cpu = {"value": round(per_row * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-               "kind": "oracle", "sample": f"{n} query rows of this workload ({el:.1f} s)"}
     kp.pion_prefix_drop(sid, -1)
     return {
         "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
         "dtype": "fp16 in, fp32 accumulate",
         "config": {"workload": "fused batched-Q prefill H_q=24 H_kv=8 (h//3) D=128 N=4096 "
-                               "M=S_suf=512 causal suffix", "flops_per_step": flops},
+                               "M=S_suf=512 causal suffix", "entry": "pion_prefix_query_fused",
+                   "calls_timed": n, "flops_per_call": flops},
         "roofline": {"bound": "mfma", "achieved": flops / (launch_us * 1e-6) / 1e12,
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "traffic": measured_traffic(PREFILL_TRAFFIC),
-                     "kernel": "prefill_kernel<128> then prefill_merge_kernel<128> (one call)",
-                     "avg_launch_us": launch_us},
+                     "kernel": plan, "flops_per_launch": flops,
+                     "avg_launch_us": launch_us, "median_launch_us": round(median_us, 3),
+                     "median_TFLOP/s": round(flops / (median_us * 1e-6) / 1e12, 2),
+                     "max_abs_err": {"out": float(abs(o - ref).max()),
+                                     "lse": float(abs(l - ref_lse).max())}},
         "cpu_baseline": cpu,
     }
+
+
+def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20):
+    """A plain streaming read of `nbytes` (past the 256 MB memory-side cache), `reps` times
+    back to back: the achievable HBM read rate, timed with HIP events."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            kp.pion_bench_stream_read(buf, sink)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            kp.pion_bench_stream_read(buf, sink)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    del buf
+    return {"value": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(us, 2), "kernel": "stream_read_kernel",
+            "note": f"plain streaming read of {nbytes >> 20} MiB with 16-byte non-temporal "
+                    f"loads, {reps} launches back to back (cold: past the memory-side cache)"}
 
 
 def run_mlx4(args, torch, kp, synth, dev, stream):
@@ -681,17 +832,11 @@ def run_vstore(args, torch, kp, synth, dev, stream):
     pion_prefix_warm (K and V of one layer into an fp16 slot, replacing the live slot:
     allocation, two relayout launches, the free of the old slot), host work included."""
     import numpy as np
-    import oracle
     from oracle import vstore as ovs
     L, H, N, D = 32, 8, 2048, 128
     kv = H * D
     NCOPY = 4
-    recs = []
-    for l in range(L):
-        inp = synth.generate(synth.DECODE, l, N=N, D=D, H_q=H, H_kv=H)
-        for x in (inp.K, inp.V):
-            rows = np.ascontiguousarray(x.transpose(1, 0, 2).reshape(N, kv))
-            recs.append(ovs.pack_records(*oracle.quantize(rows)))
+    recs = [synth.mlx4_records(N, kv, [7, l, side]) for l in range(L) for side in range(2)]
     rb = recs[0].shape[1]
     dev_recs = [[torch.from_numpy(r).to(dev) for r in recs] for _ in range(NCOPY)]
     out = [torch.empty((N, kv), dtype=torch.float32, device=dev) for _ in range(2)]
@@ -761,12 +906,30 @@ def run_vstore(args, torch, kp, synth, dev, stream):
     }
 
 
+def _finish_roofline(roof):
+    roof["achieved"] = round(roof["achieved"], 2)
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    if "avg_launch_us" in roof:
+        roof["avg_launch_us"] = round(roof["avg_launch_us"], 3)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    # Inputs of the default run, and the oracle timed on the host cores, before anything
+    # touches the GPU (the worker processes are forked from this process).
+    pre, cpu = {}, {}
+    if args.config in (2, 3) and args.copy_bytes <= 0:
+        import synth
+        if args.config == 2:
+            pre["decode"] = [synth.generate(synth.DECODE, l) for l in range(synth.DECODE.layers)]
+        if args.config == 3 or args.mode == "layers":
+            pre["prefill"] = synth.generate(synth.PREFILL)
+        if not args.no_cpu_baseline:
+            cpu = cpu_baselines(pre.get("decode"), pre.get("prefill"))
     import torch
     if args.copy_bytes > 0:
         x = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
@@ -782,15 +945,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
-    runner = {1: run_tiny, 2: run_decode, 3: run_prefill, 4: run_mlx4, 5: run_sparse,
-              6: run_query_sparse, 7: run_vstore, 8: run_sweep}[args.config]
-    r = runner(args, torch, kp, synth, dev, stream)
+    if args.config == 2:
+        r = run_decode(args, torch, kp, synth, dev, stream, inputs=pre.get("decode"),
+                       cpu=cpu.get("decode"))
+        if args.mode == "layers":   # the default run: both halves of the metric
+            bq = run_prefill(args, torch, kp, synth, dev, stream, inp=pre.get("prefill"),
+                             cpu=cpu.get("prefill"), calls=max(args.steps, 100))
+            _finish_roofline(bq["roofline"])
+            r["batched_q"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                              for k, v in bq.items()}
+            r["stream_ceiling"] = stream_ceiling(torch, kp, dev, stream)
+    elif args.config == 3:
+        r = run_prefill(args, torch, kp, synth, dev, stream, inp=pre.get("prefill"),
+                        cpu=cpu.get("prefill"))
+    else:
+        runner = {1: run_tiny, 4: run_mlx4, 5: run_sparse, 6: run_query_sparse,
+                  7: run_vstore, 8: run_sweep}[args.config]
+        r = runner(args, torch, kp, synth, dev, stream)
     roof = r["roofline"]
     if roof is not None:
-        roof["achieved"] = round(roof["achieved"], 2)
-        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-        if "avg_launch_us" in roof:
-            roof["avg_launch_us"] = round(roof["avg_launch_us"], 3)
+        _finish_roofline(roof)
     line = {
         "metric": METRIC,
         "value": round(r["value"], 3),
@@ -808,7 +982,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    for extra in ("warm", "single_query", "warm_call", "quantize", "fp16_resident", "sweep"):
+    for extra in ("warm", "batched_q", "stream_ceiling", "single_query", "warm_call",
+                  "quantize", "fp16_resident", "sweep"):
         if extra in r:
             line[extra] = r[extra]
     print(json.dumps(line), flush=True)

@@ -262,6 +262,20 @@ int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D,
 /* Static description of a status code (never NULL). */
 const char *pion_status_str(int status);
 
+/* Launch-plan telemetry (not a wire form): the names, with template arguments, of the
+ * kernels the calling thread's most recent call of this library enqueued, joined by
+ * " + " (e.g. "prefill_kernel<128> + prefill_merge_kernel<128>"); "" if it enqueued
+ * none. The string belongs to the library and stays valid until the thread's next call.
+ * Host-only. */
+const char *pion_prefix_last_plan(void);
+
+/* Measurement aid (not a wire form): reads `bytes` at the device pointer buf once with
+ * 16-byte non-temporal loads and does nothing else - the plain streaming read whose rate
+ * is the achievable ceiling the bandwidth-bound kernels are compared with. sink is one
+ * device uint32 the kernel may write (it does not, for realistic data). bytes must be a
+ * multiple of 16 (0 is a no-op); buf 16-byte aligned. Errors: INVALID, HIP. */
+int pion_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

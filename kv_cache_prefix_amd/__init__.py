@@ -49,6 +49,8 @@ SIGNATURES = {
                                      ctypes.c_int64, _vp, _vp]),
     "pion_prefix_warm": (_int, [_c_char_p, _int, _int, _int, _int, _int, _vp, _vp, _int, _vp]),
     "pion_status_str": (ctypes.c_char_p, [_int]),
+    "pion_prefix_last_plan": (ctypes.c_char_p, []),
+    "pion_bench_stream_read": (_int, [_vp, ctypes.c_int64, _vp, _vp]),
 }
 
 _lib = None
@@ -326,6 +328,22 @@ def pion_kv_quantize_mlx4g32(x, codes, scales, biases, stream=None) -> int:
         _dev(scales, torch.float16, "scales", (rows, D // 32)),
         _dev(biases, torch.float16, "biases", (rows, D // 32)), _stream(stream))
     return _check(rc, "pion_kv_quantize_mlx4g32")
+
+
+def pion_prefix_last_plan() -> str:
+    """Kernel names the calling thread's most recent library call enqueued ("" if none)."""
+    return lib().pion_prefix_last_plan().decode()
+
+
+def pion_bench_stream_read(buf, sink, stream=None) -> int:
+    """Measurement aid: one plain streaming read of the whole device tensor `buf` (its
+    byte size a multiple of 16); sink is a 1-element int32 device tensor."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    rc = lib().pion_bench_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                      _dev(sink, torch.int32, "sink", (1,)), _stream(stream))
+    return _check(rc, "pion_bench_stream_read")
 
 
 __all__ = [n for n in SIGNATURES if n != "pion_status_str"] + [

@@ -274,6 +274,7 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
 template <int D>
 hipError_t launch_d(const PartialParams &p, int x_count, hipStream_t s) {
   dim3 grid(x_count, p.y_groups, p.n_prob);
+  note_launch("gqa_mfma_kernel<%d>", D);
   hipLaunchKernelGGL(gqa_mfma_kernel<D>, grid, dim3(64 * GqaSmem<D>::NW), 0, s, p);
   return hipGetLastError();
 }

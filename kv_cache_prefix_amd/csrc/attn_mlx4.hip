@@ -385,6 +385,7 @@ template <int D, int R>
 hipError_t launch_mlx4_d(const PartialParams &p, int x_count, hipStream_t s) {
   constexpr int NW = R <= 3 ? 8 : 4;
   dim3 grid(x_count, p.y_groups, p.n_prob);
+  note_launch("mlx4_split_kernel<%d,%d,2,%d>", D, R, NW);
   hipLaunchKernelGGL((mlx4_split_kernel<D, R, 2, NW>), grid, dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }

@@ -349,6 +349,14 @@ template <int D, int R>
 hipError_t launch_partial_d(const PartialParams &p, int x_count, hipStream_t s) {
   dim3 grid(x_count, p.y_groups, p.n_prob);
   const bool f32 = p.fmt == 2;
+  if (p.gidx)
+    note_launch("attn_split_kernel<%d,1,%d,true,%s>", D, f32 ? 2 : 4, f32 ? "true" : "false");
+  else if (f32)
+    note_launch("attn_split_kernel<%d,%d,2,false,true>", D, R);
+  else if (p.waves == 8 && R <= 4)
+    note_launch("attn_split_kernel<%d,%d,4,false,false,8>", D, R);
+  else
+    note_launch("attn_split_kernel<%d,%d,4,false,false>", D, R);
   if (p.gidx && f32)
     hipLaunchKernelGGL((attn_split_kernel<D, 1, 2, true, true>), grid, dim3(256), 0, s, p);
   else if (p.gidx)

@@ -7,6 +7,11 @@
 
 namespace pion {
 
+// Records the name (printf-style, with its template arguments) of a kernel a launch
+// function enqueues; the C ABI keeps the names of the current call's launches for
+// pion_prefix_last_plan. Defined in pion_prefix.cpp; host only.
+void note_launch(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 constexpr int kMaxHeads = 128;     // H_q limit (row-group table size)
 constexpr int kRowsPerGroup = 8;   // q-heads sharing one kv-head read per workgroup
 
@@ -205,6 +210,10 @@ hipError_t launch_rows_to_fp32_slot(const void *rows, int fmt, int64_t N, int H,
                                     float *dst, hipStream_t s);
 hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, uint32_t *codes,
                                     uint32_t *pairs, hipStream_t s);
+
+// Read `bytes` (a multiple of 16) at buf once with 16-byte non-temporal loads and
+// nothing else (the streaming-read ceiling); sink receives at most one word.
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
 
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);

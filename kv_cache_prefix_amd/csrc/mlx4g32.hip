@@ -5,6 +5,8 @@
 // Per group, in fp32 with IEEE round-to-nearest-even on every op:
 //   mn = min x, mx = max x, s = fp16((mx - mn) / 15), b = fp16(mn),
 //   q = clamp(rint((x - b) / s), 0, 15), or all zero when s == 0.
+// The minimum and maximum order -0 below +0, so the bias of a group whose minimum is
+// zero is -0 exactly when the group holds a -0. Inputs must be finite.
 // Element i of a row goes to word i/8 at bits 4*(i%8).
 //
 // Layout: one lane per uint32 code word (8 elements, 16 input bytes), so four
@@ -53,6 +55,23 @@ __device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
   mn = fminf(mn, quad_xor<0x4E>(mn));  // lane ^ 2
   mx = fmaxf(mx, quad_xor<0xB1>(mx));
   mx = fmaxf(mx, quad_xor<0x4E>(mx));
+  // Signed zeros: -0 orders below +0, so a zero minimum is -0 when the group holds a -0
+  // and a zero maximum is +0 when it holds a +0 (fminf / fmaxf return either zero).
+  // Rare, and the branch is wave-uniform.
+  if (__builtin_amdgcn_ballot_w64(mn == 0.0f || mx == 0.0f)) {
+    int negz = 0, posz = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      negz |= (int)((w[c] & 0xffffu) == 0x8000u) | (int)((w[c] >> 16) == 0x8000u);
+      posz |= (int)((w[c] & 0xffffu) == 0u) | (int)((w[c] >> 16) == 0u);
+    }
+    negz |= __builtin_bit_cast(int, quad_xor<0xB1>(__builtin_bit_cast(float, negz)));
+    negz |= __builtin_bit_cast(int, quad_xor<0x4E>(__builtin_bit_cast(float, negz)));
+    posz |= __builtin_bit_cast(int, quad_xor<0xB1>(__builtin_bit_cast(float, posz)));
+    posz |= __builtin_bit_cast(int, quad_xor<0x4E>(__builtin_bit_cast(float, posz)));
+    if (mn == 0.0f) mn = negz ? -0.0f : 0.0f;
+    if (mx == 0.0f) mx = posz ? 0.0f : -0.0f;
+  }
 
   const float range = mx - mn;
   const float s32 = __fdiv_rn(range, 15.0f);
@@ -122,6 +141,7 @@ hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint3
   if (sb_stride != 1 && sb_stride != 2) return hipErrorInvalidValue;
   const int64_t blocks = (nwords + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  note_launch("quantize_mlx4g32_kernel");
   hipLaunchKernelGGL(quantize_mlx4g32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x,
                      nwords, codes, scales, biases, sb_stride);
   return hipGetLastError();

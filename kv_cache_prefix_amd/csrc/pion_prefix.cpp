@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdarg>
+#include <cstdio>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -685,9 +687,37 @@ int check_query_args(const char *sid, int H_q, int D, int M, const void *Q, cons
   return PION_OK;
 }
 
+// Kernel names of the current call's launches, on the calling thread.
+thread_local std::string g_plan;
+void plan_begin() { g_plan.clear(); }
+
 }  // namespace
 
+namespace pion {
+void note_launch(const char *fmt, ...) {
+  char buf[160];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (!g_plan.empty()) g_plan += " + ";
+  g_plan += buf;
+}
+}  // namespace pion
+
 extern "C" {
+
+const char *pion_prefix_last_plan(void) { return g_plan.c_str(); }
+
+int pion_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  plan_begin();
+  if (bytes < 0 || bytes % 16) return PION_ERR_INVALID;
+  if (bytes == 0) return PION_OK;
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4)) return PION_ERR_INVALID;
+  if (!on_device(buf) || !on_device(sink)) return PION_ERR_INVALID;
+  return launch_stream_read(buf, bytes, sink, (hipStream_t)stream) == hipSuccess ? PION_OK
+                                                                                 : PION_ERR_HIP;
+}
 
 const char *pion_status_str(int status) {
   switch (status) {
@@ -704,6 +734,7 @@ const char *pion_status_str(int status) {
 
 int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D, uint32_t *codes, void *scales,
                              void *biases, void *stream) {
+  plan_begin();
   if (rows < 0 || D <= 0 || D % 32) return PION_ERR_INVALID;
   if (rows == 0) return PION_OK;
   if (!x || !codes || !scales || !biases) return PION_ERR_INVALID;
@@ -719,6 +750,7 @@ int pion_kv_quantize_mlx4g32(const void *x, int64_t rows, int D, uint32_t *codes
 
 int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const void *K,
                       const void *V, int kv_format, void *stream) {
+  plan_begin();
   int rc = check_slot_shape(sid, H, N, D, kv_format);
   if (rc != PION_OK) return rc;
   if (!K || !V || !aligned(K, 16) || !aligned(V, 16)) return PION_ERR_INVALID;
@@ -732,6 +764,7 @@ int pion_prefix_store(const char *sid, int layer, int H, int N, int D, const voi
 
 int pion_prefix_warm(const char *sid, int layer, int H, int N, int D, int src_format,
                      const void *K_rows, const void *V_rows, int kv_format, void *stream) {
+  plan_begin();
   int rc = check_slot_shape(sid, H, N, D, kv_format);
   if (rc != PION_OK) return rc;
   if (src_format != PION_KV_FP16 && src_format != PION_KV_MLX4G32) return PION_ERR_INVALID;
@@ -781,6 +814,7 @@ int pion_prefix_warm(const char *sid, int layer, int H, int N, int D, int src_fo
 
 int pion_vstore_fetch_f32(const void *rows, int fmt, int64_t n_rows, int kv_dim, int64_t start,
                           int64_t end, float *out, void *stream) {
+  plan_begin();
   if (n_rows < 0 || kv_dim <= 0) return PION_ERR_INVALID;
   if (fmt != PION_KV_FP16 && fmt != PION_KV_MLX4G32) return PION_ERR_INVALID;
   if (kv_dim % 32) return PION_ERR_INVALID;  // whole groups of 32 values
@@ -887,6 +921,7 @@ int pion_prefix_set_capacity(int64_t max_slots, int64_t max_bytes, int64_t cold_
 
 int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const void *Q,
                       const int32_t *head_map, float *out, float *lse, void *stream) {
+  plan_begin();
   int rc = check_query_args(sid, H_q, D, M, Q, out);
   if (rc != PION_OK) return rc;
   if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
@@ -916,6 +951,7 @@ int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const v
 int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q, int D, int M,
                              const void *Q, const int32_t *head_map, float *out, float *lse,
                              void *stream) {
+  plan_begin();
   int rc = check_query_args(sid, H_q, D, M, Q, out);
   if (rc != PION_OK) return rc;
   if (n_layers < 1 || n_layers > kMaxBatch) return PION_ERR_INVALID;
@@ -959,6 +995,7 @@ int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q,
 int pion_prefix_query_fused(const char *sid, int layer, int H_q, int D, int M, int S_suf,
                             int H_kv, const void *Q, const void *K_suf, const void *V_suf,
                             const int32_t *head_map, float *out, float *lse, void *stream) {
+  plan_begin();
   int rc = check_query_args(sid, H_q, D, M, Q, out);
   if (rc != PION_OK) return rc;
   if (S_suf < 0 || H_kv < 1 || H_kv > 255) return PION_ERR_INVALID;
@@ -996,6 +1033,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
                                   int H_kv, int S_suf, const void *Q, const void *K_suf,
                                   const void *V_suf, const int32_t *head_map, float *out,
                                   float *lse, int32_t *blocks_out, void *stream) {
+  plan_begin();
   int rc = check_query_args(sid, H_q, D, 1, Q, out);
   if (rc != PION_OK) return rc;
   if (B < 1 || K_top < 1 || K_top > kMaxKTop || S_suf < 0 || H_kv < 1 || H_kv > 255)
@@ -1102,6 +1140,7 @@ int pion_prefix_query_sparse_auto(const char *sid, int layer, int H_q, int D, in
 int pion_prefix_query_sparse(const char *sid, int layer, int H, int D, int K_sparse_max,
                              const void *Q, const int32_t *indices, const int32_t *counts,
                              float *out, float *lse, void *stream) {
+  plan_begin();
   int rc = check_query_args(sid, H, D, 1, Q, out);
   if (rc != PION_OK) return rc;
   if (K_sparse_max < 1 || K_sparse_max > (1 << 24) || !indices || !counts) return PION_ERR_INVALID;

@@ -450,6 +450,8 @@ hipError_t launch_prefill(const PrefillParams &p, hipStream_t s) {
   const int tiles = p.H_q * p.n_iblk, W = tiles * p.n_splits;
   const dim3 grid(8 * ((W + 7) / 8)), mgrid(tiles * (p.D / 32));
   const bool merge = p.n_splits > 1;
+  note_launch("prefill_kernel<%d>", p.D);
+  if (merge) note_launch("prefill_merge_kernel<%d>", p.D);
 #define PION_PREFILL_D(DD)                                                              \
   case DD:                                                                              \
     hipLaunchKernelGGL(prefill_kernel<DD>, grid, dim3(256), 0, s, p);                   \

@@ -387,6 +387,7 @@ hipError_t launch_block_mean(const KVView &kv, int B, float *kmean, hipStream_t 
   int tpr = 1;
   while (tpr < kv.D / E) tpr <<= 1;
   if (tpr > 256) return hipErrorInvalidValue;
+  note_launch("block_mean_kernel<%d>", kv.fmt);
   if (kv.fmt == 0)
     hipLaunchKernelGGL(block_mean_kernel<0>, grid, dim3(256), 0, s, kv, B, nb, tpr, kmean);
   else if (kv.fmt == 2)
@@ -401,6 +402,7 @@ hipError_t launch_block_select(const void *Q, bool q32, const HeadMap &hm, const
                                uint64_t *cand, int *counters, int32_t *blocks, hipStream_t s) {
   if (K_top < 1 || nb < 1 || H_kv < 1) return hipErrorInvalidValue;
   dim3 grid((nb + kSelBlocks - 1) / kSelBlocks, H_kv);
+  note_launch("block_select_kernel<%d,%s>", D, q32 ? "true" : "false");
 #define PION_SELECT_D(DD)                                                                  \
   case DD:                                                                               \
     if (q32)                                                                             \

@@ -221,6 +221,7 @@ hipError_t launch_vstore_fetch(const void *rows, int fmt, int kv, int64_t start,
   const int64_t total = count * (kv / 4);
   const dim3 g(grid_for(total)), b(256);
   const uint8_t *r = (const uint8_t *)rows;
+  note_launch("fetch_f32_kernel<%d,%s>", fmt, narrow(total) ? "false" : "true");
   if (fmt == 0) {
     if (narrow(total)) hipLaunchKernelGGL((fetch_f32_kernel<0, false>), g, b, 0, s, r, kv, start, count, out);
     else hipLaunchKernelGGL((fetch_f32_kernel<0, true>), g, b, 0, s, r, kv, start, count, out);
@@ -236,6 +237,7 @@ hipError_t launch_rows_to_fp16_slot(const void *rows, int fmt, int64_t N, int H,
   const int64_t total = N * (H * D / 8);
   const dim3 g(grid_for(total)), b(256);
   const uint8_t *r = (const uint8_t *)rows;
+  note_launch("rows_to_fp16_slot_kernel<%d,%s>", fmt, narrow(total) ? "false" : "true");
   if (fmt == 0) {
     if (narrow(total)) hipLaunchKernelGGL((rows_to_fp16_slot_kernel<0, false>), g, b, 0, s, r, N, H, D, dst);
     else hipLaunchKernelGGL((rows_to_fp16_slot_kernel<0, true>), g, b, 0, s, r, N, H, D, dst);
@@ -251,6 +253,7 @@ hipError_t launch_rows_to_fp32_slot(const void *rows, int fmt, int64_t N, int H,
   const int64_t total = N * (H * D / 4);
   const dim3 g(grid_for(total)), b(256);
   const uint8_t *r = (const uint8_t *)rows;
+  note_launch("rows_to_fp32_slot_kernel<%d,%s>", fmt, narrow(total) ? "false" : "true");
   if (fmt == 0) {
     if (narrow(total)) hipLaunchKernelGGL((rows_to_fp32_slot_kernel<0, false>), g, b, 0, s, r, N, H, D, dst);
     else hipLaunchKernelGGL((rows_to_fp32_slot_kernel<0, true>), g, b, 0, s, r, N, H, D, dst);
@@ -266,6 +269,7 @@ hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, u
   const int64_t total = N * (H * D / 8);
   const dim3 g(grid_for(total)), b(256);
   const uint8_t *r = (const uint8_t *)rows;
+  note_launch("rows_to_mlx4_slot_kernel<%s>", narrow(total) ? "false" : "true");
   if (narrow(total)) hipLaunchKernelGGL((rows_to_mlx4_slot_kernel<false>), g, b, 0, s, r, N, H, D, codes, pairs);
   else hipLaunchKernelGGL((rows_to_mlx4_slot_kernel<true>), g, b, 0, s, r, N, H, D, codes, pairs);
   return hipGetLastError();

@@ -16,8 +16,9 @@ import numpy as np
 
 
 def f64(x) -> np.ndarray:
-    """fp16 (or any float) array -> fp64; exact for fp16 and fp32 inputs."""
-    return np.asarray(x).astype(np.float64)
+    """fp16 (or any float) array -> fp64; exact for fp16 and fp32 inputs (an fp64 array
+    is returned as it is)."""
+    return np.asarray(x, dtype=np.float64)
 
 
 def softmax_scale(D: int) -> float:
@@ -141,13 +142,17 @@ def prefix_query_fused(Q, K, V, K_suf, V_suf, head_map=None, rows=None):
     tau = softmax_scale(D)
     out = np.full((H_q, M, D), np.nan)
     lse = np.full((H_q, M), np.nan)
+    # per kv-head, the concatenated key set [prefix || suffix] in fp64; row i's keys are
+    # its first N + suffix_visible(i) entries
+    cat = {}
     for h, i in _rows(H_q, M, rows):
         g = hm[h]
-        if S_suf > 0:
-            n = suffix_visible(S_suf, M, i)
-            keys = np.concatenate([f64(K[g]), f64(K_suf[g, :n])])
-            vals = np.concatenate([f64(V[g]), f64(V_suf[g, :n])])
-        else:
-            keys, vals = K[g], V[g]
-        out[h, i], lse[h, i] = attend(Q[h, i], keys, vals, tau)
+        if g not in cat:
+            if S_suf > 0:
+                cat[g] = (np.concatenate([f64(K[g]), f64(K_suf[g])]),
+                          np.concatenate([f64(V[g]), f64(V_suf[g])]))
+            else:
+                cat[g] = (f64(K[g]), f64(V[g]))
+        n = K.shape[1] + (suffix_visible(S_suf, M, i) if S_suf > 0 else 0)
+        out[h, i], lse[h, i] = attend(Q[h, i], cat[g][0][:n], cat[g][1][:n], tau)
     return out, lse

@@ -19,6 +19,14 @@ each op IEEE-rounded (numpy float32 arithmetic):
      q_j = clamp(rint_half_even(t_j), 0, 15)
   6. row element i -> word i // 8, bits 4 * (i % 8); group G's scale and bias at index G
   7. reader: x_hat = s * q + b  (fp64 here, where it is exact)
+
+Two readings where the pages are silent, both part of the encoding here:
+  * signed zeros: -0 orders below +0 (the minimum / maximum operations of IEEE 754-2019),
+    so a group whose minimum is zero has bias -0 (bits 0x8000) when it holds a -0 and
+    +0 otherwise, and a group whose maximum is zero has maximum +0 when it holds a +0;
+    the scale (max - min) / 15 is then +0 for an all-zero group whatever its signs;
+  * non-finite input (inf, NaN) is outside the encoder's domain: it is rejected here and
+    the device encoder's result for such a group is unspecified.
 """
 from __future__ import annotations
 
@@ -36,9 +44,19 @@ def quantize(x16):
     rows, D = x16.shape
     if D % GROUP:
         raise ValueError("D must be a multiple of 32")
+    if not np.all(np.isfinite(x16)):
+        raise ValueError("mlx4g32 input must be finite")
     x = x16.astype(np.float32).reshape(rows, D // GROUP, GROUP)
     mn = x.min(axis=-1)                                   # step 1
     mx = x.max(axis=-1)
+    # -0 below +0: a zero minimum is -0 if the group holds a -0, a zero maximum +0 if it
+    # holds a +0 (numpy's reduction would return whichever zero it met first)
+    is_zero = x == 0
+    neg_zero = (is_zero & np.signbit(x)).any(axis=-1)
+    pos_zero = (is_zero & ~np.signbit(x)).any(axis=-1)
+    mn = np.where(mn == 0, np.where(neg_zero, np.float32(-0.0), np.float32(0.0)), mn)
+    mx = np.where(mx == 0, np.where(pos_zero, np.float32(0.0), np.float32(-0.0)), mx)
+    mn, mx = mn.astype(np.float32), mx.astype(np.float32)
     s32 = (mx - mn) / np.float32(15.0)                    # step 2 (fp32 / fp32)
     assert s32.dtype == np.float32
     s16 = s32.astype(np.float16)                          # step 3 (RNE)

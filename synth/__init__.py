@@ -144,3 +144,23 @@ def random_head_map(H_q: int, H_kv: int, seed: int) -> np.ndarray:
     if H_q >= H_kv:
         m[rng.permutation(H_q)[:H_kv]] = np.arange(H_kv, dtype=np.int32)
     return m
+
+
+def mlx4_records(n_tokens: int, kv_dim: int, seed) -> np.ndarray:
+    """Random V-store records of the mlx4g32 tier (the per-token layout of the V-store
+    page, "The mlx4g32 tier": kv_dim/8 little-endian uint32 code words, then kv_dim/32
+    fp16 scales, then kv_dim/32 fp16 biases) -> uint8 [n_tokens, 5 * kv_dim / 8].
+
+    Every field is drawn directly (no encoder runs): code words uniform over all 32-bit
+    values, scales |N(0, 1)| * 0.25 and biases N(0, 1) - 2, both cast to fp16 (finite,
+    scales >= 0), so the dequantized values spread over roughly [-4, 4]."""
+    if kv_dim % 32:
+        raise ValueError("kv_dim must be a multiple of 32")
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 2 ** 32, size=(n_tokens, kv_dim // 8), dtype=np.uint64)
+    codes = codes.astype("<u4")
+    scales = (np.abs(rng.standard_normal((n_tokens, kv_dim // 32))) * 0.25).astype("<f2")
+    biases = (rng.standard_normal((n_tokens, kv_dim // 32)) - 2.0).astype("<f2")
+    return np.concatenate([codes.view(np.uint8).reshape(n_tokens, -1),
+                           scales.view(np.uint8).reshape(n_tokens, -1),
+                           biases.view(np.uint8).reshape(n_tokens, -1)], axis=1)

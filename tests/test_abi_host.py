@@ -29,10 +29,20 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_last_plan_and_stream_read_without_a_gpu(lib):
+    # a call rejected before any launch leaves an empty plan; the measurement aid
+    # validates its arguments on the host
+    assert lib.pion_kv_quantize_mlx4g32(None, 4, 33, None, None, None, None) == kp.PION_ERR_INVALID
+    assert kp.pion_prefix_last_plan() == ""
+    assert lib.pion_bench_stream_read(None, 17, None, None) == kp.PION_ERR_INVALID
+    assert lib.pion_bench_stream_read(None, 0, None, None) == kp.PION_OK
+    assert kp.pion_prefix_last_plan() == ""
 
 
 def test_status_strings(lib):

@@ -2,7 +2,7 @@
 "Shared KV Cache Serving", native SDPA paragraph): every query form on fp32 K/V, Q and
 suffix against the fp64 oracle on the same seeded fp32 inputs, and the WARM rehydrate
 into an fp32 slot (the pages' own dequantize-to-fp32 path) against a slot stored from
-the oracle's fetch. With fp32 operands no fp16 rounding is allowed anywhere, so the
+the device fetch, and both against the oracle. With fp32 operands no fp16 rounding is allowed anywhere, so the
 bound is tighter than the fp16 one: 1e-4 on out, 2e-5 on lse."""
 import numpy as np
 import pytest
@@ -127,12 +127,17 @@ def test_warm_into_fp32_slot(kp, src, H, N, D):
     inp = synth.generate(synth.DECODE, 76, N=N, D=D, H_q=H, H_kv=H)
     rows = [np.ascontiguousarray(x.transpose(1, 0, 2).reshape(N, H * D)) for x in (inp.K, inp.V)]
     if src == ovs.MLX4G32:
-        rows = [ovs.pack_records(*oracle.quantize(r)) for r in rows]
+        rows = [synth.mlx4_records(N, H * D, 760 + i) for i in range(2)]
     kp.pion_prefix_warm("f32", 5, H, D, dev(rows[0]), dev(rows[1]), src, kp.PION_KV_FP32)
     assert kp.pion_prefix_info("f32", 5)[3] == kp.PION_KV_FP32
     Kw, Vw = [np.ascontiguousarray(ovs.fetch_f32(r, src, H * D, 0, N).reshape(N, H, D)
                                    .transpose(1, 0, 2)) for r in rows]
-    kp.pion_prefix_store("f32", 6, dev(Kw), dev(Vw), kp.PION_KV_FP32)
+    # the slot a WARM must produce, made on the device by the fetch kernel (bit-exact
+    # with the oracle's fetch in test_gpu_vstore) and torch's relayout
+    import torch
+    from test_gpu_vstore import fetched_slot
+    kp.pion_prefix_store("f32", 6, *(fetched_slot(kp, r, src, H, D, torch.float32) for r in rows),
+                         kp.PION_KV_FP32)
     Q = inp.Q.astype(np.float32)
     a, la = q32(kp, "f32", 5, Q)
     b, lb = q32(kp, "f32", 6, Q)

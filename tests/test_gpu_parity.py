@@ -125,6 +125,29 @@ def test_quantize_hand_worked_group_and_edges(kp):
     assert [int(w) for w in got[0][0, :4]] == [int(w, 16) for w in g["words"]]
 
 
+def test_quantize_signed_zero_groups(kp):
+    # -0 orders below +0: the bias of a zero-minimum group is -0 exactly when it holds a
+    # -0, in either order of the zeros and in any lane of the group's four words
+    nz, pz = np.float16(-0.0), np.float16(0.0)
+    x = np.zeros((8, 64), np.float16)
+    x[0, 0], x[0, 1] = pz, nz                      # +0 then -0
+    x[0, 32], x[0, 63] = nz, pz                    # -0 first, +0 in the group's last word
+    x[1, :32] = nz                                 # all -0
+    x[1, 40] = nz                                  # one -0 in the third word, else +0
+    x[2, :32] = nz
+    x[2, 7] = np.float16(2.5)                      # -0 minimum, positive range
+    x[2, 32:] = np.float16(-1.0)
+    x[2, 50], x[2, 51] = nz, pz                    # zero maximum, negative minimum
+    rng = np.random.default_rng(5)
+    x[3:] = np.abs(rng.standard_normal((5, 64))).astype(np.float16)
+    x[3:, ::7] = nz                                # -0 minima among positive values
+    x[4:, 3] = pz
+    got = _quantize_gpu(kp, x)
+    ref = oracle.quantize(x)
+    _assert_same_encoding(got, ref)
+    assert list(got[2].view(np.uint16)[:2].ravel()) == [0x8000, 0x8000, 0x8000, 0x8000]
+
+
 @pytest.mark.parametrize("rows,D", [(1, 32), (3, 96), (257, 64), (1001, 128), (77, 256)])
 def test_quantize_ragged_shapes(kp, rows, D):
     rng = np.random.default_rng(rows * D)
@@ -299,7 +322,9 @@ def test_batched_query_matches_m1_rows(kp):
     check(out, lse, *oracle.prefix_query(inp.Q, inp.K, inp.V))
 
 
-def test_fused_prefill_full_size_sampled_rows(kp):
+def test_fused_prefill_full_size_all_rows(kp):
+    # the full batched-Q workload in the launch configuration the bench times (key
+    # splits and their merge kernel): every row of every q-head against the oracle
     case = synth.PREFILL
     inp = synth.generate(case)
     kp.pion_prefix_store("t", 7, dev(inp.K), dev(inp.V))
@@ -307,12 +332,8 @@ def test_fused_prefill_full_size_sampled_rows(kp):
     lse = empty((24, 512))
     kp.pion_prefix_query_fused("t", 7, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
     out, lse = host(out), host(lse)
-    rng = np.random.default_rng(0)
-    rows = [(h, i) for h in (0, 1, 2, 12, 23) for i in (0, 1, 255, 510, 511)]
-    rows += [(int(h), int(i)) for h, i in zip(rng.integers(0, 24, 40), rng.integers(0, 512, 40))]
-    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
-    check(out, lse, ref, ref_lse, rows=rows)
-    assert np.all(np.isfinite(out))
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+    check(out, lse, ref, ref_lse)
 
 
 # ------------------------------------------------------------------ mlx4g32 decode
@@ -472,19 +493,44 @@ def check_selection(blocks, Q, K, B, K_top, head_map=None):
             assert score[g, sel][worst] + bound[g, sel][worst] >= score[g, rest][best] - bound[g, rest][best]
 
 
-@pytest.mark.parametrize("N,B,K_top", [(20000, 16, 100), (70000, 16, 20)])
-def test_sparse_auto_radix_select(kp, N, B, K_top):
-    # K_top above 64, or more per-workgroup candidates than the candidate merge holds:
-    # the selection runs the radix select
-    inp = synth.generate(synth.SPARSE, 6, N=N, H_q=4, H_kv=2, D=64, S_suf=12, n_needles=2)
+def assert_unique_selection(Q, K, B, K_top, head_map=None):
+    """The oracle's K_top-th and next block scores are separated by more than ten times
+    the rounding bound of an fp32 score, so the top-K set is decided the same way in any
+    precision the kernel may use: the selection is unique by construction."""
+    H_q, _, D = Q.shape
+    H_kv = K.shape[0]
+    hm = oracle.resolve_head_map(H_q, H_kv, head_map)
+    km = oracle.block_means(K, B)
+    score = oracle.block_scores(Q[:, 0, :], km, hm)
+    bound = 2.0 ** -12 * oracle.block_scores(np.abs(Q[:, 0, :].astype(np.float64)), np.abs(km), hm)
+    for g in range(H_kv):
+        order = np.argsort(-score[g], kind="stable")
+        if K_top < len(order):
+            a, b = order[K_top - 1], order[K_top]
+            assert score[g, a] - score[g, b] > 10 * (bound[g, a] + bound[g, b])
+
+
+# K_top above 64, or more per-workgroup candidates than the candidate merge holds: the
+# selection runs the radix select. Needle blocks planted (+3 sigma along the query
+# direction, per 64-token block, so 64 / B selected blocks each) make the top K_top
+# unique by construction; the picked indices must equal the oracle's bit for bit.
+@pytest.mark.parametrize("N,B,K_top,needles",
+                         [(20000, 16, 100, 25), (70000, 16, 20, 5), (64 * 300, 64, 65, 65),
+                          (64 * 1500, 64, 1024, 1024)])
+def test_sparse_auto_radix_select(kp, N, B, K_top, needles):
+    inp = synth.generate(synth.SPARSE, 6, N=N, H_q=4, H_kv=2, D=64, S_suf=12, n_needles=needles)
+    assert needles * (synth.SPARSE.B // B) == K_top
+    assert_unique_selection(inp.Q, inp.K, B, K_top, inp.head_map)
     kp.pion_prefix_store("t", 16, dev(inp.K), dev(inp.V))
     out, lse, blocks = sparse_call(kp, "t", 16, inp, B, K_top, 2)
-    check_selection(blocks, inp.Q, inp.K, B, K_top, inp.head_map)
-    planted = synth.SPARSE.B // B  # needles are planted per 64-token block
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(
+        inp.Q, inp.K, inp.V, B, K_top, inp.head_map, inp.K_suf, inp.V_suf)
+    np.testing.assert_array_equal(blocks, ref_blocks)
+    planted = synth.SPARSE.B // B
     for g in range(2):
-        assert {planted * n + i for n in inp.needles[g] for i in range(planted)} <= set(blocks[g])
-    ref, ref_lse = oracle.prefix_query_blocks(inp.Q, inp.K, inp.V, B, blocks, inp.head_map,
-                                              inp.K_suf, inp.V_suf)
+        want = sorted(planted * n + i for n in inp.needles[g] for i in range(planted))
+        np.testing.assert_array_equal(ref_blocks[g], want)
+    check_selection(blocks, inp.Q, inp.K, B, K_top, inp.head_map)
     check(out, lse, ref, ref_lse)
 
 
@@ -735,9 +781,7 @@ def test_query_sparse_bench_shape(kp):
 def test_vstore_fetch_bench_shape(kp):
     # one layer-side of the V-store bench workload: N = 2048 tokens, kv = 8 x 128, records
     from oracle import vstore as ovs
-    inp = synth.generate(synth.DECODE, 31, N=2048, D=128, H_q=8, H_kv=8)
-    rows = np.ascontiguousarray(inp.V.transpose(1, 0, 2).reshape(2048, 1024))
-    rec = ovs.pack_records(*oracle.quantize(rows))
+    rec = synth.mlx4_records(2048, 1024, 31)
     assert rec.shape == (2048, 640)
     out = empty((2048, 1024))
     kp.pion_vstore_fetch_f32(dev(rec), ovs.MLX4G32, 1024, 0, 2048, out)

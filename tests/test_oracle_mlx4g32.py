@@ -57,7 +57,73 @@ def test_dequant_error_at_most_half_a_step(D):
     assert np.max(np.abs(xh - xd) / s) > 0.49
 
 
+def _fl(v: Fraction, mant: int, emin: int) -> Fraction:
+    """v rounded to the binary format with `mant` fraction bits and minimum normal
+    exponent `emin`, nearest with ties to even (gradual underflow below 2^emin)."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, emin) - mant)
+    r = round(a / quantum) * quantum        # Fraction.__round__: half to even
+    return r if v > 0 else -r
+
+
+def fl32(v):
+    return _fl(v, 23, -126)
+
+
+def fl16(v):
+    r = _fl(v, 10, -14)
+    assert abs(r) <= 65504
+    return r
+
+
+def _model_group(xs):
+    """The encoder's steps on one group of fp16 values, each fp32 / fp16 operation
+    rounded by hand from exact rationals: mn, mx exact; s32 = fl32(fl32(mx - mn) / 15);
+    s = fl16(s32); b = fl16(mn); t_j = fl32(fl32(x_j - b) / s); q_j = clamp(rint(t_j)).
+    Returns (codes, s, b) as rationals (codes a list of ints)."""
+    fx = [Fraction(float(v)) for v in xs]
+    mn, mx = min(fx), max(fx)
+    s = fl16(fl32(fl32(mx - mn) / 15))
+    b = fl16(mn)
+    if s == 0:
+        return [0] * len(fx), s, b
+    codes = []
+    for v in fx:
+        t = fl32(fl32(v - b) / s)
+        codes.append(min(max(round(t), 0), 15))
+    return codes, s, b
+
+
+def _near_tie_groups(n, seed):
+    """Groups whose quotients (x - b) / s lie on, or one fp16 step either side of, the
+    half-integers k + 0.5 for random fp16 scales: where any other fp32 evaluation order
+    than (x - b) / s, or a product with 1 / s, can round to the other code."""
+    rng = np.random.default_rng(seed)
+    s = (2.0 ** rng.integers(-12, 6, n)) * rng.choice([1.0, 1.5, 1.25, 1.75, 1.375, 3.0 / 7], n)
+    base = -rng.integers(0, 40, n) * s * (np.arange(n) % 2)   # bias 0 or -j s
+    x = np.zeros((n, 32), np.float64)
+    x[:, 0] = base
+    x[:, 1] = base + 15.0 * s
+    x[:, 2:] = base[:, None] + (rng.integers(0, 15, (n, 30)) + 0.5) * s[:, None]
+    x16 = x.astype(np.float16)
+    step = rng.integers(-1, 2, x16[:, 2:].shape)
+    x16[:, 2:] = np.where(step < 0, np.nextafter(x16[:, 2:], np.float16(-np.inf)),
+                          np.where(step > 0, np.nextafter(x16[:, 2:], np.float16(np.inf)),
+                                   x16[:, 2:]))
+    return x16
+
+
 def test_each_code_is_the_nearest_level_brute_force():
+    # the mathematical pin: every code is the level nearest x (ties to even), except
+    # where the fp32 quotient lies within its rounding error of a half-integer; there the
+    # exact-rational model of the fp32 steps below decides
     x = _groups(300, 64, 7)
     codes, s16, b16 = oracle.quantize(x)
     q = oracle.unpack_codes(codes, 64).reshape(300, 2, 32)
@@ -84,6 +150,73 @@ def test_each_code_is_the_nearest_level_brute_force():
                     assert c == cands[0]
                 checked += 1
     assert checked > 15000
+
+
+@pytest.mark.parametrize("kind", ["random", "near_tie", "subnormal"])
+def test_encoding_equals_exact_rational_model_of_the_fp32_steps(kind):
+    # every element, near-ties included: codes, scale and bias equal a model that rounds
+    # each fp32 (and fp16) operation by hand from exact rationals, so the op order
+    # (x - b) / s with a correctly rounded divide is pinned, not only numpy's float32
+    if kind == "random":
+        x = _groups(160, 32, 21)
+    elif kind == "near_tie":
+        x = _near_tie_groups(400, 22)
+    else:
+        rng = np.random.default_rng(23)
+        x = (rng.standard_normal((160, 32)) * 2.0 ** -16).astype(np.float16)
+    codes, s16, b16 = oracle.quantize(x)
+    q = oracle.unpack_codes(codes, 32)
+    near = 0
+    for r in range(len(x)):
+        mc, ms, mb = _model_group(x[r])
+        assert Fraction(float(s16[r, 0])) == ms and Fraction(float(b16[r, 0])) == mb, r
+        assert list(q[r]) == mc, r
+        if ms != 0:
+            for v in x[r]:
+                t = (Fraction(float(v)) - mb) / ms
+                near += abs(abs(t - round(t)) - Fraction(1, 2)) < Fraction(1, 2 ** 18)
+    if kind == "near_tie":
+        assert near > 3000   # the window the nearest-level pin leaves to this model
+
+
+def test_model_rounds_like_ieee_binary32():
+    # the hand rounding itself: against exactly known binary32 results
+    assert fl32(Fraction(1, 3)) == Fraction(float(np.float32(1) / np.float32(3)))
+    assert fl32(Fraction(1) + Fraction(1, 2 ** 24)) == 1                    # tie -> even
+    assert fl32(Fraction(1) + Fraction(3, 2 ** 24)) == 1 + Fraction(1, 2 ** 22)
+    assert fl32(Fraction(1, 2 ** 150)) == 0 and fl32(Fraction(3, 2 ** 150)) == Fraction(1, 2 ** 148)
+    assert fl16(Fraction(1, 3)) == Fraction(float(np.float16(1 / 3)))
+    assert fl16(Fraction(3, 2 ** 26)) == Fraction(1, 2 ** 24)                # subnormal
+
+
+def test_signed_zero_minimum_and_maximum():
+    # -0 orders below +0: a zero minimum is -0 (bias bits 0x8000) if the group holds a -0,
+    # whichever zero comes first; an all-zero group has scale +0 and all codes 0
+    nz, pz = np.float16(-0.0), np.float16(0.0)
+    x = np.zeros((6, 32), np.float16)
+    x[0, 0], x[0, 1] = pz, nz            # +0 then -0
+    x[1, 0], x[1, 1] = nz, pz            # -0 then +0
+    x[2, :] = nz                         # all -0
+    x[3, :] = pz                         # all +0
+    x[4, :] = nz
+    x[4, 7] = np.float16(2.5)            # -0 minimum with a positive range
+    x[5, :] = np.float16(-1.0)
+    x[5, 9], x[5, 10] = nz, pz           # zero maximum, negative minimum
+    codes, s16, b16 = oracle.quantize(x)
+    assert list(b16.view(np.uint16)[:, 0]) == [0x8000, 0x8000, 0x8000, 0x0000, 0x8000, 0xBC00]
+    assert list(s16.view(np.uint16)[:, 0][:4]) == [0, 0, 0, 0]
+    assert np.all(codes[:4] == 0)
+    assert float(s16[4, 0]) == float(np.float16(np.float32(2.5) / np.float32(15)))
+    xh = oracle.dequantize(codes, s16, b16)
+    assert np.all(np.abs(xh - x.astype(np.float64)) <= s16.astype(np.float64).repeat(32, 1) / 2)
+
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_non_finite_input_is_rejected(bad):
+    x = np.zeros((2, 32), np.float16)
+    x[1, 4] = bad
+    with pytest.raises(ValueError):
+        oracle.quantize(x)
 
 
 def test_constant_group_has_zero_scale_and_zero_codes():
