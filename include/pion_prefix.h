@@ -69,7 +69,9 @@ enum {
     PION_ERR_NOMEM = -4,       /* device memory short with nothing left to demote, or
                                   a slot larger than the byte budget */
     PION_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
-    PION_ERR_COLDMISS = -6     /* the key was demoted to the cold tier: store it again */
+    PION_ERR_COLDMISS = -6,    /* the key was demoted to the cold tier: store it again */
+    PION_ERR_SCRATCH = -7      /* pion_prefix_query_noalloc: the call needs more scratch
+                                  than the fixed area holds (nothing was launched) */
 };
 
 /* Resident formats. FP16 keeps K and V as given. MLX4G32 is the int4 group-32 affine
@@ -144,6 +146,25 @@ int pion_prefix_set_capacity(int64_t max_slots, int64_t max_bytes, int64_t cold_
 int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M,
                       const void *Q, const int32_t *head_map,
                       float *out, float *lse, void *stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * pion_prefix_query (the same kernels run), but every device buffer the launch plan
+ * needs beyond the caller's Q, out, lse and the resident slot - the split-over-keys
+ * partials and the merge's ticket counters - lives in a fixed scratch area the library
+ * holds per GPU for the life of the process: 64 MiB (256 KiB of counters, the rest
+ * partials). The call performs no device allocation or free. The first call on a device
+ * takes that device's scratch address and clears its counters with a kernel on `stream`.
+ *   Limit: a plan whose partials exceed the area returns PION_ERR_SCRATCH before any
+ *   launch (pion_prefix_query serves it). The partials of a plan are at most
+ *   H_q * M * D * 4 bytes times its key splits: the H_q = 24, N = 4096, M = 512, D = 128
+ *   batched-Q query needs 32 MB and fits; H_q = 64, M = 512 at D = 512 (67 MB) does not.
+ *   Every call on one GPU shares its scratch area and the area keeps the last call's
+ *   contents: calls that overlap in time on one GPU (different streams, or host
+ *   threads racing) race on it. Calls ordered on one stream are safe. */
+int pion_prefix_query_noalloc(const char *sid, int layer, int H_q, int D, int M,
+                              const void *Q, const int32_t *head_map,
+                              float *out, float *lse, void *stream);
 
 /* Batched form of pion_prefix_query over the layers layer0 .. layer0 + n_layers - 1 of
  * one session, computed in a single launch. Not a wire form of the pages: it issues the

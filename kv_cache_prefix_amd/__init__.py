@@ -20,6 +20,7 @@ PION_ERR_UNSUPPORTED = -3
 PION_ERR_NOMEM = -4
 PION_ERR_HIP = -5
 PION_ERR_COLDMISS = -6
+PION_ERR_SCRATCH = -7
 PION_KV_FP16 = 0
 PION_KV_MLX4G32 = 1
 PION_KV_FP32 = 2
@@ -36,6 +37,8 @@ SIGNATURES = {
     "pion_prefix_stats": (_int, [_vp]),
     "pion_prefix_set_capacity": (_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "pion_prefix_query": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp, _vp]),
+    "pion_prefix_query_noalloc": (_int, [_c_char_p, _int, _int, _int, _int, _vp, _vp, _vp, _vp,
+                                         _vp]),
     "pion_prefix_query_layers": (_int, [_c_char_p, _int, _int, _int, _int, _int, _vp, _vp, _vp,
                                         _vp, _vp]),
     "pion_prefix_query_fused": (_int, [_c_char_p, _int, _int, _int, _int, _int, _int,

@@ -215,6 +215,16 @@ hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, u
 // nothing else (the streaming-read ceiling); sink receives at most one word.
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
 
+// Ticket counters of a workspace: one per workgroup row of a split launch.
+constexpr int kMaxCounters = 65536;
+
+// The fixed scratch of pion_prefix_query_noalloc: kMaxCounters ticket counters, then the
+// split partials. noalloc_scratch returns this device's copy (its address taken once per
+// device, the counters cleared on `s` at that first call).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+constexpr size_t kNoallocCounterBytes = (size_t)kMaxCounters * 4;
+hipError_t noalloc_scratch(hipStream_t s, void **ptr);
+
 // Zero the ticket counters of a fresh workspace.
 hipError_t launch_zero_counters(int *counters, int n, hipStream_t s);
 

@@ -77,7 +77,6 @@ struct Workspace {
   int *counters = nullptr;  // ticket counters of the split merge, kMaxCounters ints
 };
 
-constexpr int kMaxCounters = 65536;  // one per workgroup row (grid.y <= 65535)
 
 // A demoted slot: its shape and last access (the K/V bytes are gone).
 struct ColdEntry {
@@ -236,10 +235,24 @@ hipError_t order_after(hipEvent_t ev, hipStream_t src, bool &done, hipStream_t s
   return hipStreamWaitEvent(st, ev, 0);
 }
 
+// Set by pion_prefix_query_noalloc for the duration of its call (under g_mu): the launch
+// plan's workspace then comes from the fixed scratch area, never from hipMalloc.
+struct FixedScratch {
+  char *base = nullptr;     // split partials
+  size_t bytes = 0;
+  int *counters = nullptr;  // kMaxCounters zeroed ticket counters
+  bool too_small = false;   // a request exceeded `bytes`
+};
+FixedScratch *g_fixed = nullptr;
+
 // Per-stream scratch for the split partials, plus the zeroed ticket counters (the
 // merging workgroup resets its counter, so they stay zero between calls). Grows by
 // reallocating after the stream has drained; never shrinks.
 hipError_t get_counters(hipStream_t st, int **out) {
+  if (g_fixed) {
+    *out = g_fixed->counters;
+    return hipSuccess;
+  }
   Workspace &w = g_ws[st];
   if (!w.counters) {
     hipError_t e = hipMalloc(&w.counters, kMaxCounters * sizeof(int));
@@ -256,6 +269,14 @@ hipError_t get_counters(hipStream_t st, int **out) {
 }
 
 hipError_t get_ws(hipStream_t st, size_t bytes, void **out) {
+  if (g_fixed) {
+    if (bytes > g_fixed->bytes) {
+      g_fixed->too_small = true;
+      return hipErrorOutOfMemory;
+    }
+    *out = g_fixed->base;
+    return hipSuccess;
+  }
   Workspace &w = g_ws[st];
   int *cnt;
   if (hipError_t e = get_counters(st, &cnt); e != hipSuccess) return e;
@@ -524,7 +545,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   p.part_acc = (float *)ws;
   p.part_m = (float *)((char *)ws + acc_bytes);
   p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
-  p.counters = g_ws[st].counters;
+  if (get_counters(st, &p.counters) != hipSuccess) return PION_ERR_NOMEM;
 
   hipError_t e;
   if (mlx4) {
@@ -691,6 +712,47 @@ int check_query_args(const char *sid, int H_q, int D, int M, const void *Q, cons
 thread_local std::string g_plan;
 void plan_begin() { g_plan.clear(); }
 
+// pion_prefix_query, with the plan's workspace from the fixed scratch when `fixed`.
+int query_one(const char *sid, int layer, int H_q, int D, int M, const void *Q,
+              const int32_t *head_map, float *out, float *lse, void *stream, bool fixed) {
+  plan_begin();
+  int rc = check_query_args(sid, H_q, D, M, Q, out);
+  if (rc != PION_OK) return rc;
+  if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Slot *sl = find_slot(sid, layer);
+  if (!sl) return absent_status(sid, layer);
+  if (sl->D != D) return PION_ERR_INVALID;
+  std::vector<int> hm;
+  if (!resolve_map(head_map, H_q, sl->H, hm)) return PION_ERR_INVALID;
+  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
+  AttnCall c{};
+  c.Q = Q;
+  c.H_q = H_q;
+  c.M = M;
+  c.D = D;
+  c.hm = &hm;
+  c.H_kv = sl->H;
+  c.out = out;
+  c.lse = lse;
+  FixedScratch fx;
+  if (fixed) {
+    void *scr = nullptr;
+    if (noalloc_scratch(st, &scr) != hipSuccess) return PION_ERR_HIP;
+    fx.counters = (int *)scr;
+    fx.base = (char *)scr + kNoallocCounterBytes;
+    fx.bytes = kNoallocScratchBytes - kNoallocCounterBytes;
+    g_fixed = &fx;
+  }
+  rc = run_attention({sl}, c, st);
+  g_fixed = nullptr;
+  if (fx.too_small) return PION_ERR_SCRATCH;
+  if (rc == PION_OK) touch(sl);
+  return rc;
+}
+
 }  // namespace
 
 namespace pion {
@@ -728,6 +790,7 @@ const char *pion_status_str(int status) {
     case PION_ERR_NOMEM: return "out of memory";
     case PION_ERR_HIP: return "HIP error";
     case PION_ERR_COLDMISS: return "cold miss";
+    case PION_ERR_SCRATCH: return "exceeds the fixed scratch area";
     default: return "unknown status";
   }
 }
@@ -921,31 +984,12 @@ int pion_prefix_set_capacity(int64_t max_slots, int64_t max_bytes, int64_t cold_
 
 int pion_prefix_query(const char *sid, int layer, int H_q, int D, int M, const void *Q,
                       const int32_t *head_map, float *out, float *lse, void *stream) {
-  plan_begin();
-  int rc = check_query_args(sid, H_q, D, M, Q, out);
-  if (rc != PION_OK) return rc;
-  if (lse && !aligned(lse, 4)) return PION_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(g_mu);
-  Slot *sl = find_slot(sid, layer);
-  if (!sl) return absent_status(sid, layer);
-  if (sl->D != D) return PION_ERR_INVALID;
-  std::vector<int> hm;
-  if (!resolve_map(head_map, H_q, sl->H, hm)) return PION_ERR_INVALID;
-  if (!on_device(Q) || !on_device(out) || (lse && !on_device(lse))) return PION_ERR_INVALID;
-  hipStream_t st = (hipStream_t)stream;
-  if (order_after(sl->ready, sl->stream, sl->done, st) != hipSuccess) return PION_ERR_HIP;
-  AttnCall c{};
-  c.Q = Q;
-  c.H_q = H_q;
-  c.M = M;
-  c.D = D;
-  c.hm = &hm;
-  c.H_kv = sl->H;
-  c.out = out;
-  c.lse = lse;
-  rc = run_attention({sl}, c, st);
-  if (rc == PION_OK) touch(sl);
-  return rc;
+  return query_one(sid, layer, H_q, D, M, Q, head_map, out, lse, stream, false);
+}
+
+int pion_prefix_query_noalloc(const char *sid, int layer, int H_q, int D, int M, const void *Q,
+                              const int32_t *head_map, float *out, float *lse, void *stream) {
+  return query_one(sid, layer, H_q, D, M, Q, head_map, out, lse, stream, true);
 }
 
 int pion_prefix_query_layers(const char *sid, int layer0, int n_layers, int H_q, int D, int M,

@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -43,6 +43,14 @@ def test_last_plan_and_stream_read_without_a_gpu(lib):
     assert lib.pion_bench_stream_read(None, 17, None, None) == kp.PION_ERR_INVALID
     assert lib.pion_bench_stream_read(None, 0, None, None) == kp.PION_OK
     assert kp.pion_prefix_last_plan() == ""
+
+
+def test_noalloc_query_argument_validation(lib):
+    # the same host checks as pion_prefix_query, before the scratch area is touched
+    q = lib.pion_prefix_query_noalloc
+    assert q(None, 0, 8, 128, 1, None, None, None, None, None) == kp.PION_ERR_INVALID
+    assert q(b"x", 0, 8, 100, 1, None, None, None, None, None) == kp.PION_ERR_INVALID
+    assert kp.status_str(kp.PION_ERR_SCRATCH) == "exceeds the fixed scratch area"
 
 
 def test_status_strings(lib):
