@@ -188,7 +188,7 @@ struct PrefillParams {
   int H_q, M, D, H_kv, N, S_suf;
   float qscale;                   // log2(e) / sqrt(D)
   int n_iblk;                     // ceil(M / 128)
-  int n_splits, split_keys;       // split_keys a multiple of 64
+  int n_splits, split_keys;       // split_keys a multiple of 32
   float *out, *lse;
   float *part_acc, *part_m, *part_l;  // split partials (n_splits > 1)
   HeadMap hm;

@@ -416,9 +416,9 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   const long long slots = c.D <= 128 ? 512 : 256;
   long long ns = std::max<long long>(1, slots / tiles);
   if (const char *e = getenv("PION_PREFILL_SPLITS")) ns = std::max(1, atoi(e));
-  ns = std::min<long long>(ns, std::min<long long>(16, (total + 63) / 64));
+  ns = std::min<long long>(ns, std::min<long long>(16, (total + 31) / 32));
   long long sk = (total + ns - 1) / ns;
-  sk = (sk + 63) / 64 * 64;
+  sk = (sk + 31) / 32 * 32;
   if (sk > (1LL << 30)) return PION_ERR_UNSUPPORTED;
   p.split_keys = (int)sk;
   p.n_splits = (int)((total + sk - 1) / sk);

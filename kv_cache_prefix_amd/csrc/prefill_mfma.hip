@@ -52,7 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;
 constexpr int BQ = 128;   // query rows per workgroup
-constexpr int BK = 64;    // keys per tile
+constexpr int BK = 32;    // keys per tile
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMergeChunk = 8;  // splits whose partials the merge loads per round
 
@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t part_off(int c, int w, int db, int i, int la
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
-constexpr int NSTAGE = 2;  // LDS tile stages (loads run NSTAGE - 1 tiles ahead)
+constexpr int NSTAGE = 4;  // LDS tile stages (tile t + 3 loads while tile t is in use)
 
 // LDS dims per key row: D rounded up to a power of two, at least 64
 template <int D>
@@ -89,6 +89,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+
+// The rows of a 128-row block (q-head h, block ib) that wave `wave` (0..3) holds:
+// normalized out and lse when the keys are not split; else the split partial: acc
+// unnormalized against m_run, in the register layout of o (tile, split, wave, 32-dim
+// block db, quad i, lane: one 16-byte piece per lane, so every store instruction moves
+// 1 KB of consecutive bytes); m and l (log2 units) per [row][split]. prefill_merge_kernel,
+// next on the stream, combines the splits.
+template <int D>
+__device__ __forceinline__ void store_rows(const PrefillParams &p, const f16v (&o)[D / 32],
+                                           float m_run, float l_run, int h, int ib, int split,
+                                           int wave, int lane) {
+  constexpr int NDB = D / 32;
+  const int hl = lane >> 5, col = lane & 31;
+  const int i0 = ib * BQ;
+  const int qi = i0 + wave * 32 + col;
+  const int tile = h * p.n_iblk + ib;
+  if (p.n_splits == 1) {
+    if (qi < p.M) {
+      const size_t row = (size_t)h * p.M + qi;
+      const float inv = 1.f / l_run;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4 v = make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv,
+                                 o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+          *(float4 *)(p.out + row * D + 32 * db + 8 * i + 4 * hl) = v;
+        }
+      if (hl == 0 && p.lse) p.lse[row] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
+    }
+    return;
+  }
+  const int S = p.n_splits;
+  const int rows_valid = min(BQ, p.M - i0);
+  const size_t row0 = (size_t)h * p.M + i0;
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
+  const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
+                                             part_off<NDB>(split, wave, db, i, lane), 0, 0);
+    }
+  if (hl == 0) {
+    const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM, (r * S + split) * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL, (r * S + split) * 4, 0, 0);
+  }
+}
+
+// Instruction-group hints for the scheduler (masks of the AMDGPU backend's
+// sched_group_barrier: MFMA, VALU, DS read).
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
 
 template <int D>
 __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(PrefillParams p) {
@@ -127,7 +185,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const int k_stop = min(k_end, lim_wg);
   const int lim_row = p.S_suf > 0 ? p.N + p.S_suf - p.M + qi_c + 1 : p.N;
   const int row_end = min(k_end, lim_row);
-  // 32-key sub-tiles ending at or below this need no mask for any row of the workgroup
+  // key tiles ending at or below this need no mask for any row of the workgroup
   const int lim_first = p.S_suf > 0 ? p.N + p.S_suf - p.M + i0 + 1 : p.N;
   const int full_end = min(k_end, lim_first);
 
@@ -139,7 +197,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const i32x4 rVs =
       rsrc_words(has_suf ? p.Vsuf + (size_t)g * p.S_suf * D : p.V, (uint32_t)p.S_suf * ROWG);
 
-  // Tiles never straddle the prefix / suffix boundary: the split's prefix part
+  // Tiles of BK keys never straddle the prefix / suffix boundary: the split's prefix part
   // [k_begin, pre_end) is tiled from k_begin, its suffix part [suf_beg, k_stop) from
   // suf_beg. Tile j < n_pre is prefix, the rest suffix.
   const int pre_end = min(k_stop, p.N);
@@ -172,6 +230,13 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       load_lds16(rv, (uint32_t)r0 * ROWG + voff[t], st + TB + 1024 * t);
     }
   };
+  // Tile j's first key in the concatenated index, its segment's end, this row's limit
+  // inside it, and the end of the keys every row of the workgroup sees
+  auto tile_t0 = [&](int j) { return j >= n_pre ? suf_beg + (j - n_pre) * BK : k_begin + j * BK; };
+  auto tile_clean = [&](int j) {
+    return j >= n_pre ? tile_t0(j) + BK <= min(k_stop, full_end) : tile_t0(j) + BK <= pre_end;
+  };
+  auto tile_lane_end = [&](int j) { return j >= n_pre ? row_end : pre_end; };
 
   for (int j = 0; j < NSTAGE - 1 && j < n_tiles; ++j) issue(j);
   half8 qb[NDS];
@@ -184,6 +249,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   // outstanding in the loop, where any vmcnt wait it added would also drain the loads
   // of the next tiles
   __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   f16v o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -191,11 +257,11 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
 
-  // Operand addresses inside a stage, as loop-invariant lane offsets (the stage and
-  // sub-tile parts are immediates): K row 32 kb + col at logical chunk 2 ds + hl; V^T
-  // via transposed reads: lane (group gq, index q) addresses row kbase + q/4 at dims
-  // 32 db + 16 gq + 4 (q%4), for kbase = 32 kb + 16 s2 + 4 hl + 8 c (c = 0, 1: the two
-  // runs of 4 keys of a 16-key k-step); the swizzle of those rows depends on q, hl, c.
+  // Operand addresses inside a stage, as loop-invariant lane offsets (the stage part is
+  // an immediate): K row col at logical chunk 2 ds + hl; V^T via transposed reads: lane
+  // (group gq, index q) addresses row kbase + q/4 at dims 32 db + 16 gq + 4 (q%4), for
+  // kbase = 16 s2 + 4 hl + 8 c (c = 0, 1: the two runs of 4 keys of a 16-key k-step);
+  // the swizzle of those rows depends on q, hl, c.
   const char *smb = &sm.kv[0][0][0];
   uint32_t koff[NDS];
   {
@@ -218,7 +284,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
                        (uint32_t)(((4 * db + vch) ^ vsw) << 4);
     }
   }
-  auto kfrag = [&](int base, int ds) {  // base: byte offset of the 32-key sub-tile in LDS
+  auto kfrag = [&](int base, int ds) {  // base: byte offset of the K tile in LDS
     return __builtin_bit_cast(half8, *(const uint4 *)(smb + base + koff[ds]));
   };
   auto vfrag = [&](int base, int db) {  // base: byte offset of the 16-key k-step in LDS
@@ -230,75 +296,82 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     return half8{part[0][0], part[0][1], part[0][2], part[0][3],
                  part[1][0], part[1][1], part[1][2], part[1][3]};
   };
-  constexpr int KR = NDS < 4 ? NDS : 4;  // K fragments in flight ahead of their product
 
-  // One 64-key tile from LDS stage STG (a compile-time constant, so every operand
-  // address is a lane offset plus an immediate).
-  auto run_tile = [&](auto stg, int j) {
-    constexpr int STG = decltype(stg)::value;
-    const bool suf = j >= n_pre;
-    const int t0 = suf ? suf_beg + (j - n_pre) * BK : k_begin + j * BK;  // concatenated index
-    const int seg_end = suf ? k_stop : pre_end;   // keys at or past this are not in the tile
-    const int lane_end = suf ? row_end : pre_end; // this row's limit inside the tile
-    const int clean_end = suf ? min(k_stop, full_end) : pre_end;  // no mask below this
-    // this wave's loads of tile j are done (later tiles' loads may stay in flight) ...
-    if (NSTAGE > 2 && j + 1 < n_tiles)
-      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD * (NSTAGE > 2 ? NSTAGE - 2 : 0)) : "memory");
-    else
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // ... and every wave's; every wave is also done reading the stage loaded next
-    __syncthreads();
-    if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
-    // Two workgroups on a CU share its SIMDs; the arbiter favours the older waves, so one
-    // would run ahead and the other finish alone at the end. Priority falls with the tiles
-    // left, so the one behind catches up and both end together.
-    {
-      const int rem = n_tiles - j;
-      if (rem > 8) __builtin_amdgcn_s_setprio(3);
-      else if (rem > 4) __builtin_amdgcn_s_setprio(2);
-      else if (rem > 2) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
+  // S^T of tile j from stage STG: result element (i, jj) of lane l is key 8 i + 4 (l / 32)
+  // + jj of the tile, query row l % 32
+  auto s_product = [&](auto stg) {
+    constexpr int KB = decltype(stg)::value * 2 * TB;
+    half8 kf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = kfrag(KB, ds);
+    f16v s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds], qb[ds], s, 0, 0, 0);
+    return s;
+  };
+  // Two workgroups on a CU share its SIMDs; the arbiter favours the older waves, so one
+  // would run ahead and the other finish alone at the end. Priority falls with the tiles
+  // left, so the one behind catches up and both end together.
+  auto set_prio = [&](int rem) {
+    if (rem > 16) __builtin_amdgcn_s_setprio(3);
+    else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+    else if (rem > 4) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Software pipeline over key tiles, three tiles deep: iteration j runs the PV product of
+  // tile j - 1, the softmax weights of tile j and the S^T product of tile j + 1 - three
+  // independent pieces of work, so the exponentials of one tile overlap the matrix
+  // products of two others. Carried between iterations: S^T of tile j (s_cur), and the
+  // fp16 weights and V^T operands of tile j - 1 (pb_prev, vf). Tile j sits in stage
+  // j % NSTAGE (a compile-time constant in each unrolled copy of the body).
+  f16v s_cur;
+  half8 pb_prev[2];
+  half8 vf[2][NDB];
+  if (D <= 128 && n_tiles > 0) s_cur = s_product(std::integral_constant<int, 0>());
+  // stg: the stage of tile j, an integral_constant in the unrolled main loop (every LDS
+  // offset an immediate) or an int for the few tiles after it; has_prev / has_next: bool
+  // constants (tile j - 1's product pending; tile j + 1 exists)
+  auto step = [&](auto stg, int j, auto has_prev_c, auto has_next_c) {
+    constexpr bool has_prev = decltype(has_prev_c)::value;
+    constexpr bool has_next = decltype(has_next_c)::value;
+    const int STG = stg;
+    const int VB = STG * 2 * TB + TB;
+    const int KBN = ((STG + 1) & (NSTAGE - 1)) * 2 * TB;
+    if (has_next) {
+      // this wave's loads of tile j + 1 are done (tile j + 2's may stay in flight) ...
+      if (j + 2 < n_tiles)
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
+      else
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // ... and every wave's; every wave is also done with tile j - 1 (its V^T operands
+      // are in registers), whose stage tile j + 3 fills
+      __syncthreads();
+      if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
+      set_prio(n_tiles - j);
     }
-    constexpr int KB = STG * 2 * TB, VB = KB + TB;  // stage offsets of K and V
-
-    // two 32-key sub-tiles: S^T, softmax, PV
+    // Tile j: mask (boundary tiles only), raw row max scaled to log2 units, lazy rescale:
+    // the running max moves only when the tile's max exceeds it by more than
+    // kRescaleSlack; then O, l and the pending weights of tile j - 1 are scaled
+    // (wave-uniform branch, rare after the first tiles).
+    if (!tile_clean(j)) {
+      const int kt0 = tile_t0(j), lane_end = tile_lane_end(j);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kt0 = t0 + 32 * kb;
-      if (kt0 >= seg_end) break;  // workgroup-uniform
-      f16v s;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      half8 kf[KR];
+        for (int jj = 0; jj < 4; ++jj)
+          if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s_cur[4 * i + jj] = -INFINITY;
+    }
+    {
+      float mt = fmaxf(s_cur[0], s_cur[1]);  // raw-score max; the scale is positive
 #pragma unroll
-      for (int ds = 0; ds < KR; ++ds) kf[ds] = kfrag(KB + 32 * kb * (int)ROWB, ds);
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds % KR], qb[ds], s, 0, 0, 0);
-        if (ds + KR < NDS) kf[ds % KR] = kfrag(KB + 32 * kb * (int)ROWB, ds + KR);
-      }
-      // the V^T fragments of both 16-key k-steps load while the softmax runs; the
-      // scheduling barrier keeps the compiler from sinking the loads to their products,
-      // where the wait for LDS would stall the wave
-      half8 vf[NDB], vf2[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) vf[db] = vfrag(VB + 32 * kb * (int)ROWB, db);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) vf2[db] = vfrag(VB + (32 * kb + 16) * (int)ROWB, db);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt0 + 32 > clean_end) {  // boundary sub-tile: mask keys past this row's limit
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
-      }
-      float mt = -INFINITY;  // raw-score max; the scale is positive
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[e]);
+      for (int e = 2; e < 16; ++e) mt = fmaxf(mt, s_cur[e]);
       mt = max_xor32(mt) * p.qscale;
       const bool grow = mt > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rare after the first tiles
+      if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? mt : m_run;
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
@@ -307,74 +380,178 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        if (has_prev) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb_prev[k][e] = (_Float16)((float)pb_prev[k][e] * alpha);
+        }
       }
-      half8 pb[2];
+    }
+    // The three products and the weights, as one straight-line block: reads of K (tile
+    // j + 1) start first, the PV product of tile j - 1 and the weights of tile j run
+    // while they are in flight, then the V^T reads of tile j and the S^T product of tile
+    // j + 1; the scheduling groups space the matrix products by vector ops and reads.
+    constexpr int KR = NDS < 4 ? NDS : 4;  // K fragments in flight ahead of their product
+    half8 kf[KR];
+    if (has_next) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pf = fast_exp2(__builtin_fmaf(s[e], p.qscale, -m_run));  // masked: 0
-        l_run += pf;                       // row sum from the fp32 weights
-        pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
+      for (int ds = 0; ds < KR; ++ds) kf[ds] = kfrag(KBN, ds);
+    }
+    if (has_prev) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[k][db], pb_prev[k], o[db], 0, 0, 0);
+    }
+    half8 pb[2];
+    float lsum[4];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pf = fast_exp2(__builtin_fmaf(s_cur[e], p.qscale, -m_run));  // masked: 0
+      lsum[e & 3] = e < 4 ? pf : lsum[e & 3] + pf;
+      pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
+    }
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf[k][db] = vfrag(VB + 16 * k * (int)ROWB, db);
+    if (has_next) {
+      f16v s_nxt;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_nxt[e] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds % KR], qb[ds], s_nxt, 0, 0, 0);
+        if (ds + KR < NDS) kf[ds % KR] = kfrag(KBN, ds + KR);
       }
+      s_cur = s_nxt;
+    }
+    // the weights and row sum of tile j are due in this block (left alone, the compiler
+    // sinks them to the next iteration, after the matrix products, serializing the two)
+    __asm__ volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
+    pb_prev[0] = pb[0];
+    pb_prev[1] = pb[1];
+    if (has_prev && has_next) {
+      constexpr int NRD = NDS - KR + 4 * NDB;  // reads after the first K fragments
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, KR, 0);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pb[0], o[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf2[db], pb[1], o[db], 0, 0, 0);
+      for (int i = 0; i < NDS + 2 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NRD + NDS + 2 * NDB - 1) / (NDS + 2 * NDB), 0);
+      }
     }
   };
-
-  for (int j = 0; j < n_tiles; j += NSTAGE) {
-    run_tile(std::integral_constant<int, 0>(), j);
-    if (j + 1 < n_tiles) run_tile(std::integral_constant<int, 1>(), j + 1);
-    if constexpr (NSTAGE > 2)
-      if (j + 2 < n_tiles) run_tile(std::integral_constant<int, 2>(), j + 2);
-  }
-  l_run = sum_xor32(l_run);
-
-  const bool row_ok = qi < p.M;
-  const size_t row = (size_t)h * p.M + qi_c;
-  if (p.n_splits == 1) {
-    if (row_ok) {
-      const float inv = 1.f / l_run;
+  // Head dims above 128 hold twice the accumulators and operands: there the tiles run one
+  // after the other (S^T, softmax and PV of tile j in iteration j), which fits the
+  // registers without spilling.
+  auto step_seq = [&](auto stg, int j) {
+    constexpr int STG = decltype(stg)::value;
+    constexpr int KB = STG * 2 * TB, VB = KB + TB;
+    if (j > 0) {
+      // this wave's loads of tile j are done (those of the up to two tiles issued after
+      // it may stay in flight), then every wave's
+      static_assert(NSTAGE - 2 == 2, "two tiles load ahead of the one in use");
+      if (j + 2 < n_tiles)
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NLD) : "memory");
+      else if (j + 1 < n_tiles)
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
+      else
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
+    set_prio(n_tiles - j);
+    f16v s = s_product(stg);
+    if (!tile_clean(j)) {
+      const int kt0 = tile_t0(j), lane_end = tile_lane_end(j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
+    }
+    float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int e = 2; e < 16; ++e) mt = fmaxf(mt, s[e]);
+    mt = max_xor32(mt) * p.qscale;
+    const bool grow = mt > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float4 v = make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv,
-                                 o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-          *(float4 *)(p.out + row * D + 32 * db + 8 * i + 4 * hl) = v;
-        }
-      if (hl == 0 && p.lse) p.lse[row] = (m_run + __log2f(l_run)) * 0.69314718055994530942f;
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     }
-    return;
+    half8 vv[2][NDB];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vv[k][db] = vfrag(VB + 16 * k * (int)ROWB, db);
+    half8 pb[2];
+    float lsum[4];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pf = fast_exp2(__builtin_fmaf(s[e], p.qscale, -m_run));
+      lsum[e & 3] = e < 4 ? pf : lsum[e & 3] + pf;
+      pb[e >> 3][e & 7] = (_Float16)pf;
+    }
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv[k][db], pb[k], o[db], 0, 0, 0);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  using T = std::true_type;
+  using F = std::false_type;
+  static_assert(NSTAGE == 4, "the main loop is unrolled over the four stages");
+  int j = 0;
+  if constexpr (D > 128) {
+    for (; j + NSTAGE <= n_tiles; j += NSTAGE) {
+      step_seq(C0(), j);
+      step_seq(C1(), j + 1);
+      step_seq(C2(), j + 2);
+      step_seq(C3(), j + 3);
+    }
+    if (j < n_tiles) step_seq(C0(), j);
+    if (j + 1 < n_tiles) step_seq(C1(), j + 1);
+    if (j + 2 < n_tiles) step_seq(C2(), j + 2);
+  } else if (n_tiles > 1) {
+    step(C0(), 0, F(), T());
+    j = 1;
+    for (; j + NSTAGE < n_tiles; j += NSTAGE) {
+      step(C1(), j, T(), T());
+      step(C2(), j + 1, T(), T());
+      step(C3(), j + 2, T(), T());
+      step(C0(), j + 3, T(), T());
+    }
+    for (; j + 1 < n_tiles; ++j) step(j & (NSTAGE - 1), j, T(), T());
+    step(j & (NSTAGE - 1), j, T(), F());
+  } else if (n_tiles == 1) {
+    step(C0(), 0, F(), F());
   }
+  if (D <= 128 && n_tiles > 0) {  // the PV product of the last tile
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[k][db], pb_prev[k], o[db], 0, 0, 0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  l_run = sum_xor32(l_run);
 
-  // Split partial: acc unnormalized against m_run, in the register layout of o (tile,
-  // split, wave, 32-dim block db, quad i, lane: one 16-byte piece per lane, so every
-  // store instruction moves 1 KB of consecutive bytes); m and l (log2 units) per
-  // [row][split]. prefill_merge_kernel, next on the stream, combines the splits.
-  const int S = p.n_splits;
-  const int rows_valid = min(BQ, p.M - i0);
-  const size_t row0 = (size_t)h * p.M + i0;
-  const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
-  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
-  const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
-                                             part_off<NDB>(split, wave, db, i, lane), 0, 0);
-    }
-  if (hl == 0) {
-    const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM, (r * S + split) * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL, (r * S + split) * 4, 0, 0);
-  }
+  store_rows<D>(p, o, m_run, l_run, h, ib, split, wave, lane);
 }
 
 // Combine the split partials of prefill_kernel. One workgroup per (row block, 32-dim
