@@ -19,11 +19,13 @@
 // subnormal c * 2^-24, a nibble in bits 4..7 the subnormal c * 2^-20 (both exact).
 // Of a code word, the masks 0x000F000F / 0x00F000F0 on the word and on the word >> 8
 // give the element pairs (0,4), (1,5), (2,6), (3,7). q . c runs on v_dot2_f32_f16 with
-// fp16 q, exact products and fp32 sums. The value side pairs two keys per
-// v_dot2_f32_f16: the code words of keys a, b are interleaved by halves
-// ([a.lo | b.lo], [a.hi | b.hi]), the weights are fp16 (p_a s_a, p_b s_b), rounded to
-// nearest. Odd elements accumulate in units of 2^-20, even ones in 2^-24; the scale
-// back is exact.
+// fp16 q and fp32 sums; the q pairs meeting high nibbles are scaled by 1/16 so that one
+// sum holds every product in units of 2^-24 (exact unless |q| < 2^-10, where the scaled
+// value is rounded to the fp16 subnormal grid: an error below 2^-25 |c|). The value side
+// pairs two keys per v_dot2_f32_f16: byte k of the code words of keys a, b goes to the
+// low bytes of the two halves by one byte permute, and the masks give elements 2k and
+// 2k + 1 of both keys; the weights are fp16 (p_a s_a, p_b s_b), rounded to nearest. Odd
+// elements accumulate in units of 2^-20, even ones in 2^-24; the scale back is exact.
 //
 // Online softmax per key slot with a lazy rescale: the running reference m moves only
 // when a tile's max exceeds it by more than kSlack (log2 units), so p <= 2^kSlack and
@@ -192,9 +194,12 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+        // pairs k = 1, 3 meet the high nibbles (codes in units of 2^-20): scaled by 1/16
+        // so that every product lands in units of 2^-24 and one sum takes them all
+        const _Float16 f = (k & 1) ? (_Float16)0.0625f : (_Float16)1.0f;
         h2_t t;
-        t.x = __builtin_bit_cast(_Float16, e[k]);
-        t.y = __builtin_bit_cast(_Float16, e[k + 4]);
+        t.x = __builtin_bit_cast(_Float16, e[k]) * f;
+        t.y = __builtin_bit_cast(_Float16, e[k + 4]) * f;
         q[r][4 * w + k] = t;
       }
 #pragma unroll
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     for (int u = 0; u < U; ++u) {
       const float ks = lo_f(t.ksb[u]) * kq, kb = hi_f(t.ksb[u]);
       const uint32_t w4[4] = {t.kc[u].x, t.kc[u].y, t.kc[u].z, t.kc[u].w};
-      float dA[R], dB[R];
+      float dot[R];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t x0 = w4[w], x8 = w4[w] >> 8;
@@ -229,24 +234,24 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
         const h2_t c2 = as_h2(x8 & kLo4), c3 = as_h2(x8 & kHi4);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if (w == 0) {
-            dA[r] = dot2_first(q[r][0], c0);
-            dB[r] = dot2_first(q[r][1], c1);
-          } else {
-            dA[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 0], c0, dA[r], false);
-            dB[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 1], c1, dB[r], false);
-          }
-          dA[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 2], c2, dA[r], false);
-          dB[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 3], c3, dB[r], false);
+          dot[r] = w == 0 ? dot2_first(q[r][0], c0)
+                          : __builtin_amdgcn_fdot2(q[r][4 * w + 0], c0, dot[r], false);
+          dot[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 1], c1, dot[r], false);
+          dot[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 2], c2, dot[r], false);
+          dot[r] = __builtin_amdgcn_fdot2(q[r][4 * w + 3], c3, dot[r], false);
         }
       }
-      const bool ok = base + u * KPW + kk < sp.j1;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float dot = __builtin_fmaf(0.0625f, dB[r], dA[r]);  // dB is in 2^-20 units
-        float v = __builtin_fmaf(ks, dot, kb * qsq[r]);
-        v = lane_group_sum<NGP>(v);
-        s[u][r] = ok ? v : -INFINITY;
+      for (int r = 0; r < R; ++r)
+        s[u][r] = lane_group_sum<NGP>(__builtin_fmaf(ks, dot[r], kb * qsq[r]));
+    }
+    // keys past the span end (its last tile only: a wave-uniform test) get -inf
+    if (base + U * KPW > sp.j1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = base + u * KPW + kk < sp.j1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[u][r] = ok ? s[u][r] : -INFINITY;
       }
     }
 
@@ -299,12 +304,17 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
                               t.vc[2 * i + 1].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t xa = (a4[w] & 0xffffu) | (b4[w] << 16);      // elements 0..3
-        const uint32_t xb = (a4[w] >> 16) | (b4[w] & 0xffff0000u);  // elements 4..7
-        const uint32_t xa8 = xa >> 8, xb8 = xb >> 8;
-        const h2_t c[8] = {as_h2(xa & kLo4),  as_h2(xa & kHi4), as_h2(xa8 & kLo4),
-                           as_h2(xa8 & kHi4), as_h2(xb & kLo4), as_h2(xb & kHi4),
-                           as_h2(xb8 & kLo4), as_h2(xb8 & kHi4)};
+        // byte k of both keys' words (elements 2k, 2k+1) into the low bytes of the two
+        // halves: v_perm_b32 takes bytes 0-3 from its second operand, 4-7 from its
+        // first, and 0x0C is a zero byte
+        h2_t c[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t xk =
+              __builtin_amdgcn_perm(b4[w], a4[w], 0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
+          c[2 * k] = as_h2(xk & kLo4);
+          c[2 * k + 1] = as_h2(xk & kHi4);
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
