@@ -172,6 +172,9 @@ constexpr int kMlx4Rows = 4;
 hipError_t launch_partial(const PartialParams &p, int rows_per_group, int x_count, hipStream_t s);
 hipError_t launch_partial_mlx4(const PartialParams &p, int rows_per_group, int x_count,
                                hipStream_t s);
+// The same spans of an mlx4g32 prefix at D = 128 on fp16 MFMA (rows_per_group <= 4).
+hipError_t launch_mlx4_mfma(const PartialParams &p, int rows_per_group, int x_count,
+                            hipStream_t s);
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
 // causal suffix (bottom-right aligned). A workgroup serves (tile, split): tile = (q-head,
 // block of 128 query rows), split = a range of split_keys tokens of the concatenated key

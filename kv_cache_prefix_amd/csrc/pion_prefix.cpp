@@ -551,7 +551,9 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   if (mlx4) {
     p.x_begin = 0;
     p.seg_per_span = 1;
-    e = launch_partial_mlx4(p, grp_rows, pre_max, st);
+    // head dim 128: the MFMA kernel (PION_NO_MLX4_MFMA keeps the vector kernel)
+    const bool mm = c.D == 128 && !getenv_flag("PION_NO_MLX4_MFMA");
+    e = mm ? launch_mlx4_mfma(p, grp_rows, pre_max, st) : launch_partial_mlx4(p, grp_rows, pre_max, st);
     if (e == hipSuccess && p.suf_splits > 0) {
       p.x_begin = pre_max;  // single problem: its prefix spans are exactly pre_max
       e = launch_partial(p, R, p.suf_splits, st);
