@@ -11,11 +11,24 @@
 //
 // Layout: one lane per uint32 code word (8 elements, 16 input bytes), so four
 // consecutive lanes hold one group; min/max combine across those four lanes. Loads are
-// 16 B per lane and stores 4 B per lane, contiguous across the wave. The scale uses the
-// correctly rounded fp32 divide; the codes round the correctly rounded quotient (a
-// product with the reciprocal where that provably rounds the same, else the divide), and
-// there is no contraction, so the codes are bit-exact with any IEEE fp32 evaluation of
-// the steps above.
+// 16 B per lane and stores 4 B per lane, contiguous across the wave.
+//
+// Arithmetic, each step equal to its IEEE fp32 round-to-nearest-even counterpart:
+//   x - b        one fused v_fma_mix (x fp16, times 1, minus b): a single rounding;
+//   range / 15   q = fl(range * c), c = fl(1/15), then fl(q + fma(-q, 15, range) * c)
+//                by two fmas: equal to the correctly rounded quotient for every
+//                non-negative finite fp32 range (checked exhaustively on the host);
+//   (x - b) / s  rounds to the same integer as t = fl((x - b) * rcp(s)) unless t lies
+//                within 2^-16 of a half-integer: v_rcp_f32 is within 1 ulp of 1/s for
+//                every fp16 s (checked on the device), so |t - fl((x - b)/s)| <=
+//                2^-22 |t| and |t| < 22.5 (s >= range / 22.5 even where s rounds to an
+//                fp16 subnormal); such elements take the correctly rounded divide (a
+//                wave-uniform branch, rare);
+//   rint, clamp  v_med3 to [0, 15], then v_cvt_pk_u8_f32 (round to nearest even, as
+//                checked on the device) packs four codes per word: even elements in one
+//                word, odd ones in another, merged as lo | hi << 4.
+// No contraction elsewhere, so the codes are bit-exact with any IEEE fp32 evaluation
+// of the steps above.
 #include "kernels.h"
 
 #include <hip/hip_fp16.h>
@@ -30,33 +43,54 @@ __device__ __forceinline__ float quad_xor(float v) {
                                                                0xF, 0xF, false));
 }
 
+__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+
+// Packed fp16 min / max of two words (inputs are finite: no quieting needed).
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  uint32_t d;
+  __asm__("v_pk_min_f16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  uint32_t d;
+  __asm__("v_pk_max_f16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+// fl(x - b) for the fp16 x in the low (HI = 0) or high half of w: one fused operation
+// (x * 1 + nb, nb = -b), rounded once
+template <int HI>
+__device__ __forceinline__ float sub_f16(uint32_t w, float nb) {
+  float d;
+  if constexpr (HI)
+    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(nb));
+  else
+    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(nb));
+  return d;
+}
+
 // Encode code word t (elements 8t .. 8t+7) from its 16 loaded bytes; the four words of
-// a group are in one lane quad.
+// a group are in one lane quad. SBW: scale and bias share a 32-bit word (scale low).
+template <bool SBW>
 __device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
                                             uint32_t *__restrict__ codes,
                                             uint16_t *__restrict__ scales,
                                             uint16_t *__restrict__ biases, int sb_stride) {
 #pragma clang fp contract(off)
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  float v[8];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    v[2 * c] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[c] & 0xffffu));
-    v[2 * c + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[c] >> 16));
-  }
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) {
-    mn = fminf(mn, v[e]);
-    mx = fmaxf(mx, v[e]);
-  }
-  // the four lanes of a group are a lane quad (4k..4k+3): quad_perm moves
-  mn = fminf(mn, quad_xor<0xB1>(mn));  // lane ^ 1
-  mn = fminf(mn, quad_xor<0x4E>(mn));  // lane ^ 2
-  mx = fmaxf(mx, quad_xor<0xB1>(mx));
-  mx = fmaxf(mx, quad_xor<0x4E>(mx));
+  // group min and max in one packed fp16 word (min, -max), so that one packed min
+  // per step reduces both: over the lane's four words, then over the lane quad
+  // (4k..4k+3) by quad_perm moves
+  const uint32_t m2 = pk_min(pk_min(w[0], w[1]), pk_min(w[2], w[3]));
+  const uint32_t x2 = pk_max(pk_max(w[0], w[1]), pk_max(w[2], w[3])) ^ 0x80008000u;  // -max
+  uint32_t pm = pk_min(__builtin_amdgcn_perm(x2, m2, 0x05040100u),   // (m2.lo, x2.lo)
+                       __builtin_amdgcn_perm(x2, m2, 0x07060302u));  // (m2.hi, x2.hi)
+  pm = pk_min(pm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pm, 0xB1, 0xF, 0xF, true));  // lane ^ 1
+  pm = pk_min(pm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pm, 0x4E, 0xF, 0xF, true));  // lane ^ 2
+  float mn = h2f((uint16_t)(pm & 0xffffu));
+  float mx = -h2f((uint16_t)(pm >> 16));
   // Signed zeros: -0 orders below +0, so a zero minimum is -0 when the group holds a -0
-  // and a zero maximum is +0 when it holds a +0 (fminf / fmaxf return either zero).
+  // and a zero maximum is +0 when it holds a +0 (the min / max above return either zero).
   // Rare, and the branch is wave-uniform.
   if (__builtin_amdgcn_ballot_w64(mn == 0.0f || mx == 0.0f)) {
     int negz = 0, posz = 0;
@@ -74,28 +108,31 @@ __device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
   }
 
   const float range = mx - mn;
-  const float s32 = __fdiv_rn(range, 15.0f);
+  const float c15 = 1.0f / 15.0f;  // fl(1/15)
+  const float q15 = range * c15;
+  const float s32 = __builtin_fmaf(__builtin_fmaf(-q15, 15.0f, range), c15, q15);
   const __half s16 = __float2half_rn(s32);
-  const __half b16 = __float2half_rn(mn);
+  const __half b16 = __float2half_rn(mn);  // exact: mn is one of the fp16 inputs
   const float s = __half2float(s16);
-  const float b = __half2float(b16);
+  const float nb = -__half2float(b16);
   uint32_t word = 0;
   if (s != 0.0f) {
-    // rint of the correctly rounded quotient diff / s, without a divide per element:
-    // with r = fl(1 / s), fl(diff * r) is within 3 * 2^-24 * |diff / s| of fl(diff / s)
-    // (three roundings of relative size <= 2^-24), so the two round to the same integer
-    // unless a half-integer lies that close; such elements (and non-finite ones) take the
-    // correctly rounded divide.
-    const float r = __fdiv_rn(1.0f, s);
-    float diff[8], tq[8];
-    bool near = false;
+    const float r = __builtin_amdgcn_rcpf(s);
+    float diff[8], tq[8], dh[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      diff[2 * c] = sub_f16<0>(w[c], nb);
+      diff[2 * c + 1] = sub_f16<1>(w[c], nb);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      diff[e] = v[e] - b;
       tq[e] = diff[e] * r;
-      const float gap = fabsf(tq[e] - (floorf(tq[e]) + 0.5f));  // to the nearest half-integer
-      near |= !(gap > fabsf(tq[e]) * 0x1p-20f);                 // NaN counts as near
+      dh[e] = fabsf(__builtin_amdgcn_fractf(tq[e]) - 0.5f);  // distance to k + 1/2
     }
+    // the smallest distance (the compiler forms three-input mins)
+    float dmin = fminf(fminf(fminf(dh[0], dh[1]), fminf(dh[2], dh[3])),
+                       fminf(fminf(dh[4], dh[5]), fminf(dh[6], dh[7])));
+    const bool near = !(dmin > 0x1p-16f);
     // rare: a wave-uniform branch, so the divides run only for waves that need them
     if (__builtin_amdgcn_ballot_w64(near)) {
       if (near) {
@@ -103,32 +140,57 @@ __device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
         for (int e = 0; e < 8; ++e) tq[e] = __fdiv_rn(diff[e], s);
       }
     }
+    uint32_t ev = 0, od = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float q = fminf(fmaxf(rintf(tq[e]), 0.0f), 15.0f);
-      word |= (uint32_t)q << (4 * e);
+    for (int k = 0; k < 4; ++k) {
+      ev = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(tq[2 * k], 0.0f, 15.0f), k, ev);
+      od = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(tq[2 * k + 1], 0.0f, 15.0f), k, od);
     }
+    word = ev | (od << 4);
   }
   if (valid) {
-    codes[t] = word;
+    __builtin_nontemporal_store(word, codes + t);
     if ((t & 3) == 0) {
-      scales[(t >> 2) * sb_stride] = __builtin_bit_cast(uint16_t, s16);
-      biases[(t >> 2) * sb_stride] = __builtin_bit_cast(uint16_t, b16);
+      const uint16_t sb = __builtin_bit_cast(uint16_t, s16), bb = __builtin_bit_cast(uint16_t, b16);
+      if constexpr (SBW) {
+        __builtin_nontemporal_store((uint32_t)sb | ((uint32_t)bb << 16),
+                                    (uint32_t *)scales + (t >> 2));
+      } else {
+        scales[(t >> 2) * sb_stride] = sb;
+        biases[(t >> 2) * sb_stride] = bb;
+      }
     }
   }
 }
 
-// One code word per lane: lane t of the grid encodes word t.
+// One code word per lane and chunk: workgroup x encodes the kWords chunks of 256 words
+// from word 256 kWords x, lane i word 256 (kWords x + k) + i of chunk k; all chunks'
+// loads are issued before the first is encoded (more bytes in flight per wave).
+constexpr int kWords = 4;
+template <bool SBW>
 __global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *__restrict__ x,
                                                                int64_t nwords,
                                                                uint32_t *__restrict__ codes,
                                                                uint16_t *__restrict__ scales,
                                                                uint16_t *__restrict__ biases,
                                                                int sb_stride) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < nwords;
-  const uint4 raw = valid ? *(const uint4 *)(x + t * 8) : make_uint4(0, 0, 0, 0);
-  encode_word(raw, t, valid, codes, scales, biases, sb_stride);
+  const int64_t t0 = (int64_t)blockIdx.x * (256 * kWords) + threadIdx.x;
+  uint4 raw[kWords];
+#pragma unroll
+  for (int k = 0; k < kWords; ++k) {
+    const int64_t t = t0 + 256 * k;
+    if (t < nwords) {
+      const nt_u32x4 v = __builtin_nontemporal_load((const nt_u32x4 *)(x + t * 8));
+      raw[k] = make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+      raw[k] = make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kWords; ++k) {
+    const int64_t t = t0 + 256 * k;
+    encode_word<SBW>(raw[k], t, t < nwords, codes, scales, biases, sb_stride);
+  }
 }
 
 }  // namespace
@@ -139,11 +201,17 @@ hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint3
   const int64_t nwords = rows * (D / 8);
   if (nwords <= 0) return hipSuccess;
   if (sb_stride != 1 && sb_stride != 2) return hipErrorInvalidValue;
-  const int64_t blocks = (nwords + 255) / 256;
+  const int64_t blocks = (nwords + 256 * kWords - 1) / (256 * kWords);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  note_launch("quantize_mlx4g32_kernel");
-  hipLaunchKernelGGL(quantize_mlx4g32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x,
-                     nwords, codes, scales, biases, sb_stride);
+  // scale and bias interleaved in one 32-bit word (the slot layout): one store
+  const bool sbw = sb_stride == 2 && biases == scales + 1 && ((uintptr_t)scales & 3) == 0;
+  note_launch("quantize_mlx4g32_kernel<%d>", (int)sbw);
+  if (sbw)
+    hipLaunchKernelGGL(quantize_mlx4g32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                       nwords, codes, scales, biases, sb_stride);
+  else
+    hipLaunchKernelGGL(quantize_mlx4g32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                       nwords, codes, scales, biases, sb_stride);
   return hipGetLastError();
 }
 
