@@ -109,6 +109,9 @@ def parse():
                     help="config 5: after the timed queries, rebuild the block means this many "
                          "times (store a slot again, query it once; untimed, for a kernel trace)")
     ap.add_argument("--eager", action="store_true", help="calls mode: no graph")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="calls mode: the 32 layer calls of a step go round-robin to this "
+                         "many streams (independent calls overlap), joined at the step end")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -336,13 +339,26 @@ def run_decode(args, torch, kp, synth, dev, stream, inputs=None, cpu=None):
                    out[l].data_ptr(), lse[l].data_ptr()) for l in range(case.layers)]
                  for k in range(NSET)]
 
+    nstreams = max(1, args.streams) if args.mode == "calls" else 1
+    side = [torch.cuda.Stream(device=dev) for _ in range(nstreams)] if nstreams > 1 else []
+
     def make_step(cs):
         def step():
-            h = torch.cuda.current_stream().cuda_stream
-            for c in cs:
-                rc = fn(*c, h)
+            cur = torch.cuda.current_stream()
+            if not side:
+                for c in cs:
+                    rc = fn(*c, cur.cuda_stream)
+                    if rc != 0:
+                        raise kp.PionError(rc, fn.__name__)
+                return
+            for sd in side:           # fork: every side stream starts after the step's start
+                sd.wait_stream(cur)
+            for i, c in enumerate(cs):
+                rc = fn(*c, side[i % len(side)].cuda_stream)
                 if rc != 0:
                     raise kp.PionError(rc, fn.__name__)
+            for sd in side:           # join
+                cur.wait_stream(sd)
         return step
 
     graph = args.mode == "calls" and not args.eager
@@ -366,7 +382,8 @@ def run_decode(args, torch, kp, synth, dev, stream, inputs=None, cpu=None):
         "config": {"workload": "M=1 prefix attention, decode shape H_q=H_kv=8 N=2048 D=128, "
                                "32 resident layers queried per step",
                    "entry": fn.__name__, "launches_per_step": lps,
-                   "launch": "hip-graph replay" if graph else "eager",
+                   "launch": ("hip-graph replay" if graph else "eager") +
+                             (f", calls round-robin over {nstreams} streams" if nstreams > 1 else ""),
                    "bytes_per_step": bytes_step,
                    "memory_side_cache": f"cold: steps alternate over {NSET} copies of the 32 "
                                         f"layers ({NSET * bytes_step / 1e6:.0f} MB)"},

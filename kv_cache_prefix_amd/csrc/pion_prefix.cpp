@@ -518,7 +518,9 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
     p.pre_chunk = c.B;
     pre_max = c.n_sel;
   } else {
-    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 64, mlx4, p.waves);
+    // at least 128 keys per span: below that the store, ticket and merge of a split cost
+    // more than the keys save (measured on single M = 1 calls at N = 2048)
+    p.pre_chunk = pick_chunk(N_max, (long long)Y * n_prob, 128, mlx4, p.waves);
     pre_max = (N_max + p.pre_chunk - 1) / p.pre_chunk;
   }
   if (c.S_suf > 0) {
