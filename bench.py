@@ -63,7 +63,7 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "2984738fdfb1f2ddb279d617edc89f7e2947f0cbace84f37ebe2209c31823c5c",
+                  "sources_sha256": "b44c58d88d35127208492a2ecb519ee7d5a88c8d1c4653739ce9cbd8f4c8439b",
                   "bytes_per_launch": 268750056}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
 # 22,198,510 B and writes 32,232,960 B (the five splits' partials), prefill_merge_kernel<128>
@@ -469,28 +469,31 @@ def run_prefill(args, torch, kp, synth, dev, stream, inp=None, cpu=None, calls=N
     }
 
 
-def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20):
-    """A plain streaming read of `nbytes` (past the 256 MB memory-side cache), `reps` times
-    back to back: the achievable HBM read rate, timed with HIP events."""
-    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20, nbufs=1):
+    """A plain streaming read of `nbytes` (past the 256 MB memory-side cache: one buffer
+    of at least that size, or `nbufs` buffers read in rotation), `reps` times back to
+    back: the achievable HBM read rate for a pass of that size, timed with HIP events."""
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(nbufs)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        for _ in range(3):
-            kp.pion_bench_stream_read(buf, sink)
+        for i in range(3):
+            kp.pion_bench_stream_read(bufs[i % nbufs], sink)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for _ in range(reps):
-            kp.pion_bench_stream_read(buf, sink)
+        for i in range(reps):
+            kp.pion_bench_stream_read(bufs[i % nbufs], sink)
         ev1.record(stream)
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / reps
-    del buf
+    del bufs
     return {"value": round(nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s",
             "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(us, 2), "kernel": "stream_read_kernel",
             "note": f"plain streaming read of {nbytes >> 20} MiB with 16-byte non-temporal "
-                    f"loads, {reps} launches back to back (cold: past the memory-side cache)"}
+                    f"loads, {reps} launches back to back"
+                    + (f" over {nbufs} buffers in rotation" if nbufs > 1 else "")
+                    + " (cold: past the memory-side cache)"}
 
 
 def run_mlx4(args, torch, kp, synth, dev, stream):
@@ -673,6 +676,10 @@ def run_sparse(args, torch, kp, synth, dev, stream):
             make_step(i % NSLOT)()
         torch.cuda.synchronize()
         del K16, V16
+    # a plain read of the bytes one K_mean build reads (the keys of the slot), as the
+    # ceiling for a pass of that size
+    kmean_ceiling = stream_ceiling(torch, kp, dev, stream, case.H_kv * case.N * case.D * 2,
+                                   reps=50, nbufs=10)
     nb = case.N // case.B
     nbytes = (case.H_kv * nb * case.D * 4 + case.K_top * case.B * case.D * 4
               + case.S_suf * case.D * 4 + case.H_q * case.D * 6)
@@ -687,6 +694,7 @@ def run_sparse(args, torch, kp, synth, dev, stream):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
         "warm": {"value": round(wms * 1e3, 3), "unit": "us/query",
                  "note": "one slot every step (memory-side cache warm)"},
+        "kmean_read_ceiling": kmean_ceiling,
         "cpu_baseline": None,
     }
 
@@ -1001,7 +1009,7 @@ def main():
         "cpu_baseline": r["cpu_baseline"],
     }
     for extra in ("warm", "batched_q", "stream_ceiling", "single_query", "warm_call",
-                  "quantize", "fp16_resident", "sweep"):
+                  "quantize", "fp16_resident", "sweep", "kmean_read_ceiling"):
         if extra in r:
             line[extra] = r[extra]
     print(json.dumps(line), flush=True)
