@@ -4,7 +4,11 @@
 // N prefix keys of kv-head g = head_map[h] and the suffix keys j <= S_suf - M + i.
 //
 // Per workgroup: 128 query rows of one q-head (4 waves x 32 rows) against one split of
-// the key index space [0, N + S_suf) (prefix then suffix), in tiles of 64 keys.
+// the key index space [0, N + S_suf) (prefix then suffix), in tiles of 32 keys. For
+// D <= 128 the tiles run as a three-deep software pipeline: one iteration issues the
+// PV product of tile j - 1, the softmax weights of tile j and the S^T product of tile
+// j + 1, so the matrix work of one tile covers the vector work of the next; larger head
+// dims (whose accumulators leave no registers for a second tile) run tiles in sequence.
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_f16: A = a 32-key x 16-dim slice of the K tile
 //                 (LDS, row-major), B = Q^T (registers, loaded once); the result lane l
 //                 holds 16 keys x 1 query (query l % 32).
