@@ -25,6 +25,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Inline assembly that writes M0 (the LDS-writing loads of mfma_common.h) saves and
+# restores it in the same statement; a new use of M0 in inline assembly must do the same.
 
 
 def _compile(src: str) -> str:

@@ -53,15 +53,17 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes) {
 // past the buffer's end the bytes are zero. One wait state separates the M0 write from
 // the load that reads it. The compiler cannot tell which LDS bytes such a load writes,
 // so it is issued here, and the caller waits for it (s_waitcnt vmcnt) before reading.
-// The compiler treats M0 as reserved and may ignore its clobber (it warns so); that is
-// safe only because nothing else in the kernels that call this reads or writes M0 — in
-// their ISA every M0 write is this statement's own, right before its load. A kernel that
-// adds a use of M0 (LDS DMA builtins, movrel indexing, s_sendmsg) must not call this.
+// The compiler treats M0 as reserved and may ignore a clobber of it, so the statement
+// saves M0 in an SGPR of its own and restores it after the load (the load reads M0 when
+// it issues): whatever value the compiler keeps in M0 survives the call.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                   :
-                   : "v"(voff), "s"(lds), "s"(rsrc)
-                   : "memory", "m0");
+  uint32_t save;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(lds), "s"(rsrc)
+      : "memory");
 }
 
 // A row max may grow by this much (log2 units, a factor 2^8) before the accumulators
