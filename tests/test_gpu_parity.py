@@ -385,6 +385,32 @@ def test_mlx4g32_every_row_count(kp, D, H_q, H_kv):
     check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V)))
 
 
+# head dim 128 runs on the MFMA kernel by default; PION_NO_MLX4_MFMA=1 selects the vector
+# kernel: both against the oracle, on several layers of different lengths in one launch
+# (per-problem key counts, spans past a short problem's end) and on single M > 1 queries
+@pytest.mark.parametrize("vector", [False, True])
+def test_mlx4g32_d128_layers_both_kernels(kp, monkeypatch, vector):
+    if vector:
+        monkeypatch.setenv("PION_NO_MLX4_MFMA", "1")
+    Ns = [1, 63, 64, 65, 700, 5000]
+    inputs = [synth.generate(synth.MLX4_DECODE, 60 + l, N=N, H_q=6, H_kv=2) for l, N in enumerate(Ns)]
+    for l, inp in enumerate(inputs):
+        kp.pion_prefix_store("t", 40 + l, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    L = len(Ns)
+    out, lse = empty((L, 6, 1, 128)), empty((L, 6, 1))
+    kp.pion_prefix_query_layers("t", 40, dev(np.stack([i.Q for i in inputs])), out, lse)
+    plan = kp.pion_prefix_last_plan()
+    assert ("mlx4_split_kernel" if vector else "mlx4_mfma_kernel") in plan, plan
+    out, lse = host(out), host(lse)
+    for l, inp in enumerate(inputs):
+        check(out[l], lse[l], *oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V)))
+    inp = synth.generate(synth.MLX4_DECODE, 70, N=3001, H_q=8, H_kv=2, M=5)
+    kp.pion_prefix_store("t", 50, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 50, inp.Q)
+    check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V)))
+    kp.pion_prefix_drop("t", -1)
+
+
 def test_mlx4g32_uneven_head_map(kp):
     # kv-head 0 gets 5 q-heads (groups of 4 and 1), kv-head 1 gets 2, kv-head 2 gets 1
     inp = synth.generate(synth.MLX4_DECODE, 6, N=300, H_q=8, H_kv=3)
