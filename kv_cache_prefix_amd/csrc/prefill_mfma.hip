@@ -13,9 +13,11 @@
 //                 (LDS, row-major), B = Q^T (registers, loaded once); the result lane l
 //                 holds 16 keys x 1 query (query l % 32).
 //   online softmax in fp32 (log2 units, scale folded into the exponent; the row sum
-//                 uses the fp32 weights, the PV product their fp16 roundings; the
-//                 accumulators are rescaled only when a row max grows by more than
-//                 2^8, and only boundary tiles are masked); a lane's p
+//                 uses the fp32 weights, the PV product their fp16 roundings; a tile's
+//                 weights are taken against the running max as it stands, and only
+//                 when they overflow (a lane's sum past 2^15) is the tile's row max
+//                 taken and the accumulators rescaled; only boundary tiles are
+//                 masked); a lane's p
 //                 values are already the B operand of the next product: result element
 //                 (i, j) of the S^T block is key 8i + 4(l/32) + j, and a 16-key k-step of
 //                 the PV product takes elements i = 2s, 2s+1 as its eight k slots.
@@ -59,6 +61,9 @@ constexpr int BQ = 128;   // query rows per workgroup
 constexpr int BK = 32;    // keys per tile
 constexpr int kMaxPrefillSplits = 16;
 constexpr int kMergeChunk = 8;  // splits whose partials the merge loads per round
+// A lane's weights of one tile may sum to this much before the running max moves (each
+// weight then stays below 2^15, inside fp16's range with its full relative precision)
+constexpr float kGrowLimit = 32768.f;
 
 // Byte offset of the 16-byte piece (split c, wave w, 32-dim block db, quad i, lane) in a
 // row block's partials
@@ -326,6 +331,42 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     else __builtin_amdgcn_s_setprio(0);
   };
 
+  // The weights of a tile against the running max m (log2 units): fp16 into pb (masked
+  // scores give 0), and this lane's part of the row sum from the fp32 values.
+  auto tile_weights = [&](const f16v &sc, float m, half8 (&pb)[2]) {
+    float lsum[4];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pf = fast_exp2(__builtin_fmaf(sc[e], p.qscale, -m));
+      lsum[e & 3] = e < 4 ? pf : lsum[e & 3] + pf;
+      pb[e >> 3][e & 7] = (_Float16)pf;
+    }
+    return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+  };
+  // Lazy rescale without a per-tile row max: a lane's weights sum to at most kGrowLimit
+  // (so each fits fp16 with room to spare) unless some score of its row exceeds the
+  // running max by more than log2 of that (and always on a row's first keys, when m_run
+  // is still kNegBig). Only then (wave-uniform branch, rare after the first tile) is the
+  // tile's row max taken: m_run moves up to it, O and l are scaled by 2^(m_old - m_new)
+  // and the weights recomputed. Rows whose max has not grown keep m_run.
+  auto regrow = [&](const f16v &sc, float &lt, half8 (&pb)[2]) {
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kGrowLimit))) {
+      float mt = fmaxf(sc[0], sc[1]);  // raw-score max; the scale is positive
+#pragma unroll
+      for (int e = 2; e < 16; ++e) mt = fmaxf(mt, sc[e]);
+      mt = max_xor32(mt) * p.qscale;
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      lt = tile_weights(sc, m_run, pb);
+    }
+  };
+
   // Software pipeline over key tiles, three tiles deep: iteration j runs the PV product of
   // tile j - 1, the softmax weights of tile j and the S^T product of tile j + 1 - three
   // independent pieces of work, so the exponentials of one tile overlap the matrix
@@ -357,10 +398,8 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
       set_prio(n_tiles - j);
     }
-    // Tile j: mask (boundary tiles only), raw row max scaled to log2 units, lazy rescale:
-    // the running max moves only when the tile's max exceeds it by more than
-    // kRescaleSlack; then O, l and the pending weights of tile j - 1 are scaled
-    // (wave-uniform branch, rare after the first tiles).
+    // Tile j: mask (boundary tiles only); its weights are taken against the running max
+    // m_run as it stands, and the tile's own row max only when they overflow (below)
     if (!tile_clean(j)) {
       const int kt0 = tile_t0(j), lane_end = tile_lane_end(j);
 #pragma unroll
@@ -368,29 +407,6 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s_cur[4 * i + jj] = -INFINITY;
-    }
-    {
-      float mt = fmaxf(s_cur[0], s_cur[1]);  // raw-score max; the scale is positive
-#pragma unroll
-      for (int e = 2; e < 16; ++e) mt = fmaxf(mt, s_cur[e]);
-      mt = max_xor32(mt) * p.qscale;
-      const bool grow = mt > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-        if (has_prev) {
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb_prev[k][e] = (_Float16)((float)pb_prev[k][e] * alpha);
-        }
-      }
     }
     // The three products and the weights, as one straight-line block: reads of K (tile
     // j + 1) start first, the PV product of tile j - 1 and the weights of tile j run
@@ -410,20 +426,13 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[k][db], pb_prev[k], o[db], 0, 0, 0);
     }
     half8 pb[2];
-    float lsum[4];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pf = fast_exp2(__builtin_fmaf(s_cur[e], p.qscale, -m_run));  // masked: 0
-      lsum[e & 3] = e < 4 ? pf : lsum[e & 3] + pf;
-      pb[e >> 3][e & 7] = (_Float16)pf;  // at most 2^8
-    }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    float lt = tile_weights(s_cur, m_run, pb);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vf[k][db] = vfrag(VB + 16 * k * (int)ROWB, db);
+    f16v s_nxt;
     if (has_next) {
-      f16v s_nxt;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_nxt[e] = 0.f;
 #pragma unroll
@@ -431,13 +440,10 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds % KR], qb[ds], s_nxt, 0, 0, 0);
         if (ds + KR < NDS) kf[ds % KR] = kfrag(KBN, ds + KR);
       }
-      s_cur = s_nxt;
     }
     // the weights and row sum of tile j are due in this block (left alone, the compiler
     // sinks them to the next iteration, after the matrix products, serializing the two)
-    __asm__ volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
-    pb_prev[0] = pb[0];
-    pb_prev[1] = pb[1];
+    __asm__ volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(lt));
     if (has_prev && has_next) {
       constexpr int NRD = NDS - KR + 4 * NDB;  // reads after the first K fragments
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, KR, 0);
@@ -448,6 +454,11 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NRD + NDS + 2 * NDB - 1) / (NDS + 2 * NDB), 0);
       }
     }
+    regrow(s_cur, lt, pb);
+    l_run += lt;
+    pb_prev[0] = pb[0];
+    pb_prev[1] = pb[1];
+    if (has_next) s_cur = s_nxt;
   };
   // Head dims above 128 hold twice the accumulators and operands: there the tiles run one
   // after the other (S^T, softmax and PV of tile j in iteration j), which fits the
@@ -478,35 +489,15 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         for (int jj = 0; jj < 4; ++jj)
           if (kt0 + 8 * i + 4 * hl + jj >= lane_end) s[4 * i + jj] = -INFINITY;
     }
-    float mt = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int e = 2; e < 16; ++e) mt = fmaxf(mt, s[e]);
-    mt = max_xor32(mt) * p.qscale;
-    const bool grow = mt > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mt : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-    }
     half8 vv[2][NDB];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vv[k][db] = vfrag(VB + 16 * k * (int)ROWB, db);
     half8 pb[2];
-    float lsum[4];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pf = fast_exp2(__builtin_fmaf(s[e], p.qscale, -m_run));
-      lsum[e & 3] = e < 4 ? pf : lsum[e & 3] + pf;
-      pb[e >> 3][e & 7] = (_Float16)pf;
-    }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    float lt = tile_weights(s, m_run, pb);
+    regrow(s, lt, pb);
+    l_run += lt;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
