@@ -66,6 +66,27 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t l
       : "memory");
 }
 
+// Four such loads under one save and restore of M0: buffer ra at offsets v0, v1 into
+// LDS l0, l1, then buffer rb at v0, v1 into l2, l3 (the K and V pieces of two 1 KB runs
+// of a tile).
+__device__ __forceinline__ void load_lds16_x4(i32x4 ra, i32x4 rb, uint32_t v0, uint32_t v1,
+                                              uint32_t l0, uint32_t l1, uint32_t l2,
+                                              uint32_t l3) {
+  uint32_t save;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %7, 0 offen lds\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %7, 0 offen lds\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %8, 0 offen lds\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %8, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(v0), "v"(v1), "s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(ra), "s"(rb)
+      : "memory");
+}
+
 // A row max may grow by this much (log2 units, a factor 2^8) before the accumulators
 // are rescaled: weights up to 2^8 stay exact enough in fp16 and the fp32 sums cannot
 // overflow, and after the first tiles a rescale is rare.

@@ -228,26 +228,40 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     const int lc = (lane % CHP) ^ swz<DP>(r);
     voff[t] = (uint32_t)r * ROWG + (uint32_t)((lc < CH ? lc : 0) * 16);
   }
-  auto issue = [&](int j) {
-    const bool suf = j >= n_pre;  // workgroup-uniform
-    const int r0 = suf ? suf_beg - p.N + (j - n_pre) * BK : k_begin + j * BK;  // source row
-    const i32x4 rk = suf ? rKs : rK, rv = suf ? rVs : rV;
-    const uint32_t st = lds0 + (uint32_t)((j % NSTAGE) * 2 * TB + 1024 * NLD * wave_u);
-#pragma unroll
-    for (int t = 0; t < NLD; ++t) {
-      load_lds16(rk, (uint32_t)r0 * ROWG + voff[t], st + 1024 * t);
-      load_lds16(rv, (uint32_t)r0 * ROWG + voff[t], st + TB + 1024 * t);
+  // Tiles load in order; the next one's index, source byte offset and descriptors (the
+  // suffix ones from tile n_pre on)
+  int dma_j = 0;
+  uint32_t dma_src = (uint32_t)k_begin * ROWG;
+  i32x4 dk = rK, dv = rV;
+  auto issue_next = [&]() {
+    if (dma_j == n_pre) {  // workgroup-uniform
+      dk = rKs;
+      dv = rVs;
+      dma_src = (uint32_t)(suf_beg - p.N) * ROWG;
     }
+    const uint32_t st = lds0 + (uint32_t)((dma_j % NSTAGE) * 2 * TB + 1024 * NLD * wave_u);
+#pragma unroll
+    for (int t = 0; t + 1 < NLD; t += 2)
+      load_lds16_x4(dk, dv, dma_src + voff[t], dma_src + voff[t + 1], st + 1024 * t,
+                    st + 1024 * (t + 1), st + TB + 1024 * t, st + TB + 1024 * (t + 1));
+    if (NLD & 1) {
+      load_lds16(dk, dma_src + voff[NLD - 1], st + 1024 * (NLD - 1));
+      load_lds16(dv, dma_src + voff[NLD - 1], st + TB + 1024 * (NLD - 1));
+    }
+    dma_src += BK * ROWG;
+    ++dma_j;
   };
-  // Tile j's first key in the concatenated index, its segment's end, this row's limit
-  // inside it, and the end of the keys every row of the workgroup sees
+  // Tile j's first key in the concatenated index and this row's limit inside it. Tiles
+  // that need the per-key mask: the last prefix tile when the prefix part ends inside it,
+  // and the suffix tiles from j_suf_mask on (keys past the first row's causal limit).
   auto tile_t0 = [&](int j) { return j >= n_pre ? suf_beg + (j - n_pre) * BK : k_begin + j * BK; };
-  auto tile_clean = [&](int j) {
-    return j >= n_pre ? tile_t0(j) + BK <= min(k_stop, full_end) : tile_t0(j) + BK <= pre_end;
-  };
   auto tile_lane_end = [&](int j) { return j >= n_pre ? row_end : pre_end; };
+  const int j_pre_mask = (n_pre > 0 && ((pre_end - k_begin) & (BK - 1))) ? n_pre - 1 : -1;
+  const int lim_s = min(k_stop, full_end);
+  const int j_suf_mask = n_pre + (lim_s > suf_beg ? (lim_s - suf_beg) / BK : 0);
+  auto tile_clean = [&](int j) { return j != j_pre_mask && j < j_suf_mask; };
 
-  for (int j = 0; j < NSTAGE - 1 && j < n_tiles; ++j) issue(j);
+  while (dma_j < NSTAGE - 1 && dma_j < n_tiles) issue_next();
   half8 qb[NDS];
   {
     const uint16_t *qrow = p.Q + ((size_t)h * p.M + qi_c) * D;
@@ -395,8 +409,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
       // ... and every wave's; every wave is also done with tile j - 1 (its V^T operands
       // are in registers), whose stage tile j + 3 fills
       __syncthreads();
-      if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
-      set_prio(n_tiles - j);
+      if (dma_j < n_tiles) issue_next();  // tile j + NSTAGE - 1
     }
     // Tile j: mask (boundary tiles only); its weights are taken against the running max
     // m_run as it stands, and the tile's own row max only when they overflow (below)
@@ -478,7 +491,7 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if (j + NSTAGE - 1 < n_tiles) issue(j + NSTAGE - 1);
+    if (dma_j < n_tiles) issue_next();  // tile j + NSTAGE - 1
     set_prio(n_tiles - j);
     f16v s = s_product(stg);
     if (!tile_clean(j)) {
@@ -523,14 +536,17 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
     if (j + 1 < n_tiles) step_seq(C1(), j + 1);
     if (j + 2 < n_tiles) step_seq(C2(), j + 2);
   } else if (n_tiles > 1) {
+    set_prio(n_tiles);
     step(C0(), 0, F(), T());
     j = 1;
     for (; j + NSTAGE < n_tiles; j += NSTAGE) {
+      set_prio(n_tiles - j);  // once per four tiles
       step(C1(), j, T(), T());
       step(C2(), j + 1, T(), T());
       step(C3(), j + 2, T(), T());
       step(C0(), j + 3, T(), T());
     }
+    set_prio(n_tiles - j);
     for (; j + 1 < n_tiles; ++j) step(j & (NSTAGE - 1), j, T(), T());
     step(j & (NSTAGE - 1), j, T(), F());
   } else if (n_tiles == 1) {
