@@ -66,16 +66,16 @@ DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h")
                   "sources_sha256": "b44c58d88d35127208492a2ecb519ee7d5a88c8d1c4653739ce9cbd8f4c8439b",
                   "bytes_per_launch": 268750056}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
-# 22,323,161 B and writes 32,124,928 B (the five splits' partials), prefill_merge_kernel<128>
-# reads 33,518,979 B and writes 6,340,608 B (out and lse).
+# 22,314,843 B and writes 32,153,395 B (the five splits' partials), prefill_merge_kernel<128>
+# reads 33,495,302 B and writes 6,340,608 B (out and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "d526cd0a19814afceda89a9bc1e0be859fca78713d8d35870f752b0fa5b8866a",
-                   "bytes_per_launch": 94307677}
+                   "sources_sha256": "13f0f784ac8c9169ff32900f6b3323a1f17a6e3c115412aeee407cc7d148dc26",
+                   "bytes_per_launch": 94304148}
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
-# reads 671,953,844 B (671,088,640 algorithmic) and writes 644,096 B.
+# reads 671,957,310 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),
-                "sources_sha256": "58c3c1c8290d1c6a263b2c7c34855d475c321959d966c730f5b21e4eda33ea8e",
-                "bytes_per_launch": 672597940}
+                "sources_sha256": "45e624f4c8b4dbe02933f48c733c661772102799b6e0cec5505683b7359b6d9b",
+                "bytes_per_launch": 672601406}
 
 
 def kernel_sources_sha256(files=DECODE_TRAFFIC["sources"]):
