@@ -763,6 +763,31 @@ def test_mfma_prefill_shapes(kp, D, N, M, S_suf):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("growth", [12.0, 60.0])
+def test_mfma_prefill_running_max_growth(kp, D, growth):
+    # Scores that rise along the keys: K gets a ramp in the direction of every query, so a
+    # row's max keeps growing tile after tile by `growth` log2 units in all. At 12 the
+    # running max never has to move after the first tile (weights up to 2^12 in fp16);
+    # at 60 it moves several times mid-stream, rescaling accumulated O and l. All rows.
+    N, M, S_suf, H_q, H_kv = 1500, 200, 200, 4, 2
+    inp = synth.generate(synth.PREFILL, 14, N=N, M=M, S_suf=S_suf, H_q=H_q, H_kv=H_kv, D=D)
+    rng = np.random.default_rng(14)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    c = 8.0                                           # |q| along u
+    qscale = np.log2(np.e) / np.sqrt(D)
+    r_max = growth / (c * qscale)                     # ramp end: growth log2 units above 0
+    ramp = np.linspace(0.0, r_max, N + S_suf)
+    Q = (0.25 * inp.Q.astype(np.float64) + c * u).astype(np.float16)
+    K = (0.25 * inp.K.astype(np.float64) + ramp[None, :N, None] * u).astype(np.float16)
+    K_suf = (0.25 * inp.K_suf.astype(np.float64) + ramp[None, N:, None] * u).astype(np.float16)
+    kp.pion_prefix_store("t", 603, dev(K), dev(inp.V))
+    out, lse = empty((H_q, M, D)), empty((H_q, M))
+    kp.pion_prefix_query_fused("t", 603, dev(Q), dev(K_suf), dev(inp.V_suf), out, lse)
+    check(host(out), host(lse), *oracle.prefix_query_fused(Q, K, inp.V, K_suf, inp.V_suf))
+
+
 def test_mfma_prefill_arbitrary_head_map_all_rows(kp):
     inp = synth.generate(synth.PREFILL, 12, N=200, M=48, S_suf=50, H_q=5, H_kv=3)
     hm = synth.random_head_map(5, 3, 7)
