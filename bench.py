@@ -44,6 +44,9 @@ the host before the GPU is touched: worker processes (one BLAS thread each) over
 usable host cores (at most 16) on a fixed sample of the workload - whole 32-layer decode
 passes, or every row of one prefill step - median of 3 runs, with the 1-thread figure of
 a smaller sample beside it (`single_thread`). Other configs: one thread, about 10 s.
+The same leg checks the GPU's results of the run against the oracle on the same inputs
+(exiting on a disagreement; the prefill's max-abs errors go into its roofline object):
+it is the only part of the bench that calls the oracle, and --no-cpu-baseline skips it.
 """
 from __future__ import annotations
 
@@ -304,6 +307,13 @@ def cpu_baselines(decode_inputs=None, prefill_input=None):
     return res
 
 
+def oracle_leg(args):
+    """True when this run includes the oracle leg: the oracle timed on the host cores
+    (cpu_baseline) and, on the same inputs, the GPU's results checked against it. That leg
+    is the only part of bench.py that calls the oracle; --no-cpu-baseline skips it."""
+    return not args.no_cpu_baseline
+
+
 def check_close(got, ref, tol, what):
     import numpy as np
     err = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
@@ -314,7 +324,6 @@ def check_close(got, ref, tol, what):
 # ----------------------------------------------------------------------------- configs
 def run_decode(args, torch, kp, synth, dev, stream, inputs=None, cpu=None):
     import numpy as np
-    import oracle
     case = synth.DECODE
     if inputs is None:
         inputs = [synth.generate(case, l) for l in range(case.layers)]
@@ -368,10 +377,12 @@ def run_decode(args, torch, kp, synth, dev, stream, inputs=None, cpu=None):
         steps[0]()
     plan = kp.pion_prefix_last_plan()   # the kernel(s) of one launch of the step
     (ms, launch_us), (wms, wlaunch_us) = warm_cold(torch, stream, steps, lps, graph, args)
-    for l in (0, case.layers - 1):
-        ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
-        check_close(out[l].cpu().numpy(), ref, 2e-3, "out")
-        check_close(lse[l].cpu().numpy(), ref_lse, 1e-4, "lse")
+    if oracle_leg(args):   # the first and last layers against the oracle
+        import oracle
+        for l in (0, case.layers - 1):
+            ref, ref_lse = oracle.prefix_query(inputs[l].Q, inputs[l].K, inputs[l].V)
+            check_close(out[l].cpu().numpy(), ref, 2e-3, "out")
+            check_close(lse[l].cpu().numpy(), ref_lse, 1e-4, "lse")
     bytes_layer = case.H_kv * case.N * case.D * 2 * 2
     bytes_step = bytes_layer * case.layers
     bytes_launch = bytes_step // lps
@@ -404,7 +415,6 @@ def run_prefill(args, torch, kp, synth, dev, stream, inp=None, cpu=None, calls=N
     """The fused batched-Q prefill: `calls` timed back-to-back calls (default: --steps)
     between one pair of HIP events on the launch stream, whose mean is the roofline's
     launch time; a second pass with an event after every call gives the median."""
-    import oracle
     case = synth.PREFILL
     if inp is None:
         inp = synth.generate(case)
@@ -455,11 +465,14 @@ def run_prefill(args, torch, kp, synth, dev, stream, inp=None, cpu=None, calls=N
     torch.cuda.synchronize()
     per_call = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
     median_us = per_call[n // 2]
-    # every row checked against the oracle (the timed calls all wrote the same output)
-    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
-    o, l = out.cpu().numpy(), lse.cpu().numpy()
-    check_close(o, ref, 2e-3, "out")
-    check_close(l, ref_lse, 1e-4, "lse")
+    err = None
+    if oracle_leg(args):   # every row against the oracle (the timed calls all wrote it)
+        import oracle
+        ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf)
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        check_close(o, ref, 2e-3, "out")
+        check_close(l, ref_lse, 1e-4, "lse")
+        err = {"out": float(abs(o - ref).max()), "lse": float(abs(l - ref_lse).max())}
     flops = 4 * case.H_q * case.D * (case.M * case.N + case.M * (case.M + 1) // 2)
     kp.pion_prefix_drop(sid, -1)
     return {
@@ -475,8 +488,7 @@ def run_prefill(args, torch, kp, synth, dev, stream, inp=None, cpu=None, calls=N
                      "avg_launch_us": launch_us, "median_launch_us": round(median_us, 3),
                      "median_TFLOP/s": round(flops / (median_us * 1e-6) / 1e12, 2),
                      "median_note": "median of a second pass with a HIP event after every call",
-                     "max_abs_err": {"out": float(abs(o - ref).max()),
-                                     "lse": float(abs(l - ref_lse).max())}},
+                     "max_abs_err": err},
         "cpu_baseline": cpu,
     }
 
@@ -509,7 +521,6 @@ def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20, nbufs=1):
 
 
 def run_mlx4(args, torch, kp, synth, dev, stream):
-    import oracle
     case = synth.MLX4_DECODE
     LAYERS, NSET = 16, 2   # 16 layers per step (671 MB); two sets alternate (1.34 GB)
     inp = synth.generate(case)
@@ -587,23 +598,27 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
         return step
     (ms16, _), _ = warm_cold(torch, stream, [make_step16(k) for k in range(NSET)], 1, False,
                              args)
-    ref16, _ = oracle.prefix_query(inp.Q, inp.K, inp.V)
-    check_close(out16[LAYERS - 1].cpu().numpy(), ref16, 2e-3, "out")
+    if oracle_leg(args):
+        import oracle
+        ref16, _ = oracle.prefix_query(inp.Q, inp.K, inp.V)
+        check_close(out16[LAYERS - 1].cpu().numpy(), ref16, 2e-3, "out")
     kp.pion_prefix_drop(sid16, -1)
     del out16, lse16
     nbytes16 = LAYERS * case.H_kv * case.N * case.D * 4
 
-    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
-    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
-    ref, ref_lse = oracle.prefix_query(inp.Q, Kh, Vh)
-    o = out.cpu().numpy()
-    for l in (0, LAYERS - 1):
-        check_close(o[l], ref, 2e-3, "out")
-    check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 1e-4, "lse")
     nbytes_layer = case.H_kv * case.N * 160
     nbytes = nbytes_layer * LAYERS
     cpu = None
-    if not args.no_cpu_baseline:
+    if oracle_leg(args):   # the first and last layers against the oracle, then its timing
+        import oracle
+        Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+        Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+        ref, ref_lse = oracle.prefix_query(inp.Q, Kh, Vh)
+        o = out.cpu().numpy()
+        for l in (0, LAYERS - 1):
+            check_close(o[l], ref, 2e-3, "out")
+        check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 1e-4, "lse")
+
         def one_layer():
             oracle.prefix_query(inp.Q, Kh, Vh)
         n, el = cpu_time(one_layer, args.cpu_seconds)
@@ -647,7 +662,6 @@ def run_mlx4(args, torch, kp, synth, dev, stream):
 
 
 def run_sparse(args, torch, kp, synth, dev, stream):
-    import oracle
     case = synth.SPARSE
     inp = synth.generate(case)
     sid = "bench-sparse"
@@ -675,11 +689,13 @@ def run_sparse(args, torch, kp, synth, dev, stream):
     # per slot by the first query, inside the untimed warm-up)
     (ms, _), (wms, _) = warm_cold(torch, stream, [make_step(k) for k in range(NSLOT)], 2,
                                   False, args)
-    ref, _, ref_blocks = oracle.prefix_query_sparse_auto(inp.Q, inp.K, inp.V, case.B,
-                                                         case.K_top, None, inp.K_suf, inp.V_suf)
-    check_close(out.cpu().numpy(), ref, 2e-3, "out")
-    if not (blocks.cpu().numpy() == ref_blocks).all():
-        raise SystemExit("bench sparse blocks disagree with the oracle")
+    if oracle_leg(args):
+        import oracle
+        ref, _, ref_blocks = oracle.prefix_query_sparse_auto(
+            inp.Q, inp.K, inp.V, case.B, case.K_top, None, inp.K_suf, inp.V_suf)
+        check_close(out.cpu().numpy(), ref, 2e-3, "out")
+        if not (blocks.cpu().numpy() == ref_blocks).all():
+            raise SystemExit("bench sparse blocks disagree with the oracle")
     if args.kmean_builds > 0:   # a STORE replaces the slot, so its next query rebuilds K_mean
         K16 = torch.from_numpy(inp.K).to(dev)
         V16 = torch.from_numpy(inp.V).to(dev)
@@ -712,7 +728,6 @@ def run_sparse(args, torch, kp, synth, dev, stream):
 
 
 def run_tiny(args, torch, kp, synth, dev, stream):
-    import oracle
     case = synth.TINY
     inp = synth.generate(case)
     kp.pion_prefix_store("bench-tiny", 0, torch.from_numpy(inp.K).to(dev),
@@ -729,7 +744,9 @@ def run_tiny(args, torch, kp, synth, dev, stream):
 
     t = Timed(torch, stream, step, 1, False)
     ms, _ = t.measure(args.steps, args.warmup)
-    check_close(out.cpu().numpy(), oracle.prefix_query(inp.Q, inp.K, inp.V)[0], 2e-3, "out")
+    if oracle_leg(args):
+        import oracle
+        check_close(out.cpu().numpy(), oracle.prefix_query(inp.Q, inp.K, inp.V)[0], 2e-3, "out")
     kp.pion_prefix_drop("bench-tiny", -1)
     return {"value": ms * 1e3, "unit": "us/query", "ms_per_step": ms, "dtype": "fp16",
             "config": {"workload": "tiny dense query H=2 N=128 D=64 M=1"},
@@ -742,7 +759,6 @@ def run_query_sparse(args, torch, kp, synth, dev, stream):
     Not one of the five headline workloads; it measures the QUERY_SPARSE row. Bytes are
     the gathered K and V rows: H * K_sparse_max * 2 * D * 2."""
     import numpy as np
-    import oracle
     H, N, D, KS = 8, 65536, 128, 2048
     NSLOT = 4   # 4 slots of 268 MB each (1.07 GB)
     inp = synth.generate(synth.DECODE, 21, N=N, H_q=H, H_kv=H, D=D)
@@ -772,11 +788,13 @@ def run_query_sparse(args, torch, kp, synth, dev, stream):
 
     (ms, launch_us), (wms, _) = warm_cold(torch, stream, [make_step(k) for k in range(NSLOT)],
                                           1, False, args)
-    ref, _ = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
-    check_close(out.cpu().numpy(), ref, 2e-3, "out")
     nbytes = H * KS * 2 * D * 2
     cpu = None
-    if not args.no_cpu_baseline:
+    if oracle_leg(args):   # the result against the oracle, then its timing
+        import oracle
+        ref, _ = oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
+        check_close(out.cpu().numpy(), ref, 2e-3, "out")
+
         def one_query():
             oracle.prefix_query_sparse(inp.Q, inp.K, inp.V, idx, counts)
         n, el = cpu_time(one_query, args.cpu_seconds)
@@ -802,7 +820,6 @@ def run_sweep(args, torch, kp, synth, dev, stream):
     at every supported head dim with fp16 slots, and with fp32-resident slots at D = 64,
     128 and 256. One seeded layer per case is stored in all 64 slots."""
     import numpy as np
-    import oracle
     LAYERS, NSET, H, N = 32, 2, 8, 2048
     cases = [(D, kp.PION_KV_FP16) for D in (32, 64, 96, 128, 160, 192, 256, 512)]
     cases += [(D, kp.PION_KV_FP32) for D in (64, 128, 256)]
@@ -832,9 +849,11 @@ def run_sweep(args, torch, kp, synth, dev, stream):
             return step
         ms, launch_us = Timed(torch, stream, [make_step(k) for k in range(NSET)], 1,
                               False).measure(args.steps, args.warmup)
-        ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
-        check_close(out[LAYERS - 1].cpu().numpy(), ref, 1e-4 if f32 else 2e-3, "out")
-        check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 2e-5 if f32 else 1e-4, "lse")
+        if oracle_leg(args):
+            import oracle
+            ref, ref_lse = oracle.prefix_query(inp.Q, inp.K, inp.V)
+            check_close(out[LAYERS - 1].cpu().numpy(), ref, 1e-4 if f32 else 2e-3, "out")
+            check_close(lse[LAYERS - 1].cpu().numpy(), ref_lse, 2e-5 if f32 else 1e-4, "lse")
         kp.pion_prefix_drop(sid, -1)
         nbytes = LAYERS * H * N * D * 2 * (4 if f32 else 2)
         row = {"D": D, "resident": "fp32" if f32 else "fp16", "bytes_per_launch": nbytes,
@@ -870,7 +889,6 @@ def run_vstore(args, torch, kp, synth, dev, stream):
     pion_prefix_warm (K and V of one layer into an fp16 slot, replacing the live slot:
     allocation, two relayout launches, the free of the old slot), host work included."""
     import numpy as np
-    from oracle import vstore as ovs
     L, H, N, D = 32, 8, 2048, 128
     kv = H * D
     NCOPY = 4
@@ -893,10 +911,12 @@ def run_vstore(args, torch, kp, synth, dev, stream):
 
     (ms, launch_us), (wms, _) = warm_cold(torch, stream, [make_step(c) for c in range(NCOPY)],
                                           2 * L, False, args)
-    got = out[1].cpu().numpy()                      # the last launch: layer 31, V
-    want = ovs.fetch_f32(recs[-1], ovs.MLX4G32, kv, 0, N)
-    if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
-        raise SystemExit("bench fetch disagrees with the oracle")
+    if oracle_leg(args):
+        from oracle import vstore as ovs
+        got = out[1].cpu().numpy()                  # the last launch: layer 31, V
+        want = ovs.fetch_f32(recs[-1], ovs.MLX4G32, kv, 0, N)
+        if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
+            raise SystemExit("bench fetch disagrees with the oracle")
     per_launch = N * (rb + 4 * kv)
     nbytes = 2 * L * per_launch
 
@@ -916,7 +936,7 @@ def run_vstore(args, torch, kp, synth, dev, stream):
     kp.pion_prefix_drop(sid, -1)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if oracle_leg(args):
         i = [0]
 
         def one_layer_side():
