@@ -69,11 +69,11 @@ DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h")
                   "sources_sha256": "b44c58d88d35127208492a2ecb519ee7d5a88c8d1c4653739ce9cbd8f4c8439b",
                   "bytes_per_launch": 268750056}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
-# 22,314,843 B and writes 32,153,395 B (the five splits' partials), prefill_merge_kernel<128>
-# reads 33,495,302 B and writes 6,340,608 B (out and lse).
+# 22,314,919 B and writes 32,159,360 B (the five splits' partials), prefill_merge_kernel<128>
+# reads 33,495,353 B and writes 6,340,608 B (out and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "13f0f784ac8c9169ff32900f6b3323a1f17a6e3c115412aeee407cc7d148dc26",
-                   "bytes_per_launch": 94304148}
+                   "sources_sha256": "bdc8735bca9007a49102420ece2d783f154b4703e48e543644c1d68b0ec70c34",
+                   "bytes_per_launch": 94310240}
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
 # reads 671,957,310 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),

@@ -180,7 +180,6 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
   const int split = L % p.n_splits, ts = L / p.n_splits;
   const int hs = ts / p.n_iblk, ib = ts - hs * p.n_iblk;
   const int h = p.order[hs], i0 = ib * BQ;
-  const int tile = h * p.n_iblk + ib;
   const int g = p.hm.m[h];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
