@@ -763,6 +763,34 @@ def test_mfma_prefill_shapes(kp, D, N, M, S_suf):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_mfma_prefill_random_shapes(kp, seed):
+    # Seeded random shapes: every head dim (with and without LDS padding) once without a
+    # suffix and once with a causal suffix (the M queries and up to 200 keys before
+    # them); ragged prefix lengths (tiles and splits ending mid-tile), H_q a multiple of
+    # H_kv. Rows: the first and last of every 128-row block, plus random ones.
+    rng = np.random.default_rng(1000 + seed)
+    D = (64, 96, 128, 160, 192, 256)[seed % 6]
+    H_kv = int(rng.integers(1, 4))
+    H_q = H_kv * int(rng.integers(1, 4))
+    N = int(rng.integers(1, 3000))
+    M = int(rng.integers(32, 300))
+    S_suf = M + int(rng.integers(0, 200)) if seed >= 6 else 0
+    inp = synth.generate(synth.PREFILL, 2000 + seed, N=N, M=M, S_suf=S_suf, H_q=H_q,
+                         H_kv=H_kv, D=D)
+    kp.pion_prefix_store("t", 604, dev(inp.K), dev(inp.V))
+    out, lse = empty((H_q, M, D)), empty((H_q, M))
+    if S_suf:
+        kp.pion_prefix_query_fused("t", 604, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    else:
+        kp.pion_prefix_query("t", 604, dev(inp.Q), out, lse)
+    ends = sorted({i for b in range(0, M, 128) for i in (b, min(b + 127, M - 1))})
+    rows = [(h, i) for h in range(H_q) for i in ends] + \
+        [(int(h), int(i)) for h, i in zip(rng.integers(0, H_q, 24), rng.integers(0, M, 24))]
+    ref, ref_lse = oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf, rows=rows)
+    check(host(out), host(lse), ref, ref_lse, rows=rows)
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("growth", [12.0, 60.0])
 def test_mfma_prefill_running_max_growth(kp, D, growth):
