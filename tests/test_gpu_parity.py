@@ -469,7 +469,12 @@ def sparse_call(kp, sid, layer, inp, B, K_top, H_kv, suffix=True, head_map=None)
     return host(out), host(lse), host(blocks)
 
 
-def test_sparse_auto_full_size(kp):
+@pytest.mark.parametrize("force", ["PION_GQA_MFMA", "PION_NO_GQA_MFMA", None])
+def test_sparse_auto_full_size(kp, monkeypatch, force):
+    # the attention over the chosen blocks on the grouped-query MFMA kernel, on the
+    # vector kernel, and on the default choice
+    if force:
+        monkeypatch.setenv(force, "1")
     case = synth.SPARSE
     inp = synth.generate(case)
     kp.pion_prefix_store("t", 11, dev(inp.K), dev(inp.V))
