@@ -768,6 +768,26 @@ def test_mfma_prefill_shapes(kp, D, N, M, S_suf):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_mfma_prefill_single_split(kp, monkeypatch, D):
+    # one split per row block: the kernel writes normalized out and lse itself, with no
+    # merge kernel (forced here; also the plan for at most 32 keys, the second call)
+    monkeypatch.setenv("PION_PREFILL_SPLITS", "1")
+    inp = synth.generate(synth.PREFILL, 15, N=1000, M=200, S_suf=250, D=D, H_q=4, H_kv=2)
+    kp.pion_prefix_store("t", 605, dev(inp.K), dev(inp.V))
+    out, lse = empty((4, 200, D)), empty((4, 200))
+    kp.pion_prefix_query_fused("t", 605, dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf), out, lse)
+    assert kp.pion_prefix_last_plan() == f"prefill_kernel<{D}>"
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, inp.K, inp.V, inp.K_suf, inp.V_suf))
+    monkeypatch.delenv("PION_PREFILL_SPLITS")
+    inp = synth.generate(synth.PREFILL, 16, N=20, M=64, S_suf=0, D=D, H_q=4, H_kv=2)
+    kp.pion_prefix_store("t", 606, dev(inp.K), dev(inp.V))
+    out, lse = empty((4, 64, D)), empty((4, 64))
+    kp.pion_prefix_query("t", 606, dev(inp.Q), out, lse)
+    assert kp.pion_prefix_last_plan() == f"prefill_kernel<{D}>"
+    check(host(out), host(lse), *oracle.prefix_query(inp.Q, inp.K, inp.V))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_mfma_prefill_random_shapes(kp, seed):
     # Seeded random shapes: every head dim (with and without LDS padding) once without a
