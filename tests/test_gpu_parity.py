@@ -891,3 +891,52 @@ def test_vstore_fetch_bench_shape(kp):
     kp.pion_vstore_fetch_f32(dev(rec), ovs.MLX4G32, 1024, 0, 2048, out)
     want = ovs.fetch_f32(rec, ovs.MLX4G32, 1024, 0, 2048)
     np.testing.assert_array_equal(host(out).view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ HIP graph capture
+def test_graph_replays_match_eager_calls(kp):
+    # Two decode calls whose keys are split (partial stores, ticket, in-kernel merge) and
+    # a fused prefill (split kernel and merge kernel), captured into one HIP graph. Each
+    # replay, with eager work and synchronizations between replays, must reproduce the
+    # eager calls bit for bit: the ticket counters reset themselves inside the kernels.
+    import torch
+    s = torch.cuda.Stream()
+    dec = [synth.generate(synth.DECODE, l) for l in range(2)]
+    for l, inp in enumerate(dec):
+        kp.pion_prefix_store("t", 700 + l, dev(inp.K), dev(inp.V))
+    pre = synth.generate(synth.PREFILL, 17, N=500, M=64, S_suf=64, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 702, dev(pre.K), dev(pre.V))
+    Qd = [dev(inp.Q) for inp in dec]
+    Qp, Ks, Vs = dev(pre.Q), dev(pre.K_suf), dev(pre.V_suf)
+    outs = [empty((8, 1, 128)), empty((8, 1)), empty((8, 1, 128)), empty((8, 1)),
+            empty((6, 64, 128)), empty((6, 64))]
+
+    def calls():
+        kp.pion_prefix_query("t", 700, Qd[0], outs[0], outs[1], stream=s)
+        kp.pion_prefix_query("t", 701, Qd[1], outs[2], outs[3], stream=s)
+        kp.pion_prefix_query_fused("t", 702, Qp, Ks, Vs, outs[4], outs[5], stream=s)
+
+    with torch.cuda.stream(s):
+        calls()                       # eager: also sets up the stream's workspace
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    check(host(ref[0]), host(ref[1]), *oracle.prefix_query(dec[0].Q, dec[0].K, dec[0].V))
+    check(host(ref[4]), host(ref[5]), *oracle.prefix_query_fused(pre.Q, pre.K, pre.V,
+                                                                 pre.K_suf, pre.V_suf))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    x_out, x_lse = empty((8, 1, 128)), empty((8, 1))
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"replay {rep} differs from the eager call"
+        kp.pion_prefix_query("t", 701, Qd[1], x_out, x_lse)   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(x_out, ref[2])
+    for l in range(3):
+        kp.pion_prefix_drop("t", 700 + l)
