@@ -940,3 +940,34 @@ def test_graph_replays_match_eager_calls(kp):
         assert torch.equal(x_out, ref[2])
     for l in range(3):
         kp.pion_prefix_drop("t", 700 + l)
+
+
+def test_concurrent_queries_on_four_streams(kp):
+    # split queries (partial stores, tickets, merges) and a fused prefill issued on four
+    # streams at once, no synchronization between the streams: each stream has its own
+    # workspace and ticket counters, so the launches may overlap freely
+    import torch
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    layers = [synth.generate(synth.DECODE, 20 + l, N=1500 + 300 * l) for l in range(8)]
+    for l, inp in enumerate(layers):
+        kp.pion_prefix_store("t", 720 + l, dev(inp.K), dev(inp.V))
+    pre = synth.generate(synth.PREFILL, 18, N=700, M=96, S_suf=96, H_q=6, H_kv=2)
+    kp.pion_prefix_store("t", 730, dev(pre.K), dev(pre.V))
+    Qs = [dev(inp.Q) for inp in layers]
+    outs = [(empty((8, 1, 128)), empty((8, 1))) for _ in range(16)]
+    pout, plse = empty((6, 96, 128)), empty((6, 96))
+    torch.cuda.synchronize()
+    for k in range(16):                              # two rounds over the eight layers
+        l, s = k % 8, streams[k % 4]
+        kp.pion_prefix_query("t", 720 + l, Qs[l], outs[k][0], outs[k][1], stream=s)
+        if k == 5:
+            kp.pion_prefix_query_fused("t", 730, dev(pre.Q), dev(pre.K_suf), dev(pre.V_suf),
+                                       pout, plse, stream=s)
+    torch.cuda.synchronize()
+    for k in range(16):
+        inp = layers[k % 8]
+        check(host(outs[k][0]), host(outs[k][1]), *oracle.prefix_query(inp.Q, inp.K, inp.V))
+    check(host(pout), host(plse), *oracle.prefix_query_fused(pre.Q, pre.K, pre.V, pre.K_suf,
+                                                             pre.V_suf))
+    for l in range(9):
+        kp.pion_prefix_drop("t", 720 + l if l < 8 else 730)
