@@ -971,3 +971,48 @@ def test_concurrent_queries_on_four_streams(kp):
                                                              pre.V_suf))
     for l in range(9):
         kp.pion_prefix_drop("t", 720 + l if l < 8 else 730)
+
+
+def test_mlx4g32_store_on_one_stream_query_on_another(kp):
+    # the store quantizes on its stream; a query on another stream, issued at once, waits
+    # for the codes (the slot's ready event)
+    import torch
+    inp = synth.generate(synth.MLX4_DECODE, 6, N=5000, H_q=6, H_kv=2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    K, V, Q = dev(inp.K), dev(inp.V), dev(inp.Q)
+    torch.cuda.synchronize()
+    out, lse = empty((6, 1, 128)), empty((6, 1))
+    kp.pion_prefix_store("t", 16, K, V, kp.PION_KV_MLX4G32, stream=s1)
+    kp.pion_prefix_query("t", 16, Q, out, lse, head_map=inp.head_map, stream=s2)
+    torch.cuda.synchronize()
+    Kh = oracle.dequantize(*oracle.quantize(inp.K.reshape(-1, 128))).reshape(inp.K.shape)
+    Vh = oracle.dequantize(*oracle.quantize(inp.V.reshape(-1, 128))).reshape(inp.V.shape)
+    check(host(out), host(lse), *oracle.prefix_query(inp.Q, Kh, Vh, inp.head_map))
+    kp.pion_prefix_drop("t", 16)
+
+
+def test_sparse_auto_block_means_shared_across_streams(kp):
+    # the first query builds the slot's block means on its stream; a second query on
+    # another stream, issued without waiting, must wait for that build (the cache's
+    # ready event) and pick the same blocks
+    import torch
+    case = synth.SPARSE
+    inp = synth.generate(case, 3, N=16384, H_q=8, H_kv=1, D=256, n_needles=8)
+    kp.pion_prefix_store("t", 17, dev(inp.K), dev(inp.V))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    Q, Ks, Vs = dev(inp.Q), dev(inp.K_suf), dev(inp.V_suf)
+    res = []
+    torch.cuda.synchronize()
+    for s in (s1, s2):
+        out, lse = empty((8, 256)), empty((8,))
+        blocks = torch.full((1, case.K_top), -7, dtype=torch.int32, device="cuda")
+        kp.pion_prefix_query_sparse_auto("t", 17, Q, case.B, case.K_top, out, lse, blocks, Ks, Vs,
+                                         H_kv=1, stream=s)
+        res.append((out, lse, blocks))
+    torch.cuda.synchronize()
+    ref, ref_lse, ref_blocks = oracle.prefix_query_sparse_auto(
+        inp.Q, inp.K, inp.V, case.B, case.K_top, None, inp.K_suf, inp.V_suf)
+    for out, lse, blocks in res:
+        np.testing.assert_array_equal(host(blocks), ref_blocks)
+        check(host(out), host(lse), ref, ref_lse)
+    kp.pion_prefix_drop("t", 17)
