@@ -1016,3 +1016,25 @@ def test_sparse_auto_block_means_shared_across_streams(kp):
         np.testing.assert_array_equal(host(blocks), ref_blocks)
         check(host(out), host(lse), ref, ref_lse)
     kp.pion_prefix_drop("t", 17)
+
+
+def test_store_replacing_a_slot_while_a_query_reads_it(kp):
+    # a query on one stream, then at once a store that replaces the same slot from another
+    # stream: the query reads the old K/V to the end (the old memory is released only
+    # after the work queued on it), and a query after the store sees the new K/V
+    import torch
+    old = synth.generate(synth.DECODE, 7, N=30000, H_q=8, H_kv=8)
+    new = synth.generate(synth.DECODE, 8, N=30000, H_q=8, H_kv=8)
+    kp.pion_prefix_store("t", 18, dev(old.K), dev(old.V))
+    Knew, Vnew, Q = dev(new.K), dev(new.V), dev(old.Q)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out_a, lse_a = empty((8, 1, 128)), empty((8, 1))
+    out_b, lse_b = empty((8, 1, 128)), empty((8, 1))
+    kp.pion_prefix_query("t", 18, Q, out_a, lse_a, stream=s1)
+    kp.pion_prefix_store("t", 18, Knew, Vnew, stream=s2)
+    kp.pion_prefix_query("t", 18, Q, out_b, lse_b, stream=s2)
+    torch.cuda.synchronize()
+    check(host(out_a), host(lse_a), *oracle.prefix_query(old.Q, old.K, old.V))
+    check(host(out_b), host(lse_b), *oracle.prefix_query(old.Q, new.K, new.V))
+    kp.pion_prefix_drop("t", 18)
