@@ -974,7 +974,7 @@ def _finish_roofline(roof):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     # Inputs of the default run, and the oracle timed on the host cores, before anything

@@ -65,7 +65,7 @@ enum {
     PION_OK = 0,
     PION_ERR_NOT_FOUND = -1,   /* no slot for (sid, layer), warm or cold */
     PION_ERR_INVALID = -2,     /* bad argument: null pointer, shape mismatch, range */
-    PION_ERR_UNSUPPORTED = -3, /* valid request this build does not implement (D, ...) */
+    PION_ERR_UNSUPPORTED = -3, /* valid request the library does not implement (D, ...) */
     PION_ERR_NOMEM = -4,       /* device memory short with nothing left to demote, or
                                   a slot larger than the byte budget */
     PION_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
