@@ -37,7 +37,9 @@ is reported beside it, labelled.
 The default run reports both halves of the metric in one JSON line: `value` is the M=1
 decode figure above (GB/s), and `batched_q` the fused batched-Q prefill (--config 3's
 workload, TFLOP/s) with its own roofline and CPU baseline; `stream_ceiling` is a plain
-streaming read of 1 GiB timed in the same run (the achievable HBM read rate).
+streaming read of 1 GiB timed in the same run (the achievable HBM read rate), and
+`batched_q.mfma_ceiling` fp16 MFMA products alone on every SIMD (the achievable matrix
+rate under full load).
 
 cpu_baseline (default run and --config 3): the fp64 numpy oracle as it stands, timed on
 the host before the GPU is touched: worker processes (one BLAS thread each) over all
@@ -518,6 +520,30 @@ def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20, nbufs=1):
                     f"loads, {reps} launches back to back"
                     + (f" over {nbufs} buffers in rotation" if nbufs > 1 else "")
                     + " (cold: past the memory-side cache)"}
+
+
+def mfma_ceiling(torch, kp, dev, stream, iters=2048, reps=20):
+    """fp16 MFMA products alone on every SIMD (four waves per SIMD, no memory traffic),
+    `reps` launches of about 0.5 ms back to back, as long as a batched-Q run: the dense
+    fp16 rate the chip sustains under full matrix load, timed with HIP events."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            flops = kp.pion_bench_mfma_peak(iters, sink)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            kp.pion_bench_mfma_peak(iters, sink)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"value": round(tflops, 1), "unit": "TFLOP/s",
+            "frac_of_peak": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(us, 2), "kernel": "mfma_peak_kernel",
+            "note": f"v_mfma_f32_32x32x16_f16 alone, {iters} rounds of 4 independent products "
+                    f"per wave, 4 waves per SIMD, {reps} launches back to back"}
 
 
 def run_mlx4(args, torch, kp, synth, dev, stream):
@@ -1012,10 +1038,12 @@ def main():
             _finish_roofline(bq["roofline"])
             r["batched_q"] = {k: (round(v, 4) if isinstance(v, float) else v)
                               for k, v in bq.items()}
+            r["batched_q"]["mfma_ceiling"] = mfma_ceiling(torch, kp, dev, stream)
             r["stream_ceiling"] = stream_ceiling(torch, kp, dev, stream)
     elif args.config == 3:
         r = run_prefill(args, torch, kp, synth, dev, stream, inp=pre.get("prefill"),
                         cpu=cpu.get("prefill"))
+        r["mfma_ceiling"] = mfma_ceiling(torch, kp, dev, stream)
     else:
         runner = {1: run_tiny, 4: run_mlx4, 5: run_sparse, 6: run_query_sparse,
                   7: run_vstore, 8: run_sweep}[args.config]
@@ -1040,7 +1068,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": r["cpu_baseline"],
     }
-    for extra in ("warm", "batched_q", "stream_ceiling", "single_query", "warm_call",
+    for extra in ("warm", "batched_q", "stream_ceiling", "mfma_ceiling", "single_query",
+                  "warm_call",
                   "quantize", "fp16_resident", "sweep", "kmean_read_ceiling"):
         if extra in r:
             line[extra] = r[extra]

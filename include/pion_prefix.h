@@ -297,6 +297,15 @@ const char *pion_prefix_last_plan(void);
  * multiple of 16 (0 is a no-op); buf 16-byte aligned. Errors: INVALID, HIP. */
 int pion_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
+/* Measurement aid (not a wire form): `iters` rounds of four independent fp16 matrix
+ * products (v_mfma_f32_32x32x16_f16, 32,768 flops each, the instruction of the batched-Q
+ * kernels) in every wave of four 256-lane workgroups per compute unit, and nothing else -
+ * the dense fp16 rate the chip sustains under full matrix load, which the batched-Q
+ * kernels are compared with beside the rated peak. *flops (a host double) receives the
+ * launch's flop count. sink is one device uint32 the kernel may write (it does not).
+ * Errors: INVALID (iters < 1, a null or misaligned pointer), HIP. */
+int pion_bench_mfma_peak(int iters, double *flops, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,7 @@ SIGNATURES = {
     "pion_status_str": (ctypes.c_char_p, [_int]),
     "pion_prefix_last_plan": (ctypes.c_char_p, []),
     "pion_bench_stream_read": (_int, [_vp, ctypes.c_int64, _vp, _vp]),
+    "pion_bench_mfma_peak": (_int, [_int, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -347,6 +348,17 @@ def pion_bench_stream_read(buf, sink, stream=None) -> int:
     rc = lib().pion_bench_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
                                       _dev(sink, torch.int32, "sink", (1,)), _stream(stream))
     return _check(rc, "pion_bench_stream_read")
+
+
+def pion_bench_mfma_peak(iters, sink, stream=None) -> float:
+    """Measurement aid: one launch of `iters` rounds of fp16 MFMA products on every SIMD;
+    returns the launch's flop count. sink is a 1-element int32 device tensor."""
+    import torch
+    flops = ctypes.c_double(0.0)
+    rc = lib().pion_bench_mfma_peak(int(iters), ctypes.byref(flops),
+                                    _dev(sink, torch.int32, "sink", (1,)), _stream(stream))
+    _check(rc, "pion_bench_mfma_peak")
+    return flops.value
 
 
 __all__ = [n for n in SIGNATURES if n != "pion_status_str"] + [

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libpion_prefix.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_partial.hip", "attn_mlx4.hip", "attn_mlx4_mfma.hip", "attn_gqa_mfma.hip", "prefill_mfma.hip", "mlx4g32.hip", "sparse.hip", "vstore.hip", "stream_read.hip", "noalloc.hip", "pion_prefix.cpp"]
+SOURCES = ["attn_partial.hip", "attn_mlx4.hip", "attn_mlx4_mfma.hip", "attn_gqa_mfma.hip", "prefill_mfma.hip", "mlx4g32.hip", "sparse.hip", "vstore.hip", "stream_read.hip", "mfma_peak.hip", "noalloc.hip", "pion_prefix.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,

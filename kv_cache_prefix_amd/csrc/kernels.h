@@ -217,6 +217,9 @@ hipError_t launch_rows_to_mlx4_slot(const void *rows, int64_t N, int H, int D, u
 // Read `bytes` (a multiple of 16) at buf once with 16-byte non-temporal loads and
 // nothing else (the streaming-read ceiling); sink receives at most one word.
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
+// iters rounds of four independent fp16 MFMA products in every wave of four 256-lane
+// workgroups per CU (the sustained MFMA ceiling); *flops (host) gets the launch's flops.
+hipError_t launch_mfma_peak(int iters, double *flops, uint32_t *sink, hipStream_t s);
 
 // Ticket counters of a workspace: one per workgroup row of a split launch.
 constexpr int kMaxCounters = 65536;

@@ -785,6 +785,14 @@ int pion_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void 
                                                                                  : PION_ERR_HIP;
 }
 
+int pion_bench_mfma_peak(int iters, double *flops, uint32_t *sink, void *stream) {
+  plan_begin();
+  if (iters < 1 || !flops || !sink || !aligned(sink, 4)) return PION_ERR_INVALID;
+  if (!on_device(sink)) return PION_ERR_INVALID;
+  return launch_mfma_peak(iters, flops, sink, (hipStream_t)stream) == hipSuccess ? PION_OK
+                                                                                : PION_ERR_HIP;
+}
+
 const char *pion_status_str(int status) {
   switch (status) {
     case PION_OK: return "ok";

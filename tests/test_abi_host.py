@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert set(names) == set(kp.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
@@ -43,6 +43,10 @@ def test_last_plan_and_stream_read_without_a_gpu(lib):
     assert lib.pion_bench_stream_read(None, 17, None, None) == kp.PION_ERR_INVALID
     assert lib.pion_bench_stream_read(None, 0, None, None) == kp.PION_OK
     assert kp.pion_prefix_last_plan() == ""
+    flops = ctypes.c_double(-1.0)
+    assert lib.pion_bench_mfma_peak(0, ctypes.byref(flops), None, None) == kp.PION_ERR_INVALID
+    assert lib.pion_bench_mfma_peak(8, None, None, None) == kp.PION_ERR_INVALID
+    assert flops.value == -1.0 and kp.pion_prefix_last_plan() == ""
 
 
 def test_noalloc_query_argument_validation(lib):
