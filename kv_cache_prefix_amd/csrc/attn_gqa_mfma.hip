@@ -58,12 +58,13 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
   const int z = blockIdx.z, y = blockIdx.y;
-  const Prob b = get_prob(p, z, y);
+  int hg;
+  Prob b;
+  const Group gr = entry_group(p, z, y, hg, b);
   const int x = blockIdx.x + p.x_begin;
   if (x >= b.S_total) return;  // this problem has fewer spans than the grid
-  const int hg = y / p.M, qi = y - hg * p.M;
-  const int g = p.rg.g[hg], cnt = p.rg.cnt[hg];
-  const uint8_t *heads = p.rg.heads[hg];
+  const int qi = y - hg * p.M;
+  const int g = gr.g, cnt = gr.cnt;
 
   // the span's segments: start key, suffix flag and cumulative sub-tile counts
   const int seg0 = x * p.seg_per_span, nseg = min(seg0 + p.seg_per_span, b.n_seg) - seg0;
@@ -147,11 +148,11 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
     cur = locate(k);
     issue(cur, 0);
   }
-  // Q^T operand: row col is q-head heads[col] (zero past the group)
+  // Q^T operand: row col is q-head gr.head(col) (zero past the group)
   half8 qb[NDS];
   {
     const bool live = col < cnt;
-    const uint16_t *qrow = (const uint16_t *)b.Q + ((size_t)heads[live ? col : 0] * p.M + qi) * D;
+    const uint16_t *qrow = (const uint16_t *)b.Q + ((size_t)gr.head(live ? col : 0) * p.M + qi) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       const half8 v = *(const half8 *)(qrow + 16 * ds + 8 * hl);
@@ -259,16 +260,16 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
       lw = __builtin_fmaf(f, sm.wm.l[w][r], lw);
     }
     if (b.S_total == 1) {  // the only span of its rows: final output, no merge
-      const size_t row = (size_t)heads[r] * p.M + qi;
+      const size_t row = (size_t)gr.head(r) * p.M + qi;
       const float inv = 1.f / lw;
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
       if (dq == 0 && b.lse) b.lse[row] = (mm + __log2f(lw)) * 0.69314718055994530942f;
     } else {
-      store_part(pr, heads[r], x, dq, a);
-      if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+      store_part(pr, gr.head(r), x, dq, a);
+      if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
 }
 
 template <int D>

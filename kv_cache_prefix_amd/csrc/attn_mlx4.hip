@@ -133,12 +133,13 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
   const int g = lane % NGP, kk = lane / NGP;
   const bool grp = g < NG;  // this lane owns a group of its keys
   const int z = blockIdx.z, y = blockIdx.y;
-  const Prob b = get_prob(p, z, y);
+  int hg;
+  Prob b;
+  const Group gr = entry_group(p, z, y, hg, b);
   const int x = blockIdx.x + p.x_begin;
   if (x >= b.S_total) return;  // this problem has fewer spans than the grid
-  const int hg = y / p.M, qi = y - hg * p.M;
-  const int gk = p.rg.g[hg], cnt = p.rg.cnt[hg];
-  const uint8_t *heads = p.rg.heads[hg];
+  const int qi = y - hg * p.M;
+  const int gk = gr.g, cnt = gr.cnt;
   Span sp = get_segment(p, x, b.pre_splits, b.N, gk, qi);  // one segment per span here
   if (sp.suffix) sp.j1 = sp.j0;  // suffix spans belong to the fp16 kernel
 
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
   float qsq[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int h = heads[r < cnt ? r : 0];
+    const int h = gr.head(r < cnt ? r : 0);
     const uint4 *qp =
         (const uint4 *)((const uint16_t *)b.Q + ((size_t)h * p.M + qi) * D + 32 * (grp ? g : 0));
     float qs = 0.f;
@@ -382,11 +383,11 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
       lw = __builtin_fmaf(f, sm.l[q2][r], lw);
       a += f * *(const f32x4 *)&sm.acc[q2][r][4 * dq];
     }
-    store_part(pr, heads[r], x, dq, a);
-    if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+    store_part(pr, gr.head(r), x, dq, a);
+    if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
   }
   // (ticket_and_merge's barrier precedes any reuse of acc as merge scratch)
-  ticket_and_merge<D, NT>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
 }
 
 // 8 waves per workgroup (two per SIMD: one wave alone issues VALU work at about half

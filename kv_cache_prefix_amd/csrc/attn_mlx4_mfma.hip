@@ -117,12 +117,13 @@ __global__ __launch_bounds__(64 * NW) void mlx4_mfma_kernel(PartialParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 15, hb = lane >> 4;
   const int z = blockIdx.z, y = blockIdx.y;
-  const Prob b = get_prob(p, z, y);
+  int hg;
+  Prob b;
+  const Group gr = entry_group(p, z, y, hg, b);
   const int x = blockIdx.x + p.x_begin;
   if (x >= b.S_total) return;  // this problem has fewer spans than the grid
-  const int hg = y / p.M, qi = y - hg * p.M;
-  const int gk = p.rg.g[hg], cnt = p.rg.cnt[hg];
-  const uint8_t *heads = p.rg.heads[hg];
+  const int qi = y - hg * p.M;
+  const int gk = gr.g, cnt = gr.cnt;
   Span sp = get_segment(p, x, b.pre_splits, b.N, gk, qi);
   if (sp.suffix) sp.j1 = sp.j0;  // suffix spans belong to the fp16 kernel
 
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_mfma_kernel(PartialParams p) {
     const int gq = n >> 2, rq = n & 3;
     const bool live = gq == hb && rq < cnt;
     const uint4 *qp = (const uint4 *)((const uint16_t *)b.Q +
-                                      ((size_t)heads[live ? rq : 0] * p.M + qi) * D + 32 * hb);
+                                      ((size_t)gr.head(live ? rq : 0) * p.M + qi) * D + 32 * hb);
     uint16_t e[32];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_mfma_kernel(PartialParams p) {
   for (int r = 0; r < 4; ++r) {
     const bool lr = r < cnt;
     const uint4 *qp = (const uint4 *)((const uint16_t *)b.Q +
-                                      ((size_t)heads[lr ? r : 0] * p.M + qi) * D + 32 * hb);
+                                      ((size_t)gr.head(lr ? r : 0) * p.M + qi) * D + 32 * hb);
     float qs = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -389,16 +390,16 @@ __global__ __launch_bounds__(64 * NW) void mlx4_mfma_kernel(PartialParams p) {
       lw = __builtin_fmaf(f, sm.wm.l[w][r], lw);
     }
     if (b.S_total == 1) {  // the only span of its rows: final output, no merge
-      const size_t row = (size_t)heads[r] * p.M + qi;
+      const size_t row = (size_t)gr.head(r) * p.M + qi;
       const float inv = lw > 0.f ? 1.f / lw : 0.f;
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
       if (dq == 0 && b.lse) b.lse[row] = lw > 0.f ? (mm + __log2f(lw)) * 0.69314718055994530942f : -INFINITY;
     } else {
-      store_part(pr, heads[r], x, dq, a);
-      if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+      store_part(pr, gr.head(r), x, dq, a);
+      if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
 }
 
 }  // namespace

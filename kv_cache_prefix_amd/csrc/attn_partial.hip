@@ -98,7 +98,7 @@ struct Scratch {
 template <int D, int R, int LPR, int NW>
 __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Scratch<D, R, NW> &sm,
                                        float (&m)[R], float (&l)[R], float (&acc)[R][8],
-                                       const uint8_t *heads, int cnt, int qi, int x) {
+                                       const Group &gr, int qi, int x) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sub = lane % LPR, kk = lane / LPR;
@@ -122,7 +122,7 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
   __syncthreads();
   const PartRsrc pr = part_rsrc(p, b, qi);
   constexpr int DQ = D / 4;
-  for (int t = threadIdx.x; t < cnt * DQ; t += 64 * NW) {
+  for (int t = threadIdx.x; t < gr.cnt * DQ; t += 64 * NW) {
     const int r = t / DQ, dq = t - r * DQ;
     float mm = ws.m[0][r];
 #pragma unroll
@@ -136,17 +136,17 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
       lw = __builtin_fmaf(f, ws.l[w][r], lw);
     }
     if (b.S_total == 1) {  // the only span of its rows: final output, no merge
-      const size_t row = (size_t)heads[r] * p.M + qi;
+      const size_t row = (size_t)gr.head(r) * p.M + qi;
       const float inv = lw > 0.f ? 1.f / lw : 0.f;  // no key at all: out 0, lse -inf
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
       if (dq == 0 && b.lse)
         b.lse[row] = lw > 0.f ? (mm + __log2f(lw)) * 0.69314718055994530942f : -INFINITY;
     } else {
-      store_part(pr, heads[r], x, dq, a);
-      if (dq == 0) store_ml(pr, heads[r], x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
+      store_part(pr, gr.head(r), x, dq, a);
+      if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, heads, cnt, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, gr, qi, sm.ms, sm.last);
 }
 
 // One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.
@@ -180,17 +180,18 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(PartialParams p) {
   const int sub = lane % LPR, kk = lane / LPR;
   const bool dims = sub < D / 8;  // this lane holds 8 dims of a row
   const int z = blockIdx.z, y = blockIdx.y;
-  const Prob b = get_prob(p, z, y);
+  int hg;
+  Prob b;
+  const Group gr = entry_group(p, z, y, hg, b);
   const int x = blockIdx.x + p.x_begin;
   if (x >= b.S_total) return;  // this problem has fewer spans than the grid
-  const int hg = y / p.M, qi = y - hg * p.M;
-  const int g = p.rg.g[hg], cnt = p.rg.cnt[hg];
-  const uint8_t *heads = p.rg.heads[hg];
+  const int qi = y - hg * p.M;
+  const int g = gr.g, cnt = gr.cnt;
   // q of each row: this lane's 8 values
   QRegs<F32, R> qr;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int h = heads[r < cnt ? r : 0];
+    const int h = gr.head(r < cnt ? r : 0);
     const uint4 *qp =
         (const uint4 *)((const char *)b.Q + (((size_t)h * p.M + qi) * D + sub * 8) * ESZ);
 #pragma unroll
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(PartialParams p) {
     Span sp = get_segment(p, sgi, b.pre_splits, b.N, g, qi);
     if (!sp.suffix && p.fmt == 1) continue;  // an mlx4g32 prefix has its own kernel
     if constexpr (GATHER) {  // list positions [j0, j1) of q-head heads[0]'s token list
-      const int h = heads[0];
+      const int h = gr.head(0);
       sp.j1 = min(sp.j1, max(sp.j0, min(p.gcount[h], p.gmax)));
       __syncthreads();  // the previous segment is done with gsp
       for (int t = threadIdx.x; t < sp.j1 - sp.j0; t += 64 * NW)
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split_kernel(PartialParams p) {
       base = next;
     }
   }
-  finish<D, R, LPR, NW>(p, b, sm, m, l, acc, heads, cnt, qi, x);
+  finish<D, R, LPR, NW>(p, b, sm, m, l, acc, gr, qi, x);
 }
 
 // fp32 (slot format 2) tiles hold twice the bytes per key, so half the keys per lane

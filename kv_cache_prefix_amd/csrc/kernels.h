@@ -17,13 +17,15 @@ constexpr int kRowsPerGroup = 8;   // q-heads sharing one kv-head read per workg
 
 // Groups of up to kRowsPerGroup q-heads that read the same kv-head. A workgroup of the
 // partial-attention kernel serves one group at one query index, so the K/V bytes it
-// streams are shared by every q-head of the group (GQA).
+// streams are shared by every q-head of the group (GQA). Group i: gc[i] = kv-head |
+// rows << 8; heads[i] = its q-heads, row r in byte r of the 64-bit word. Whole words, so
+// a kernel reads its group with two scalar loads at entry.
 struct RowGroups {
   int n;
-  uint8_t g[kMaxHeads];
-  uint8_t cnt[kMaxHeads];
-  uint8_t heads[kMaxHeads][kRowsPerGroup];
+  uint32_t gc[kMaxHeads];
+  uint64_t heads[kMaxHeads];
 };
+static_assert(kRowsPerGroup <= 8, "a group's q-heads are the bytes of one 64-bit word");
 
 constexpr int kMaxBatch = 64;     // problems (layers) per launch
 
@@ -130,8 +132,6 @@ struct PartialParams {
   int waves;              // waves per workgroup of the fp16 kernel: 4, or 8 (rows <= 4)
   float qscale;           // log2(e) / sqrt(D)
   int n_prob;
-  const void *kv_base[kMaxBatch];
-  int N[kMaxBatch];
   const void *Q;          // fp16 (fp32 for an fp32 slot) [n_prob][H_q, M, D]
   size_t q_stride;
   float *out;             // [n_prob][H_q, M, D]
@@ -155,6 +155,14 @@ struct PartialParams {
   size_t part_stride, ml_stride;
   int *counters;
   int y_groups;
+  // (the scalars and pointers above come first: the few cache lines every workgroup
+  // reads at entry; then the per-problem and per-group tables, of which it reads one
+  // entry each)
+  const void *kv_base[kMaxBatch];
+  int N[kMaxBatch];
+  // per problem: its prefix segments | its spans (S_total) << 16, both below 2^16;
+  // computed by the host, so a workgroup knows its problem's shape from two loads
+  uint32_t spans[kMaxBatch];
   RowGroups rg;
 };
 
@@ -178,10 +186,9 @@ hipError_t launch_mlx4_mfma(const PartialParams &p, int rows_per_group, int x_co
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
 // causal suffix (bottom-right aligned). A workgroup serves (tile, split): tile = (q-head,
 // block of 128 query rows), split = a range of split_keys tokens of the concatenated key
-// index [0, N + S_suf). With n_splits > 1 the splits' partials (acc: [tile][n_splits]
-// [128 * D] in the kernel's register layout; m, l: [H_q*M][n_splits]) merge in the workgroup that draws the last ticket of each tile
-// (counters[tile]) once done[tile] counts the others' stores; both are zero before a
-// launch and left zero.
+// index [0, N + S_suf). With n_splits > 1 the splits store partials (acc: [tile][n_splits]
+// [128 * D] in the kernel's register layout; m, l: [H_q*M][n_splits]) and
+// prefill_merge_kernel, launched next on the same stream, merges them into out and lse.
 // The 1-D grid is ordered so that the workgroups of one kv-head share an XCD:
 // order[] lists the q-heads grouped by kv-head.
 struct PrefillParams {

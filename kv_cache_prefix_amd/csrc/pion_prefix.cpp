@@ -325,18 +325,32 @@ int build_groups(const std::vector<int> &hm, int H_kv, int cap, RowGroups &rg) {
   memset(&rg, 0, sizeof(rg));
   int maxcnt = 0;
   for (int g = 0; g < H_kv; ++g) {
-    int cur = -1;
+    int cur = -1, cnt = 0;
     for (int h = 0; h < (int)hm.size(); ++h) {
       if (hm[h] != g) continue;
-      if (cur < 0 || rg.cnt[cur] == cap) {
+      if (cur < 0 || cnt == cap) {
         cur = rg.n++;
-        rg.g[cur] = (uint8_t)g;
+        cnt = 0;
       }
-      rg.heads[cur][rg.cnt[cur]++] = (uint8_t)h;
-      maxcnt = std::max(maxcnt, (int)rg.cnt[cur]);
+      rg.heads[cur] |= (uint64_t)h << (8 * cnt);  // row cnt of the group
+      ++cnt;
+      rg.gc[cur] = (uint32_t)g | (uint32_t)cnt << 8;
+      maxcnt = std::max(maxcnt, cnt);
     }
   }
   return maxcnt;
+}
+
+// The per-problem segment and span counts the kernels read (p.spans), once
+// seg_per_span and the prefix chunking are set: a problem's prefix segments are its
+// selected blocks, or its token-list positions or keys in chunks of pre_chunk.
+void fill_spans(PartialParams &p) {
+  for (int z = 0; z < p.n_prob; ++z) {
+    const int keys = p.gidx ? p.gmax : p.N[z];
+    const int pre = p.blocks ? p.n_sel : (keys + p.pre_chunk - 1) / p.pre_chunk;
+    const int total = (pre + p.suf_splits + p.seg_per_span - 1) / p.seg_per_span;
+    p.spans[z] = (uint32_t)pre | (uint32_t)total << 16;
+  }
 }
 
 int pow2_at_least(int n) {
@@ -553,6 +567,7 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
   if (mlx4) {
     p.x_begin = 0;
     p.seg_per_span = 1;
+    fill_spans(p);
     // head dim 128: the MFMA kernel (PION_NO_MLX4_MFMA keeps the vector kernel)
     const bool mm = c.D == 128 && !getenv_flag("PION_NO_MLX4_MFMA");
     e = mm ? launch_mlx4_mfma(p, grp_rows, pre_max, st) : launch_partial_mlx4(p, grp_rows, pre_max, st);
@@ -586,9 +601,11 @@ int run_attention(const std::vector<const Slot *> &slots, const AttnCall &c, hip
       }();
       const long long one_span = (long long)(c.D == 256 ? 2 : 4) * 32 * one_span_sub;
       p.seg_per_span = keys <= one_span && p.S_max <= kGqaMaxSegs ? p.S_max : 1;
+      fill_spans(p);
       e = launch_gqa_mfma(p, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
     } else {
       p.seg_per_span = keys <= one_span_keys(c.D) && !c.gidx ? p.S_max : 1;
+      fill_spans(p);
       e = launch_partial(p, R, (p.S_max + p.seg_per_span - 1) / p.seg_per_span, st);
     }
   }

@@ -17,6 +17,8 @@
 
 #include "kernels.h"
 
+#include <stddef.h>
+
 namespace pion {
 namespace {
 
@@ -90,6 +92,14 @@ __device__ __forceinline__ Span get_segment(const PartialParams &p, int x, int p
   return s;
 }
 
+// Row group hg: its kv-head, row count and q-heads (row r: byte r of heads), from two
+// scalar loads. The row group of workgroup row y is y / M (y itself for one query index,
+// the latency-bound case, which then skips the division).
+struct Group {
+  int g, cnt;
+  uint64_t heads;
+  __device__ __forceinline__ int head(int r) const { return (int)((heads >> (8 * r)) & 0xffu); }
+};
 // Per-problem pointers of this workgroup.
 struct Prob {
   int N, pre_splits, n_seg, S_total;  // pre_splits: prefix segments
@@ -101,17 +111,82 @@ struct Prob {
 __device__ __forceinline__ Prob get_prob(const PartialParams &p, int z, int y) {
   Prob b;
   b.N = p.N[z];
-  b.pre_splits = p.blocks ? p.n_sel : ((p.gidx ? p.gmax : b.N) + p.pre_chunk - 1) / p.pre_chunk;
+  const uint32_t sp = p.spans[z];  // prefix segments and spans, counted by the host
+  b.pre_splits = (int)(sp & 0xffffu);
   b.n_seg = b.pre_splits + p.suf_splits;
-  b.S_total = (b.n_seg + p.seg_per_span - 1) / p.seg_per_span;
+  b.S_total = (int)(sp >> 16);
   b.Q = (const char *)p.Q + z * p.q_stride * p.esz;
   b.out = p.out + z * p.out_stride;
-  b.lse = p.lse ? p.lse + z * p.lse_stride : nullptr;
+  float *const lse_z = p.lse + z * p.lse_stride;  // (no branch: read with the rest)
+  b.lse = p.lse ? lse_z : nullptr;
   b.part_acc = p.part_acc + z * p.part_stride;
   b.part_m = p.part_m + z * p.ml_stride;
   b.part_l = p.part_l + z * p.ml_stride;
   b.counter = p.counters + (size_t)z * p.y_groups + y;
   return b;
+}
+
+// At entry: the group of workgroup row y (its index in hg), with every kernel argument
+// the first loads depend on read in the same round of scalar loads. Left to itself the
+// compiler loads each argument just before its use, behind the branches between them: a
+// chain of round trips before the first K/V load. The record is read for hg = y, the
+// group when M = 1 (the latency-bound case; y < kMaxHeads then), and read again after
+// the division otherwise.
+__device__ __forceinline__ Group entry_group(const PartialParams &p, int z, int y, int &hg,
+                                             Prob &b) {
+  const int M = p.M;
+  const int hy = min(y, kMaxHeads - 1);
+  {
+    // One round of scalar loads that brings every kernel-argument cache line the entry
+    // reads into the scalar cache: the header (its first 256 bytes) and this
+    // workgroup's entries of the per-problem and per-group tables. The compiler's own
+    // loads below then hit that cache instead of each waiting on L2. p is the kernel's
+    // only argument, at offset 0 of the argument segment.
+    const char __attribute__((address_space(4))) *ka =
+        (const char __attribute__((address_space(4))) *)__builtin_amdgcn_kernarg_segment_ptr();
+    // (byte offsets of the table entries, read into scalar registers)
+    const auto off = [](size_t o) { return __builtin_amdgcn_readfirstlane((int)o); };
+    const int o_sp = off(offsetof(PartialParams, spans) + 4 * (size_t)z);
+    const int o_n = off(offsetof(PartialParams, N) + 4 * (size_t)z);
+    const int o_kv = off(offsetof(PartialParams, kv_base) + 8 * (size_t)z);
+    const int o_gc = off(offsetof(PartialParams, rg) + offsetof(RowGroups, gc) + 4 * (size_t)hy);
+    const int o_hw = off(offsetof(PartialParams, rg) + offsetof(RowGroups, heads) + 8 * (size_t)hy);
+    uint32_t t[9];
+    __asm__ volatile(
+        "s_load_dword %0, %9, 0x0\n\t"
+        "s_load_dword %1, %9, 0x40\n\t"
+        "s_load_dword %2, %9, 0x80\n\t"
+        "s_load_dword %3, %9, 0xc0\n\t"
+        "s_load_dword %4, %9, %10\n\t"
+        "s_load_dword %5, %9, %11\n\t"
+        "s_load_dword %6, %9, %12\n\t"
+        "s_load_dword %7, %9, %13\n\t"
+        "s_load_dword %8, %9, %14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(t[0]), "=&s"(t[1]), "=&s"(t[2]), "=&s"(t[3]), "=&s"(t[4]), "=&s"(t[5]),
+          "=&s"(t[6]), "=&s"(t[7]), "=&s"(t[8])
+        : "s"(ka), "s"(o_sp), "s"(o_n), "s"(o_kv), "s"(o_gc), "s"(o_hw)
+        : "memory");
+  }
+  uint32_t gc = p.rg.gc[hy];
+  uint64_t hw = p.rg.heads[hy];
+  b = get_prob(p, z, y);
+  __asm__ volatile("" ::"s"(M), "s"(gc), "s"(hw), "s"(b.N), "s"(b.S_total), "s"(b.n_seg),
+                   "s"(b.Q), "s"(b.out), "s"(b.lse), "s"(b.part_acc), "s"(b.part_m),
+                   "s"(b.part_l), "s"(b.counter), "s"(p.kv_base[z]), "s"(p.x_begin),
+                   "s"(p.pre_chunk), "s"(p.seg_per_span), "s"(p.fmt), "s"(p.H_kv), "s"(p.esz),
+                   "s"(p.blocks), "s"(p.gidx), "s"(p.qscale), "s"(p.S_suf), "s"(p.suf_chunk));
+  hg = y;
+  if (M != 1) {
+    hg = y / M;
+    gc = p.rg.gc[hg];
+    hw = p.rg.heads[hg];
+  }
+  Group gr;
+  gr.g = (int)(gc & 0xffu);
+  gr.cnt = (int)(gc >> 8);
+  gr.heads = hw;
+  return gr;
 }
 
 // Partials of one (problem, query index): rows are the q-heads h, layout
@@ -197,17 +272,17 @@ struct MergeScratch {
 // phase results of a pair merge through LDS.
 template <int D, int NT>
 __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b,
-                                           const PartRsrc &pr, const uint8_t *heads, int cnt,
-                                           int qi, MergeScratch<NT> &ms) {
+                                           const PartRsrc &pr, const Group &gr, int qi,
+                                           MergeScratch<NT> &ms) {
   constexpr int DQ = D / 4, CH = 16;
   const int tid = threadIdx.x;
-  const int RT = cnt * DQ;
+  const int RT = gr.cnt * DQ;
   for (int pass0 = 0; pass0 < RT; pass0 += NT) {
     const int np = min(NT, RT - pass0);
     const int P = NT / np;
     const int ph = tid / np, pair = pass0 + tid % np;
     const int r = pair / DQ, dq = pair - r * DQ;
-    const int h = heads[r];
+    const int h = gr.head(r);
     float m = kNegBig, l = 0.f;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     if (ph < P) {
@@ -217,12 +292,14 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
           const int c = c0 + k * P;
-          const bool in = c < b.S_total;
-          const int cc = in ? c : 0;
-          mc[k] = load_m(pr, h, cc);
-          lc[k] = load_l(pr, h, cc);
-          ac[k] = load_part(pr, h, cc, dq);
-          if (!in) mc[k] = -INFINITY;
+          mc[k] = -INFINITY;  // past the last span: weight 0
+          lc[k] = 0.f;
+          ac[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (c < b.S_total) {  // (no request at all for the slots past it)
+            mc[k] = load_m(pr, h, c);
+            lc[k] = load_l(pr, h, c);
+            ac[k] = load_part(pr, h, c, dq);
+          }
         }
         float mx = m;
 #pragma unroll
@@ -247,11 +324,13 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
       ms.l[tid] = l;
       ms.a[tid] = a;
       __syncthreads();
-      if (ph == 0) {
-        float M = m;
-        for (int q = 1; q < P; ++q) M = fmaxf(M, ms.m[q * np + tid]);
+      if (ph == 0) {  // (unrolled: the LDS reads of 8 phases in flight together)
+        float M = m;  // (q = 0 is this thread's own m: P, a power of two, stays whole)
+#pragma unroll 8
+        for (int q = 0; q < P; ++q) M = fmaxf(M, ms.m[q * np + tid]);
         float L = 0.f;
         f32x4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
         for (int q = 0; q < P; ++q) {
           const float f = fast_exp2(ms.m[q * np + tid] - M);
           L = __builtin_fmaf(f, ms.l[q * np + tid], L);
@@ -277,9 +356,8 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
 // counter to zero for the next call. `last` is a workgroup-shared flag.
 template <int D, int NT>
 __device__ __forceinline__ void ticket_and_merge(const PartialParams &p, const Prob &b,
-                                                 const PartRsrc &pr, const uint8_t *heads,
-                                                 int cnt, int qi, MergeScratch<NT> &ms,
-                                                 int &last) {
+                                                 const PartRsrc &pr, const Group &gr, int qi,
+                                                 MergeScratch<NT> &ms, int &last) {
   // this wave's partial stores have completed before the barrier and the ticket
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -289,7 +367,7 @@ __device__ __forceinline__ void ticket_and_merge(const PartialParams &p, const P
   }
   __syncthreads();
   if (!last) return;
-  merge_rows<D, NT>(p, b, pr, heads, cnt, qi, ms);
+  merge_rows<D, NT>(p, b, pr, gr, qi, ms);
   if (threadIdx.x == 0)
     __hip_atomic_store(b.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
