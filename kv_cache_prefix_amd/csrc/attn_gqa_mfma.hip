@@ -38,7 +38,6 @@ struct GqaSmem {
       float m[NW][kGqaMaxRows], l[NW][kGqaMaxRows];
       alignas(16) float acc[NW][kGqaMaxRows][D];
     } wm;
-    MergeScratch<64 * NW> ms;
   };
   int seg_j0[kGqaMaxSegs], seg_j1[kGqaMaxSegs], seg_cum[kGqaMaxSegs + 1];
   unsigned char seg_suf[kGqaMaxSegs];
@@ -269,7 +268,7 @@ __global__ __launch_bounds__(64 * GqaSmem<D>::NW) void gqa_mfma_kernel(PartialPa
       if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.last);
 }
 
 template <int D>

@@ -100,7 +100,6 @@ struct Mlx4Scratch {
   float m[kParts][R], l[kParts][R];
   union {
     alignas(16) float acc[kParts][R][D];
-    MergeScratch<64 * NW> ms;
   };
   int last;
 };
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_split_kernel(PartialParams p) {
     if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
   }
   // (ticket_and_merge's barrier precedes any reuse of acc as merge scratch)
-  ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
+  ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.last);
 }
 
 // 8 waves per workgroup (two per SIMD: one wave alone issues VALU work at about half

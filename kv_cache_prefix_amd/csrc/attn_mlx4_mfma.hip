@@ -63,7 +63,6 @@ struct Mlx4MfmaSmem {
       float m[NW][4], l[NW][4], bs[NW][4][4];
       alignas(16) float acc[NW][4][128];
     } wm;
-    MergeScratch<64 * NW> ms;
   };
   int last;
 };
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(64 * NW) void mlx4_mfma_kernel(PartialParams p) {
       if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, NT>(p, b, pr, gr, qi, sm.last);
 }
 
 }  // namespace

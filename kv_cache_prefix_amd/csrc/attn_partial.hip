@@ -89,7 +89,6 @@ template <int D, int R, int NW>
 struct Scratch {
   union {
     WaveState<D, R, NW> ws;
-    MergeScratch<64 * NW> ms;
   };
   int last;
 };
@@ -146,7 +145,7 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
       if (dq == 0) store_ml(pr, gr.head(r), x, lw > 0.f ? mm : -INFINITY, lw);  // empty: weight 0
     }
   }
-  if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, gr, qi, sm.ms, sm.last);
+  if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, gr, qi, sm.last);
 }
 
 // One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.

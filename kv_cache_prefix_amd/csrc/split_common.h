@@ -257,35 +257,35 @@ __device__ __forceinline__ float load_l(const PartRsrc &r, int h, int c) {
                             __builtin_amdgcn_raw_buffer_load_b32(r.l, (h * r.S_max + c) * 4, 0, kSC1));
 }
 
-// LDS of the merge: per thread a running (m, l, acc piece); NT threads.
-template <int NT>
-struct MergeScratch {
-  f32x4 a[NT];
-  float m[NT], l[NT];
-};
-
 // Merge the S_total partials of the rows of this workgroup into out / lse, in the one
-// workgroup of the row group that took the last ticket. Thread t takes (row r, dim
-// quad dq) = pair t % np of the np = min(NT, cnt * D/4) pairs of a pass, and spans
-// c = t / np, + P, ... (P = NT / np phases); it issues the loads of CH spans of its
-// row before consuming any, so every row's partials are in flight together. The P
-// phase results of a pair merge through LDS.
+// workgroup of the row group that took the last ticket. A pass covers np = min(NT,
+// cnt * D/4) (row r, dim quad dq) pairs; each pair gets P adjacent lanes of one wave (P
+// a power of two, at most 64, P * np <= NT), lane ph taking spans ph, ph + P, ... and
+// issuing the loads of CH of them before consuming any, so every row's partials are in
+// flight together. The P lanes of a pair then combine their (m, l, acc) by lane
+// exchanges, log2 P steps of the same LSE rule (no LDS, no barrier).
+__device__ __forceinline__ float xor_lane(float v, int s) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ s) & 63) * 4, __builtin_bit_cast(int, v)));
+}
 template <int D, int NT>
 __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b,
-                                           const PartRsrc &pr, const Group &gr, int qi,
-                                           MergeScratch<NT> &ms) {
+                                           const PartRsrc &pr, const Group &gr, int qi) {
   constexpr int DQ = D / 4, CH = 16;
   const int tid = threadIdx.x;
   const int RT = gr.cnt * DQ;
   for (int pass0 = 0; pass0 < RT; pass0 += NT) {
     const int np = min(NT, RT - pass0);
-    const int P = NT / np;
-    const int ph = tid / np, pair = pass0 + tid % np;
+    int P = 1;  // workgroup-uniform
+    while (2 * P * np <= NT && 2 * P <= 64) P *= 2;
+    const int ph = tid & (P - 1), pi = tid / P;
+    const bool active = pi < np;
+    const int pair = pass0 + (active ? pi : 0);
     const int r = pair / DQ, dq = pair - r * DQ;
     const int h = gr.head(r);
     float m = kNegBig, l = 0.f;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    if (ph < P) {
+    if (active) {
       for (int c0 = ph; c0 < b.S_total; c0 += P * CH) {
         float mc[CH], lc[CH];
         f32x4 ac[CH];
@@ -319,30 +319,17 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
         m = mx;
       }
     }
-    if (P > 1) {
-      ms.m[tid] = m;
-      ms.l[tid] = l;
-      ms.a[tid] = a;
-      __syncthreads();
-      if (ph == 0) {  // (unrolled: the LDS reads of 8 phases in flight together)
-        float M = m;  // (q = 0 is this thread's own m: P, a power of two, stays whole)
-#pragma unroll 8
-        for (int q = 0; q < P; ++q) M = fmaxf(M, ms.m[q * np + tid]);
-        float L = 0.f;
-        f32x4 A = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int q = 0; q < P; ++q) {
-          const float f = fast_exp2(ms.m[q * np + tid] - M);
-          L = __builtin_fmaf(f, ms.l[q * np + tid], L);
-          A += f * ms.a[q * np + tid];
-        }
-        m = M;
-        l = L;
-        a = A;
-      }
-      __syncthreads();
+    // every lane's m is finite (at least kNegBig), so the weights below are too
+    for (int s = 1; s < P; s <<= 1) {
+      const float m2 = xor_lane(m, s), l2 = xor_lane(l, s);
+      const f32x4 a2 = {xor_lane(a.x, s), xor_lane(a.y, s), xor_lane(a.z, s), xor_lane(a.w, s)};
+      const float mx = fmaxf(m, m2);
+      const float f1 = fast_exp2(m - mx), f2 = fast_exp2(m2 - mx);
+      l = __builtin_fmaf(l, f1, l2 * f2);
+      a = a * f1 + a2 * f2;
+      m = mx;
     }
-    if (ph == 0) {  // a row with no key at all (an empty token list): out 0, lse -inf
+    if (active && ph == 0) {  // a row with no key at all (an empty token list): out 0, lse -inf
       const size_t row = (size_t)h * p.M + qi;
       const float inv = l > 0.f ? 1.f / l : 0.f;
       *(float4 *)(b.out + row * D + 4 * dq) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
@@ -357,7 +344,7 @@ __device__ __forceinline__ void merge_rows(const PartialParams &p, const Prob &b
 template <int D, int NT>
 __device__ __forceinline__ void ticket_and_merge(const PartialParams &p, const Prob &b,
                                                  const PartRsrc &pr, const Group &gr, int qi,
-                                                 MergeScratch<NT> &ms, int &last) {
+                                                 int &last) {
   // this wave's partial stores have completed before the barrier and the ticket
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -367,7 +354,7 @@ __device__ __forceinline__ void ticket_and_merge(const PartialParams &p, const P
   }
   __syncthreads();
   if (!last) return;
-  merge_rows<D, NT>(p, b, pr, gr, qi, ms);
+  merge_rows<D, NT>(p, b, pr, gr, qi);
   if (threadIdx.x == 0)
     __hip_atomic_store(b.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
