@@ -68,19 +68,19 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "b44c58d88d35127208492a2ecb519ee7d5a88c8d1c4653739ce9cbd8f4c8439b",
-                  "bytes_per_launch": 268750056}
+                  "sources_sha256": "22d0ec88a22d42dd9745e8ab2b0666563c3f567a4be25ccf09339b4f0b1ff5c7",
+                  "bytes_per_launch": 268722577}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
-# 22,314,919 B and writes 32,159,360 B (the five splits' partials), prefill_merge_kernel<128>
+# 22,314,919 B and writes 32,164,224 B (the five splits' partials), prefill_merge_kernel<128>
 # reads 33,495,353 B and writes 6,340,608 B (out and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "bdc8735bca9007a49102420ece2d783f154b4703e48e543644c1d68b0ec70c34",
-                   "bytes_per_launch": 94310240}
+                   "sources_sha256": "d88187b47f748a3a50687800329ecf1caa5e301260e1f3791dc108ac88100656",
+                   "bytes_per_launch": 94315105}
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
-# reads 671,957,310 B (671,088,640 algorithmic) and writes 644,096 B.
+# reads 671,928,641 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),
-                "sources_sha256": "45e624f4c8b4dbe02933f48c733c661772102799b6e0cec5505683b7359b6d9b",
-                "bytes_per_launch": 672601406}
+                "sources_sha256": "d8f6c17cbccc2e036259ffd6248c24efcfa78a68d5b1575944e82263e54427ce",
+                "bytes_per_launch": 672572737}
 
 
 def kernel_sources_sha256(files=DECODE_TRAFFIC["sources"]):
