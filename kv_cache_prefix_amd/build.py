@@ -24,7 +24,11 @@ SOURCES = ["attn_partial.hip", "attn_mlx4.hip", "attn_mlx4_mfma.hip", "attn_gqa_
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
-DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               # kernels with scalar arguments receive them in SGPRs at launch (gfx950
+               # kernel-argument preload) instead of loading them first; the compiler
+               # also emits the loads for a loader that does not preload
+               "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 # Inline assembly that writes M0 (the LDS-writing loads of mfma_common.h) saves and
 # restores it in the same statement; a new use of M0 in inline assembly must do the same.
 
