@@ -68,7 +68,7 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "22d0ec88a22d42dd9745e8ab2b0666563c3f567a4be25ccf09339b4f0b1ff5c7",
+                  "sources_sha256": "7bcf1e34220ae3eeb37e6b289187bc84d857953d98696d2b31bdde8a991a9a17",
                   "bytes_per_launch": 268722577}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
 # 22,314,919 B and writes 32,164,224 B (the five splits' partials), prefill_merge_kernel<128>
@@ -79,7 +79,7 @@ PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h")
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
 # reads 671,928,641 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),
-                "sources_sha256": "d8f6c17cbccc2e036259ffd6248c24efcfa78a68d5b1575944e82263e54427ce",
+                "sources_sha256": "502e39e22ef47ff1594a2f4be490fb14c7f19dd27139b033570277a01b1e5c59",
                 "bytes_per_launch": 672572737}
 
 

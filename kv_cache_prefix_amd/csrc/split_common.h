@@ -126,12 +126,14 @@ __device__ __forceinline__ Prob get_prob(const PartialParams &p, int z, int y) {
   return b;
 }
 
-// At entry: the group of workgroup row y (its index in hg), with every kernel argument
-// the first loads depend on read in the same round of scalar loads. Left to itself the
-// compiler loads each argument just before its use, behind the branches between them: a
-// chain of round trips before the first K/V load. The record is read for hg = y, the
-// group when M = 1 (the latency-bound case; y < kMaxHeads then), and read again after
-// the division otherwise.
+// At entry: the group of workgroup row y (its index in hg) and the problem's pointers.
+// Left to itself the compiler loads each kernel argument just before its use, behind the
+// branches between them, and a scalar load can only be waited for together with every
+// other outstanding one: a chain of round trips to L2 before the first K/V load. Here one
+// batch of loads first brings every argument line the entry reads into the scalar
+// cache; the compiler's loads, all made before the first branch, then hit that cache.
+// The group record is read for hg = y, the group when M = 1 (the latency-bound case;
+// y < kMaxHeads then), and read again after the division otherwise.
 __device__ __forceinline__ Group entry_group(const PartialParams &p, int z, int y, int &hg,
                                              Prob &b) {
   const int M = p.M;
