@@ -517,7 +517,7 @@ def stream_ceiling(torch, kp, dev, stream, nbytes=1 << 30, reps=20, nbufs=1):
             "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(us, 2), "kernel": "stream_read_kernel",
             "note": f"plain streaming read of {nbytes >> 20} MiB with 16-byte non-temporal "
-                    f"loads, {reps} launches back to back"
+                    f"loads, one contiguous chunk per workgroup, {reps} launches back to back"
                     + (f" over {nbufs} buffers in rotation" if nbufs > 1 else "")
                     + " (cold: past the memory-side cache)"}
 

@@ -291,8 +291,9 @@ const char *pion_status_str(int status);
 const char *pion_prefix_last_plan(void);
 
 /* Measurement aid (not a wire form): reads `bytes` at the device pointer buf once with
- * 16-byte non-temporal loads and does nothing else - the plain streaming read whose rate
- * is the achievable ceiling the bandwidth-bound kernels are compared with. sink is one
+ * 16-byte non-temporal loads, one contiguous chunk per workgroup, and does nothing else -
+ * the plain streaming read whose rate is the achievable ceiling the bandwidth-bound
+ * kernels are compared with. sink is one
  * device uint32 the kernel may write (it does not, for realistic data). bytes must be a
  * multiple of 16 (0 is a no-op); buf 16-byte aligned. Errors: INVALID, HIP. */
 int pion_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
