@@ -68,7 +68,7 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "7bcf1e34220ae3eeb37e6b289187bc84d857953d98696d2b31bdde8a991a9a17",
+                  "sources_sha256": "ecc7c2bb5c97aa78bdb6b40beb6f5c814a248db96b00114ea34daa2e868d8313",
                   "bytes_per_launch": 268722577}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
 # 22,314,919 B and writes 32,164,224 B (the five splits' partials), prefill_merge_kernel<128>

@@ -148,7 +148,6 @@ __device__ __forceinline__ void finish(const PartialParams &p, const Prob &b, Sc
   if (b.S_total > 1) ticket_and_merge<D, 64 * NW>(p, b, pr, gr, qi, sm.last);
 }
 
-// One tile: U keys per lane (keys base + u*KPI + kk), fp16 rows.
 // One tile: U keys per lane (keys base + u*KPI + kk), NV 16-byte pieces per key and side.
 template <int U, int NV>
 struct Tile {
