@@ -200,7 +200,8 @@ struct PrefillParams {
   int n_iblk;                     // ceil(M / 128)
   int n_splits, split_keys;       // split_keys a multiple of 32
   float *out, *lse;
-  float *part_acc, *part_m, *part_l;  // split partials (n_splits > 1)
+  uint16_t *part_acc;             // split partials (n_splits > 1): fp16 normalized outputs
+  float *part_lse;                // and per [row][split] log-sum-exp (log2 units)
   HeadMap hm;
   uint8_t order[kMaxHeads];       // q-heads sorted by kv-head
 };

@@ -448,14 +448,14 @@ int run_prefill(const Slot &sl, const AttnCall &c, hipStream_t st) {
   }
   if (p.n_splits > 1) {
     const size_t rows = (size_t)c.H_q * c.M;
-    // acc partials per (tile, split): 128 rows x D in the kernel's register layout
-    const size_t acc_bytes = align256((size_t)tiles * 128 * p.n_splits * c.D * sizeof(float));
-    const size_t ml_bytes = align256(rows * p.n_splits * sizeof(float));
+    // fp16 partials per (tile, split): 128 rows x D in the kernel's register layout;
+    // one fp32 log-sum-exp per (row, split)
+    const size_t acc_bytes = align256((size_t)tiles * 128 * p.n_splits * c.D * sizeof(uint16_t));
+    const size_t lse_bytes = align256(rows * p.n_splits * sizeof(float));
     void *ws = nullptr;
-    if (get_ws(st, acc_bytes + 2 * ml_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
-    p.part_acc = (float *)ws;
-    p.part_m = (float *)((char *)ws + acc_bytes);
-    p.part_l = (float *)((char *)ws + acc_bytes + ml_bytes);
+    if (get_ws(st, acc_bytes + lse_bytes, &ws) != hipSuccess) return PION_ERR_NOMEM;
+    p.part_acc = (uint16_t *)ws;
+    p.part_lse = (float *)((char *)ws + acc_bytes);
   }
   return launch_prefill(p, st) == hipSuccess ? PION_OK : PION_ERR_HIP;
 }

@@ -39,9 +39,9 @@
 // would wait for every outstanding one before any LDS read; the loads are issued
 // through inline assembly instead and the kernel waits for them itself (s_waitcnt
 // vmcnt, then a barrier) before a stage is read.
-// Splits of the key range run in different workgroups, which store their (acc, m, l)
-// partials; a second kernel merges them with the LSE rule (no workgroup waits on
-// another).
+// Splits of the key range run in different workgroups, which store their partials (the
+// split's normalized output in fp16 and its log-sum-exp in fp32); a second kernel merges
+// them with the LSE rule (no workgroup waits on another).
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -65,11 +65,11 @@ constexpr int kMergeChunk = 8;  // splits whose partials the merge loads per rou
 // weight then stays below 2^15, inside fp16's range with its full relative precision)
 constexpr float kGrowLimit = 32768.f;
 
-// Byte offset of the 16-byte piece (split c, wave w, 32-dim block db, quad i, lane) in a
-// row block's partials
+// Byte offset of the 16-byte piece (split c, wave w, 32-dim block db, pair of quads i2,
+// lane) in a row block's fp16 partials
 template <int NDB>
-__device__ __forceinline__ uint32_t part_off(int c, int w, int db, int i, int lane) {
-  return (uint32_t)(((((c * 4 + w) * NDB + db) * 4 + i) * 64 + lane) * 16);
+__device__ __forceinline__ uint32_t part_off(int c, int w, int db, int i2, int lane) {
+  return (uint32_t)(((((c * 4 + w) * NDB + db) * 2 + i2) * 64 + lane) * 16);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -100,11 +100,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // The rows of a 128-row block (q-head h, block ib) that wave `wave` (0..3) holds:
-// normalized out and lse when the keys are not split; else the split partial: acc
-// unnormalized against m_run, in the register layout of o (tile, split, wave, 32-dim
-// block db, quad i, lane: one 16-byte piece per lane, so every store instruction moves
-// 1 KB of consecutive bytes); m and l (log2 units) per [row][split]. prefill_merge_kernel,
-// next on the stream, combines the splits.
+// normalized out and lse when the keys are not split; else the split partial: the
+// split's own normalized output acc / l rounded to fp16, in the register layout of o
+// (tile, split, wave, 32-dim block db, quads 2 i2 and 2 i2 + 1, lane: one 16-byte piece
+// per lane, so every store instruction moves 1 KB of consecutive bytes), and its
+// log-sum-exp m + log2 l (log2 units; -inf for a split with no key of the row) per
+// [row][split]. A normalized partial is a convex combination of fp16 V rows, so it lies
+// in fp16's range and its rounding costs at most 2^-11 of its magnitude (half the bytes
+// of fp32 partials). prefill_merge_kernel, next on the stream, combines the splits.
 template <int D>
 __device__ __forceinline__ void store_rows(const PrefillParams &p, const f16v (&o)[D / 32],
                                            float m_run, float l_run, int h, int ib, int split,
@@ -134,22 +137,23 @@ __device__ __forceinline__ void store_rows(const PrefillParams &p, const f16v (&
   const int rows_valid = min(BQ, p.M - i0);
   const size_t row0 = (size_t)h * p.M + i0;
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
-  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
+      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 2));
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_lse + row0 * S, (uint32_t)(rows_valid * S * 4));
   const int r = wave * 32 + col;  // local row; rows past rows_valid fall out of range
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;  // an empty split stores zeros
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 v = {o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+    for (int i2 = 0; i2 < 2; ++i2) {
+      half8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(o[db][8 * i2 + e] * inv);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rA,
-                                             part_off<NDB>(split, wave, db, i, lane), 0, 0);
+                                             part_off<NDB>(split, wave, db, i2, lane), 0, 0);
     }
   if (hl == 0) {
-    const float mv = l_run > 0.f ? m_run : -INFINITY;  // empty split: weight 0
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, mv), rM, (r * S + split) * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_run), rL, (r * S + split) * 4, 0, 0);
+    const float lv = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;  // empty: weight 0
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lv), rM, (r * S + split) * 4, 0, 0);
   }
 }
 
@@ -567,58 +571,66 @@ __global__ __launch_bounds__(256, (D <= 128) ? 2 : 1) void prefill_kernel(Prefil
 // Combine the split partials of prefill_kernel. One workgroup per (row block, 32-dim
 // block db): thread (wave w, lane l) takes the place of the split kernel's lane, row
 // 32 w + l % 32 and dims 32 db + 8 i + 4 (l / 32) + 0..3, and reads that piece of every
-// split (up to kMergeChunk splits per round of loads) with the row's m and l, then
-// applies the LSE rule: out = sum_c 2^(m_c - m*) acc_c / sum_c 2^(m_c - m*) l_c.
+// split (up to kMergeChunk splits per round of loads) with the row's per-split
+// log-sum-exp s_c, then applies the LSE rule to the normalized partials o_c:
+// out = sum_c 2^(s_c - s*) o_c / sum_c 2^(s_c - s*), lse = s* + log2 sum_c 2^(s_c - s*).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
   constexpr int NDB = D / 32, CH = kMergeChunk;
   const int S = p.n_splits;
-  const int tile = blockIdx.x / NDB, db = blockIdx.x - tile * NDB;
-  const int h = tile / p.n_iblk, ib = tile - h * p.n_iblk;
+  // Logical workgroups (row block in the split kernel's q-head order, then db) spread
+  // over the XCDs as the split kernel's are: XCD x takes the same share of row blocks
+  // whose splits it ran, so the partials are read from its own L2 while they are there.
+  const int T = p.H_q * p.n_iblk, W = T * NDB, C = (W + 7) >> 3;
+  const int Lm = (blockIdx.x & 7) * C + (blockIdx.x >> 3);
+  if (Lm >= W) return;
+  const int ts = Lm / NDB, db = Lm - ts * NDB;
+  const int hs = ts / p.n_iblk, ib = ts - hs * p.n_iblk;
+  const int h = p.order[hs], tile = h * p.n_iblk + ib;
   const int i0 = ib * BQ, rows_valid = min(BQ, p.M - i0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
   const int r = wave * 32 + (lane & 31);
   const int rr = min(r, rows_valid - 1);  // rows past the end repeat the last row, unstored
   const size_t row0 = (size_t)h * p.M + i0;
   const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 4));
-  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_m + row0 * S, (uint32_t)(rows_valid * S * 4));
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.part_l + row0 * S, (uint32_t)(rows_valid * S * 4));
-  float mv[kMaxPrefillSplits], lv[kMaxPrefillSplits];
+      make_rsrc(p.part_acc + (size_t)tile * BQ * S * D, (uint32_t)(BQ * S * D * 2));
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(p.part_lse + row0 * S, (uint32_t)(rows_valid * S * 4));
+  float wv[kMaxPrefillSplits];
 #pragma unroll
-  for (int c = 0; c < kMaxPrefillSplits; ++c) {
-    mv[c] = c < S ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, (rr * S + c) * 4, 0, 0))
+  for (int c = 0; c < kMaxPrefillSplits; ++c)
+    wv[c] = c < S ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rM, (rr * S + c) * 4, 0, 0))
                   : -INFINITY;
-    lv[c] = c < S ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, (rr * S + c) * 4, 0, 0))
-                  : 0.f;
-  }
   f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float M = -INFINITY, L = 0.f;
   for (int c0 = 0; c0 < S; c0 += CH) {
-    f32x4 v[CH][4];
+    u32x4 v[CH][2];
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v[cc][i] = c0 + cc < S ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                     rA, part_off<NDB>(c0 + cc, wave, db, i, lane), 0, 0))
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i2 = 0; i2 < 2; ++i2)
+        v[cc][i2] = c0 + cc < S ? __builtin_amdgcn_raw_buffer_load_b128(
+                                      rA, part_off<NDB>(c0 + cc, wave, db, i2, lane), 0, 0)
+                                : u32x4{0u, 0u, 0u, 0u};
     if (c0 == 0) {
 #pragma unroll
-      for (int c = 0; c < kMaxPrefillSplits; ++c) M = fmaxf(M, mv[c]);
+      for (int c = 0; c < kMaxPrefillSplits; ++c) M = fmaxf(M, wv[c]);
 #pragma unroll
       for (int c = 0; c < kMaxPrefillSplits; ++c) {
-        mv[c] = fast_exp2(mv[c] - M);  // the split's weight; -inf (empty or absent) -> 0
-        L = __builtin_fmaf(mv[c], lv[c], L);
+        wv[c] = fast_exp2(wv[c] - M);  // the split's weight; -inf (empty or absent) -> 0
+        L += wv[c];
       }
     }
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       float w = 0.f;
 #pragma unroll
-      for (int c = 0; c < kMaxPrefillSplits; ++c) w = c == c0 + cc ? mv[c] : w;
+      for (int c = 0; c < kMaxPrefillSplits; ++c) w = c == c0 + cc ? wv[c] : w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += w * v[cc][i];
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const half8 hv = __builtin_bit_cast(half8, v[cc][i2]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[2 * i2 + e / 4][e % 4] += w * (float)hv[e];
+      }
     }
   }
   if (r < rows_valid) {
@@ -635,7 +647,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t s) {
   if (p.n_splits < 1 || p.n_splits > kMaxPrefillSplits || p.split_keys % BK) return hipErrorInvalidValue;
   const int tiles = p.H_q * p.n_iblk, W = tiles * p.n_splits;
-  const dim3 grid(8 * ((W + 7) / 8)), mgrid(tiles * (p.D / 32));
+  const dim3 grid(8 * ((W + 7) / 8)), mgrid(8 * ((tiles * (p.D / 32) + 7) / 8));
   const bool merge = p.n_splits > 1;
   note_launch("prefill_kernel<%d>", p.D);
   if (merge) note_launch("prefill_merge_kernel<%d>", p.D);
