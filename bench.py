@@ -68,19 +68,20 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "ecc7c2bb5c97aa78bdb6b40beb6f5c814a248db96b00114ea34daa2e868d8313",
-                  "bytes_per_launch": 268722577}
+                  "sources_sha256": "2725541d45f631e7699de35ebaddbda0ea065bbe18745e9cfad906b42f61d07e",
+                  "bytes_per_launch": 268719091}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
-# 22,314,919 B and writes 32,164,224 B (the five splits' partials), prefill_merge_kernel<128>
-# reads 33,495,353 B and writes 6,340,608 B (out and lse).
+# 22,317,556 B and writes 15,979,110 B (the five splits' fp16 partials and their
+# log-sum-exps), prefill_merge_kernel<128> reads 16,065,150 B and writes 6,340,608 B (out
+# and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "d88187b47f748a3a50687800329ecf1caa5e301260e1f3791dc108ac88100656",
-                   "bytes_per_launch": 94315105}
+                   "sources_sha256": "91f6f1a56b3e834d1309f06a01ac4a3d87481d121961e2d60dc0565027240820",
+                   "bytes_per_launch": 60702424}
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
-# reads 671,928,641 B (671,088,640 algorithmic) and writes 644,096 B.
+# reads 671,929,782 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),
-                "sources_sha256": "502e39e22ef47ff1594a2f4be490fb14c7f19dd27139b033570277a01b1e5c59",
-                "bytes_per_launch": 672572737}
+                "sources_sha256": "8972a242a10db657de46cc2dae90e2448aa19144bd1f06752be4b6be944dfd50",
+                "bytes_per_launch": 672573878}
 
 
 def kernel_sources_sha256(files=DECODE_TRAFFIC["sources"]):
