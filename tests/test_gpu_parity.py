@@ -788,6 +788,20 @@ def test_mfma_prefill_single_split(kp, monkeypatch, D):
     check(host(out), host(lse), *oracle.prefix_query(inp.Q, inp.K, inp.V))
 
 
+def test_mfma_prefill_sixteen_splits_fp16_partials(kp):
+    # One 128-row block per q-head and a long prefix: the plan's largest split count (16)
+    # per row block, each split stored as an fp16 normalized partial with its fp32
+    # log-sum-exp and merged by the LSE rule. V scaled by 4 (exact in fp16) makes the
+    # partials' fp16 rounding four times larger; every row against the oracle.
+    inp = synth.generate(synth.PREFILL, 17, N=8000, M=100, S_suf=100, D=128, H_q=2, H_kv=1)
+    V4, Vs4 = (inp.V * 4).astype(np.float16), (inp.V_suf * 4).astype(np.float16)
+    kp.pion_prefix_store("t", 607, dev(inp.K), dev(V4))
+    out, lse = empty((2, 100, 128)), empty((2, 100))
+    kp.pion_prefix_query_fused("t", 607, dev(inp.Q), dev(inp.K_suf), dev(Vs4), out, lse)
+    check(host(out), host(lse), *oracle.prefix_query_fused(inp.Q, inp.K, V4, inp.K_suf, Vs4))
+    kp.pion_prefix_drop("t", 607)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_mfma_prefill_random_shapes(kp, seed):
     # Seeded random shapes: every head dim (with and without LDS padding) once without a
