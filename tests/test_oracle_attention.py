@@ -208,3 +208,27 @@ def test_lse_is_natural_log():
     o, lse = oracle.attend(q, K, V, math.log(3.0))
     assert lse == pytest.approx(math.log(4.0), abs=1e-15)
     assert o[0] == pytest.approx(0.75, abs=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fp16_rounded_split_partials_stay_within_the_stated_bound(seed):
+    # The batched-Q kernel keeps each key split's partial as the split's normalized
+    # output rounded to fp16, with its log-sum-exp exact, and merges the splits by the
+    # LSE rule. Since the merge weights sum to one, the result differs from attention
+    # over all keys by at most 2^-11 of the largest partial element (fp16's unit
+    # roundoff), and the LSE not at all. Exact partials from the oracle, rounded here.
+    rng = np.random.default_rng(900 + seed)
+    D, N, S = 64, 3000, 2 + 4 * seed
+    q = rng.standard_normal(D).astype(np.float16)
+    K = rng.standard_normal((N, D)).astype(np.float16)
+    V = (rng.standard_normal((N, D)) * (4.0 if seed % 2 else 1.0)).astype(np.float16)
+    scale = oracle.softmax_scale(D)
+    cuts = [0, *np.sort(rng.choice(np.arange(1, N), size=S - 1, replace=False)), N]
+    parts = [oracle.attend(q, K[a:b], V[a:b], scale) for a, b in zip(cuts[:-1], cuts[1:])]
+    rounded = [(o.astype(np.float16).astype(np.float64), l) for o, l in parts]
+    want_o, want_l = oracle.attend(q, K, V, scale)
+    got_o, got_l = oracle.combine(rounded)
+    err = np.abs(got_o - want_o).max()
+    bound = 2.0 ** -11 * max(np.abs(o).max() for o, _ in parts)
+    assert 0 < err <= bound * (1 + 1e-9) + 1e-12
+    assert abs(got_l - want_l) <= 1e-12 * max(1.0, abs(want_l))
