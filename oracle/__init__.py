@@ -6,9 +6,11 @@ leg may import it. It shares no code with ``kv_cache_prefix_amd`` and imports
 nothing from it; both sides take their inputs from ``synth`` only.
 
 Parity pins (what each function is checked against, besides itself) live in
-``tests/test_oracle_*.py``. Unpinned readings: the LSE base (pinned only through
-merge consistency), the causal alignment for M < S_suf (the plain bottom-right
-reading), and ``top_k`` / ``fa_window`` (not implemented).
+``tests/test_oracle_*.py``. Where the pages leave a point open the oracle follows one
+reading and is pinned to that reading, not to the pages (parity with the pages is
+unpinned there): the LSE base (natural log: ln N at q = 0 and a two-key hand case),
+the causal alignment for M < S_suf (bottom-right: torch's masked SDPA with a shifted
+lower triangle, at M < S_suf too). ``top_k`` and ``fa_window`` are not implemented.
 """
 from .cold_tier import ColdTier
 from . import vstore
