@@ -29,7 +29,7 @@
 //                word, odd ones in another, merged as lo | hi << 4.
 // No contraction elsewhere, so the codes are bit-exact with any IEEE fp32 evaluation
 // of the steps above.
-#include "kernels.h"
+#include "mlx4g32.h"
 
 #include <hip/hip_fp16.h>
 
@@ -163,17 +163,26 @@ __device__ __forceinline__ void encode_word(uint4 raw, int64_t t, bool valid,
   }
 }
 
+// One tensor's input rows and output arrays.
+struct QuantTensor {
+  const uint16_t *x;
+  uint32_t *codes;
+  uint16_t *scales, *biases;
+};
+
 // One code word per lane and chunk: workgroup x encodes the kWords chunks of 256 words
 // from word 256 kWords x, lane i word 256 (kWords x + k) + i of chunk k; all chunks'
-// loads are issued before the first is encoded (more bytes in flight per wave).
+// loads are issued before the first is encoded (more bytes in flight per wave). Grid row
+// y encodes tensor y (a, or b for y = 1: the K and V of a store in one launch).
 constexpr int kWords = 4;
 template <bool SBW>
-__global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(const uint16_t *__restrict__ x,
-                                                               int64_t nwords,
-                                                               uint32_t *__restrict__ codes,
-                                                               uint16_t *__restrict__ scales,
-                                                               uint16_t *__restrict__ biases,
-                                                               int sb_stride) {
+__global__ __launch_bounds__(256) void quantize_mlx4g32_kernel(QuantTensor qa, QuantTensor qb,
+                                                               int64_t nwords, int sb_stride) {
+  const QuantTensor q = blockIdx.y ? qb : qa;
+  const uint16_t *__restrict__ x = q.x;
+  uint32_t *__restrict__ codes = q.codes;
+  uint16_t *__restrict__ scales = q.scales;
+  uint16_t *__restrict__ biases = q.biases;
   const int64_t t0 = (int64_t)blockIdx.x * (256 * kWords) + threadIdx.x;
   uint4 raw[kWords];
 #pragma unroll
@@ -205,13 +214,30 @@ hipError_t launch_quantize_mlx4g32(const uint16_t *x, int64_t rows, int D, uint3
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   // scale and bias interleaved in one 32-bit word (the slot layout): one store
   const bool sbw = sb_stride == 2 && biases == scales + 1 && ((uintptr_t)scales & 3) == 0;
+  const QuantTensor q{x, codes, scales, biases};
   note_launch("quantize_mlx4g32_kernel<%d>", (int)sbw);
   if (sbw)
-    hipLaunchKernelGGL(quantize_mlx4g32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, x,
-                       nwords, codes, scales, biases, sb_stride);
+    hipLaunchKernelGGL(quantize_mlx4g32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, q,
+                       q, nwords, sb_stride);
   else
-    hipLaunchKernelGGL(quantize_mlx4g32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
-                       nwords, codes, scales, biases, sb_stride);
+    hipLaunchKernelGGL(quantize_mlx4g32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, q,
+                       q, nwords, sb_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mlx4g32_pair(const uint16_t *xa, uint32_t *codes_a, uint32_t *sb_a,
+                                        const uint16_t *xb, uint32_t *codes_b, uint32_t *sb_b,
+                                        int64_t rows, int D, hipStream_t s) {
+  const int64_t nwords = rows * (D / 8);
+  if (nwords <= 0) return hipSuccess;
+  const int64_t blocks = (nwords + 256 * kWords - 1) / (256 * kWords);
+  if (blocks > 0x7fffffffLL || ((uintptr_t)sb_a & 3) || ((uintptr_t)sb_b & 3))
+    return hipErrorInvalidValue;
+  const QuantTensor qa{xa, codes_a, (uint16_t *)sb_a, (uint16_t *)sb_a + 1};
+  const QuantTensor qb{xb, codes_b, (uint16_t *)sb_b, (uint16_t *)sb_b + 1};
+  note_launch("quantize_mlx4g32_kernel<1>");
+  hipLaunchKernelGGL(quantize_mlx4g32_kernel<true>, dim3((unsigned)blocks, 2), dim3(256), 0, s,
+                     qa, qb, nwords, 2);
   return hipGetLastError();
 }
 

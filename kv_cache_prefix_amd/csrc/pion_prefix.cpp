@@ -41,6 +41,7 @@
 
 #include "attn_gqa.h"
 #include "kernels.h"
+#include "mlx4g32.h"
 #include "sparse.h"
 
 namespace {
@@ -636,13 +637,11 @@ hipError_t fill_from_fp16(char *base, const SlotLayout &L, int kv_format, const 
     if (e != hipSuccess) return e;
     return hipMemcpyAsync(base + L.off[1], V, bytes, hipMemcpyDeviceToDevice, st);
   }
+  // K and V in one launch
   const int64_t rows = (int64_t)(elems / D);
-  uint16_t *ksb = (uint16_t *)(base + L.off[1]), *vsb = (uint16_t *)(base + L.off[3]);
-  hipError_t e = launch_quantize_mlx4g32((const uint16_t *)K, rows, D,
-                                         (uint32_t *)(base + L.off[0]), ksb, ksb + 1, 2, st);
-  if (e != hipSuccess) return e;
-  return launch_quantize_mlx4g32((const uint16_t *)V, rows, D, (uint32_t *)(base + L.off[2]), vsb,
-                                 vsb + 1, 2, st);
+  return launch_quantize_mlx4g32_pair(
+      (const uint16_t *)K, (uint32_t *)(base + L.off[0]), (uint32_t *)(base + L.off[1]),
+      (const uint16_t *)V, (uint32_t *)(base + L.off[2]), (uint32_t *)(base + L.off[3]), rows, D, st);
 }
 
 // Allocate the slot (sid, layer), let `fill` write its arrays on stream `st`, and install
