@@ -68,19 +68,19 @@ HBM_PEAK_GBS = 8000.0
 # Each figure is valid only for the kernel sources it was taken on (sha256 of the listed
 # files, in order); any other source reports null.
 DECODE_TRAFFIC = {"sources": ("attn_partial.hip", "split_common.h", "kernels.h"),
-                  "sources_sha256": "2725541d45f631e7699de35ebaddbda0ea065bbe18745e9cfad906b42f61d07e",
+                  "sources_sha256": "5da6a98a744fbd32523d1ee6332b086633c214cfb42a54dc2c46e4d4279774b4",
                   "bytes_per_launch": 268719091}
 # One fused prefill call (H_q 24, N 4096, M = S_suf = 512): prefill_kernel<128> reads
 # 22,317,556 B and writes 15,979,110 B (the five splits' fp16 partials and their
 # log-sum-exps), prefill_merge_kernel<128> reads 16,065,150 B and writes 6,340,608 B (out
 # and lse).
 PREFILL_TRAFFIC = {"sources": ("prefill_mfma.hip", "mfma_common.h", "kernels.h"),
-                   "sources_sha256": "91f6f1a56b3e834d1309f06a01ac4a3d87481d121961e2d60dc0565027240820",
+                   "sources_sha256": "a70705e19e6f3443d27f57a953f484ffcc7973ef30d1d3278357953cba96ec0f",
                    "bytes_per_launch": 60702424}
 # The 16-layer mlx4g32 decode launch (H_q 24, H_kv 8, N 32768): mlx4_mfma_kernel<8>
 # reads 671,929,782 B (671,088,640 algorithmic) and writes 644,096 B.
 MLX4_TRAFFIC = {"sources": ("attn_mlx4_mfma.hip", "mfma_common.h", "split_common.h", "kernels.h"),
-                "sources_sha256": "8972a242a10db657de46cc2dae90e2448aa19144bd1f06752be4b6be944dfd50",
+                "sources_sha256": "88898101b5fd8c21a66c4048be28116ba7a71469c019597a634d56efb0282a31",
                 "bytes_per_launch": 672573878}
 
 

@@ -186,9 +186,10 @@ hipError_t launch_mlx4_mfma(const PartialParams &p, int rows_per_group, int x_co
 // Batched-Q attention on fp16 MFMA over a resident fp16 prefix plus an optional fp16
 // causal suffix (bottom-right aligned). A workgroup serves (tile, split): tile = (q-head,
 // block of 128 query rows), split = a range of split_keys tokens of the concatenated key
-// index [0, N + S_suf). With n_splits > 1 the splits store partials (acc: [tile][n_splits]
-// [128 * D] in the kernel's register layout; m, l: [H_q*M][n_splits]) and
-// prefill_merge_kernel, launched next on the same stream, merges them into out and lse.
+// index [0, N + S_suf). With n_splits > 1 the splits store partials (each split's
+// normalized output in fp16: [tile][n_splits][128 * D] in the kernel's register layout;
+// its log-sum-exp in log2 units: [H_q*M][n_splits]) and prefill_merge_kernel, launched
+// next on the same stream, merges them into out and lse.
 // The 1-D grid is ordered so that the workgroups of one kv-head share an XCD:
 // order[] lists the q-heads grouped by kv-head.
 struct PrefillParams {
