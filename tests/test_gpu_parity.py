@@ -445,6 +445,21 @@ def test_mlx4g32_rising_logits_rescale(kp):
     check(out, lse, *oracle.prefix_query(inp.Q, *mlx4_ref(K, inp.V)))
 
 
+@pytest.mark.parametrize("D,H_q,H_kv", [(64, 8, 8), (128, 8, 8), (128, 24, 8)])
+def test_mlx4g32_store_encoding_single_key(kp, D, H_q, H_kv):
+    # One key per kv-head: out is that token's dequantized V row and lse its scaled
+    # q . k over the dequantized K, so every code, scale and bias the store's encoder
+    # wrote (K and V in one launch) shows up far above the 1e-5 tolerance if it differs
+    # from the oracle's encoding (one code step moves a value by a whole scale).
+    inp = synth.generate(synth.MLX4_DECODE, 19 + D + H_q, N=1, H_q=H_q, H_kv=H_kv, D=D)
+    kp.pion_prefix_store("t", 16, dev(inp.K), dev(inp.V), kp.PION_KV_MLX4G32)
+    out, lse = query(kp, "t", 16, inp.Q)
+    ref, ref_lse = oracle.prefix_query(inp.Q, *mlx4_ref(inp.K, inp.V))
+    np.testing.assert_allclose(out, ref.reshape(out.shape), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(lse, ref_lse.reshape(lse.shape), rtol=0, atol=1e-5)
+    kp.pion_prefix_drop("t", 16)
+
+
 def test_mlx4g32_dominant_key(kp):
     # one key aligned with every query: its weight is ~1 and the rest ~0
     inp = synth.generate(synth.MLX4_DECODE, 9, N=2048, H_q=4, H_kv=1)
